@@ -1,0 +1,191 @@
+"""Pins for the CPU oracle: checks that tie it to the pages and to mathematics, not to itself.
+
+Each ``pin_*`` function takes a row sampler with the signature of ``oracle.sample_row`` and
+returns a list of failure descriptions (empty = pass). The oracle tests call them with the real
+oracle; the mutation tests call them with deliberately broken copies of it, to show that a
+plausible mistake in the oracle (a dropped tie, a strict inequality, a wrong normalizer, a
+flipped sign) fails at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import token_uniforms
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+def pin_tie_example(sample_row):
+    """The pages' worked tie case (sglang PR #36630 summary, 'Key code' tie test): probabilities
+    [0.4, 0.2, 0.2, 0.1, 0.1] with top_k=2 and top_p=0.45 keep ids {0, 1, 2}, more than top_k.
+    Logits are the float32 logs of those probabilities, so equal probabilities have equal bits.
+    The renormalized support is {0.4, 0.2, 0.2} / 0.8, so the logprobs are ln 1/2, ln 1/4, ln 1/4
+    (closed form); the drawn token must lie in the support."""
+    g = json.load(open(os.path.join(GOLDEN, "tie_example.json")))
+    x = np.log(np.array(g["probs"], dtype=np.float32)).astype(np.float32).astype(np.float64)
+    fails = []
+    for seed in range(16):
+        try:
+            r = sample_row(x, 1.0, g["top_k"], g["top_p"], 0.0, seed, 0)
+        except Exception as e:  # a broken oracle may raise
+            return [f"tie example raised {e!r}"]
+        if r.support.tolist() != g["expected_support_ids"]:
+            fails.append(f"tie example support {r.support.tolist()}")
+        want = np.array([math.log(0.5), math.log(0.25), math.log(0.25)])
+        if r.L == 3 and np.max(np.abs(r.logprobs - want)) > 1e-6:
+            fails.append(f"tie example logprobs {r.logprobs}")
+        if r.token not in g["expected_support_ids"]:
+            fails.append(f"tie example token {r.token}")
+    return fails
+
+
+def brute_force(x, T, k, p, min_p):
+    """Per-token closed form of the joint filter, O(V^2), no sorting:
+    i in S  <=>  x_i finite, #{j: x_j > x_i} < k_eff, sum_{x_j > x_i} w_j <= p * Z (if p < 1),
+    and (x_i - max)/T >= ln(min_p) (if min_p > 0).
+    Returns (support in (logit desc, id asc) order, near_boundary)."""
+    T, p, min_p = _f32(T), _f32(p), _f32(min_p)
+    V = len(x)
+    F = [i for i in range(V) if x[i] > -math.inf]
+    n = len(F)
+    m = max(x[i] for i in F)
+    k_eff = k if 1 <= k < n else n
+    w = {i: math.exp((x[i] - m) / T) for i in F}
+    Z = math.fsum(w.values())
+    S, near = [], False
+    for i in F:
+        gt = [j for j in F if x[j] > x[i]]
+        mass = math.fsum(w[j] for j in gt)
+        ok = len(gt) < k_eff
+        if p < 1.0:
+            ok = ok and mass <= p * Z
+            near |= abs(mass - p * Z) <= 1e-9 * Z
+        if min_p > 0.0:
+            lhs = (x[i] - m) / T
+            ok = ok and lhs >= math.log(min_p)
+            near |= abs(lhs - math.log(min_p)) <= 1e-9
+        if ok:
+            S.append(i)
+    S.sort(key=lambda i: (-x[i], i))
+    return S, near
+
+
+def _check_against_brute(sample_row, x, T, k, p, mp, seed, pos):
+    """Compare one oracle row with the brute force; returns a failure string or None."""
+    S, near = brute_force(x, T, k, p, mp)
+    try:
+        r = sample_row(np.asarray(x, dtype=np.float64), T, k, p, mp, seed, pos)
+    except Exception as e:
+        return f"raised {e!r} for x={x} T={T} k={k} p={p} mp={mp}"
+    if near:
+        return None
+    if r.support.tolist() != S:
+        return f"support {r.support.tolist()} != {S} for x={x} T={T} k={k} p={p} mp={mp}"
+    m = max(x[i] for i in S)
+    lse = math.log(math.fsum(math.exp((x[i] - m) / _f32(T)) for i in S))
+    want = np.array([(x[i] - m) / _f32(T) - lse for i in S])
+    if np.max(np.abs(r.logprobs.astype(np.float64) - want)) > 2e-6:
+        return f"logprobs {r.logprobs} != {want} for x={x}"
+    u = token_uniforms(np.array(S), seed, pos)
+    score = [(x[i] - m) / _f32(T) - math.log(-math.log(u[j])) for j, i in enumerate(S)]
+    best = max(score)
+    tok = min(i for j, i in enumerate(S) if score[j] == best)
+    if r.token != tok:
+        return f"token {r.token} != {tok} for x={x}"
+    return None
+
+
+LEVELS = (1.0, 0.0, -0.75, -math.inf)
+
+
+def pin_brute_force(sample_row, max_v=6, full_grid_v=4, rng_seed=0, stop_after=None):
+    """Exhaustive comparison over every logit vector of length <= max_v drawn from a 4-level grid
+    (so every tie pattern and -inf exclusions occur), against the per-token closed form. Vectors
+    with V <= full_grid_v run the whole parameter grid; longer ones a seeded sample of it."""
+    ks = (-1, 0, 1, 2, 3, 5)
+    ps = (0.0, 0.5, 0.8, 1.0)
+    mps = (0.0, 0.3, 1.0)
+    Ts = (0.5, 2.0)
+    grid = list(itertools.product(ks, ps, mps, Ts))
+    rng = np.random.default_rng(rng_seed)
+    fails = []
+    for V in range(1, max_v + 1):
+        for x in itertools.product(LEVELS, repeat=V):
+            if all(v == -math.inf for v in x):
+                continue
+            combos = grid if V <= full_grid_v else [grid[i] for i in rng.choice(len(grid), 3, replace=False)]
+            for (k, p, mp, T) in combos:
+                f = _check_against_brute(sample_row, list(x), T, k, p, mp, 7 + V, 3)
+                if f:
+                    fails.append(f)
+                    if stop_after and len(fails) >= stop_after:
+                        return fails
+    return fails
+
+
+def pin_special_cases(sample_row, rng_seed=1):
+    """Cases that reduce to textbook or library routines."""
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(rng_seed)
+    fails = []
+    for trial in range(4):
+        V = 700
+        x = (rng.standard_normal(V) * 2).astype(np.float32).astype(np.float64)
+        x[rng.choice(V, 20, replace=False)] = -np.inf
+        T = [0.7, 1.0, 1.9, 0.35][trial]
+        F = np.nonzero(np.isfinite(x))[0]
+        # No filter at all: the support is every finite token and logprobs are log_softmax(x/T).
+        r = sample_row(x, T, -1, 1.0, 0.0, trial, 0)
+        if sorted(r.support.tolist()) != F.tolist():
+            fails.append("unfiltered support is not the finite set")
+        else:
+            ref = log_softmax(x[F] / _f32(T))
+            got = np.empty(V)
+            got[r.support] = r.logprobs
+            if np.max(np.abs(got[F] - ref)) > 1e-5:
+                fails.append("unfiltered logprobs differ from scipy log_softmax")
+        # Distinct logits, top-k only: the set is numpy's top-k and does not depend on T.
+        k = [1, 10, 64, 300][trial]
+        xs = x[F]
+        if np.unique(xs).size == xs.size:
+            want = set(F[np.argsort(-xs, kind="stable")[:k]].tolist())
+            for TT in (0.5, 1.0, 3.0):
+                rr = sample_row(x, TT, k, 1.0, 0.0, trial, 0)
+                if set(rr.support.tolist()) != want:
+                    fails.append(f"top-{k} set differs from argsort at T={TT}")
+        # top_p = 0 and min_p = 1 keep exactly the top tie group.
+        xt = x.copy()
+        top = np.max(xt[F])
+        tied = rng.choice(F, 3, replace=False)
+        xt[tied] = top
+        want = sorted(np.nonzero(xt == top)[0].tolist())
+        for (p, mp) in ((0.0, 0.0), (1.0, 1.0), (0.0, 1.0)):
+            rr = sample_row(xt, T, -1, p, mp, trial, 0)
+            if rr.support.tolist() != want:
+                fails.append(f"top_p={p} min_p={mp} is not the top tie group")
+        # Greedy: numpy's argmax (first index of the maximum), width 1, logprob 0.
+        g = sample_row(xt, 0.0, 5, 0.9, 0.0, trial, 0)
+        if g.token != int(np.argmax(np.where(np.isfinite(xt), xt, -np.inf))) or g.L != 1 or g.logprobs[0] != 0.0:
+            fails.append("greedy row is not argmax / width 1 / logprob 0")
+    return fails
+
+
+def pin_race_distribution(sample_row, draws=6000):
+    """The exponential race draws token i with probability w_i / sum(w) (chi-square, 3 dof)."""
+    from scipy.stats import chisquare
+    probs = np.array([0.4, 0.3, 0.2, 0.1])
+    x = np.log(probs)
+    counts = np.zeros(4)
+    for s in range(draws):
+        counts[sample_row(x, 1.0, -1, 1.0, 0.0, 10_000 + s, 17).token] += 1
+    p = chisquare(counts, probs * draws).pvalue
+    return [] if p > 1e-4 else [f"race frequencies {counts} reject w/Z (p={p:.2e})"]
