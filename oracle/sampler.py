@@ -38,8 +38,9 @@ Readings taken where the pages are silent or disagree (each is a documented choi
   R8 any NaN or +inf logit makes the row NONFINITE; a row with no finite logit is NO_SUPPORT;
      invalid parameters (negative / non-finite / subnormal temperature, top_p or min_p NaN or
      outside [0, 1]) make it INVALID_PARAM; such rows return token -1 and an empty capture;
-  R9 capture slot j is valid iff 0 <= optin_rows[j] < B and (j == 0 or optin_rows[j-1] <
-     optin_rows[j]); invalid slots get length 0 and a NaN selected logprob;
+  R9 capture slot j is valid iff 0 <= optin_rows[j] < B and optin_rows[j] exceeds every earlier
+     entry (so valid slots name distinct rows, in ascending order); invalid slots get length 0
+     and a NaN selected logprob;
   R10 logprobs are normalized over the full support even when the packed prefix is clamped.
 """
 from __future__ import annotations
@@ -196,10 +197,11 @@ class BatchResult:
 
 
 def slot_validity(optin_rows: np.ndarray, B: int) -> np.ndarray:
-    """R9: a capture slot is valid iff its row is in range and exceeds the previous slot's row."""
+    """R9: a capture slot is valid iff its row is in range and exceeds every earlier entry."""
     e = np.asarray(optin_rows, dtype=np.int64)
     ok = (e >= 0) & (e < B)
-    ok[1:] &= e[1:] > e[:-1]
+    if e.size > 1:
+        ok[1:] &= e[1:] > np.maximum.accumulate(e)[:-1]
     return ok
 
 

@@ -108,8 +108,11 @@ def test_overflow_and_status_rows():
 
 
 def test_slot_validity():
-    v = oracle.slot_validity(np.array([0, 2, 2, 1, 9, 5, -1], np.int32), 8)
-    assert v.tolist() == [True, True, False, False, False, False, False]
+    v = oracle.slot_validity(np.array([0, 2, 2, 1, 5, -1, 7, 3, 6, 8], np.int32), 8)
+    assert v.tolist() == [True, True, False, False, True, False, True, False, False, False]
+    # An out-of-range entry still raises the running maximum that later entries must exceed.
+    v = oracle.slot_validity(np.array([1, 9, 5], np.int32), 8)
+    assert v.tolist() == [True, False, False]
     assert oracle.slot_validity(np.array([1, 3, 7], np.int32), 8).all()
 
 
