@@ -1,0 +1,124 @@
+/*
+ * tsc.h -- batched top-k / top-p / min-p sampler with exact support capture, for AMD MI355X
+ * (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * What one call computes, per row r of a [B, V] logits matrix x (definitions from the pages):
+ *   - weights w_i = exp((x_i - max x) / T) over the finite logits (a temperature softmax without
+ *     its normalizer); a -inf logit is an excluded token (vLLM "Sampling Mask / Distribution
+ *     Replay" article, "How it works", steps 1-2);
+ *   - joint top-k and top-p on that one distribution, as thresholds that keep every token tied
+ *     with a cutoff, so the support may hold more than k tokens; top-p keeps a token when the mass
+ *     of the tokens with strictly larger logit is at most top_p times the total mass; then min-p
+ *     keeps w_i >= min_p (sglang PR #36630 summary, "Implementation breakdown" items 2-3 and the
+ *     "Key code" tie test);
+ *   - the token, drawn by the exponential race argmax_i w_i / E_i over the support (Gaudi
+ *     cookbook "topk-subset-sampler", "The fix"), with E_i = -ln u_i and u_i a Philox4x32-10
+ *     uniform keyed by the row's seed and counter (token id / 4, 0, position lo, position hi),
+ *     word id % 4, u = (2 * (word >> 9) + 1) / 2^24 (Salmon et al., SC'11); equal scores go to
+ *     the lowest id;
+ *   - for opt-in rows only: the support S = {i | w_i > 0 after filtering} packed as token ids in
+ *     (logit descending, id ascending) order, its length clamped to the packed width W, the
+ *     logprobs log(w_i / sum_S w) and the sampled token's logprob (sglang PR #40986, "Contract",
+ *     "Design" and "Checks removed": no opt-in costs nothing, lengths are clamped to the packed
+ *     width, a wider support has OVERFLOW status, a greedy row has width 1 and length 1; its
+ *     "Correctness" section: the selected logprob equals the token's support logprob).
+ *
+ * Conventions: all array arguments are DEVICE pointers on the current HIP device unless noted.
+ * The call is asynchronous on `stream` (a hipStream_t passed as void*; NULL = default stream);
+ * outputs are valid once the stream has synchronized. The caller owns every buffer; the library
+ * keeps no per-call state and never allocates device memory on this path. The return code
+ * covers host-checkable errors only; per-row data problems go to row_status without a host sync.
+ */
+#ifndef TSC_H_
+#define TSC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of the host entry points. */
+enum {
+  TSC_OK = 0,
+  TSC_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad dtype, misaligned logits        */
+  TSC_ERR_UNSUPPORTED = 2,      /* a valid request this build does not serve (W too large)     */
+  TSC_ERR_WORKSPACE = 3,        /* workspace smaller than tsc_workspace_size()                 */
+  TSC_ERR_HIP = 4               /* the HIP runtime reported an error at launch                  */
+};
+
+/* Logits element types. */
+enum { TSC_DTYPE_F32 = 0, TSC_DTYPE_BF16 = 1 };
+
+/* Per-row status codes written to row_status. */
+enum {
+  TSC_ROW_OK = 0,
+  TSC_ROW_OVERFLOW = 1,      /* opt-in row whose support is wider than W: the first W entries of
+                                the ordered support are written, logprobs still use the full S */
+  TSC_ROW_NO_SUPPORT = 2,    /* every logit is -inf                                            */
+  TSC_ROW_NONFINITE = 3,     /* some logit is NaN or +inf                                       */
+  TSC_ROW_INVALID_PARAM = 4  /* temperature negative / non-finite / subnormal, or top_p or min_p
+                                NaN or outside [0, 1]                                          */
+};
+
+/* Largest packed width W this build accepts. */
+#define TSC_MAX_PACKED_WIDTH 16384
+
+/*
+ * tsc_sample_with_mask -- sample one token per row and capture the support of opt-in rows.
+ *
+ * logits       [B, V] row-major with row stride ld >= V elements; float32 or bfloat16 (raw bits)
+ *              per dtype; naturally aligned for its element type. Read only.
+ * dtype        TSC_DTYPE_F32 or TSC_DTYPE_BF16.
+ * B, V, ld     batch rows (>= 0), vocabulary size (1 <= V < 2^31), row stride in elements.
+ * temperature  [B] float32: 0 = greedy (first index of the maximum, width-1 support, logprob 0);
+ *              otherwise a normal positive finite value.
+ * top_k        [B] int32: <= 0 or >= the number of finite logits disables the filter.
+ * top_p        [B] float32 in [0, 1]; 1 disables it; 0 keeps only the top tie group.
+ * min_p        [B] float32 in [0, 1]; 0 disables it.
+ * optin_rows   [R] int32 capture rows; slot j is valid iff 0 <= optin_rows[j] < B and it exceeds
+ *              every earlier entry (a strictly ascending list in range makes every slot valid).
+ *              An invalid slot gets lengths[j] = 0 and selected_logprob[j] = NaN. May be NULL
+ *              when R = 0.
+ * R            number of capture slots, 0 <= R <= B. With R = 0 no capture work runs and
+ *              packed_ids, logprobs, lengths and selected_logprob may be NULL.
+ * seeds        [B] uint64 per-row Philox key.
+ * positions    [B] uint64 per-row Philox counter words (e.g. the decode position).
+ * W            packed width, 1 <= W <= TSC_MAX_PACKED_WIDTH (ignored when R = 0).
+ * tokens       [B] int32 out: sampled token id; -1 when row_status >= TSC_ROW_NO_SUPPORT.
+ * row_status   [B] int8 out: one of TSC_ROW_*. OVERFLOW is reported for captured rows only.
+ * packed_ids   [R, W] int32 out: slot j's first lengths[j] entries hold the support ids in
+ *              (logit descending, id ascending) order; entries past the length are unspecified.
+ * logprobs     [R, W] float32 out, aligned with packed_ids; NULL selects "selected mode" (ids and
+ *              the selected logprob only).
+ * lengths      [R] int32 out: min(|S|, W); 0 for invalid slots and rows with status >= 2.
+ * selected_logprob [R] float32 out: the sampled token's logprob (bit-identical to its packed
+ *              logprob entry); NaN for invalid slots and rows with status >= 2.
+ * workspace, workspace_bytes  device scratch of at least tsc_workspace_size() bytes (may be
+ *              NULL when that is 0).
+ * stream       hipStream_t as void*.
+ * Returns TSC_OK or a TSC_ERR_* code; on an error nothing is launched.
+ */
+int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64_t V, int64_t ld,
+                             const float* temperature, const int32_t* top_k, const float* top_p,
+                             const float* min_p, const int32_t* optin_rows, int64_t R,
+                             const uint64_t* seeds, const uint64_t* positions, int32_t W,
+                             int32_t* tokens, int8_t* row_status, int32_t* packed_ids,
+                             float* logprobs, int32_t* lengths, float* selected_logprob,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device scratch bytes tsc_sample_with_mask needs for these sizes (currently always 0). */
+size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dtype);
+
+/* Static, human-readable name of a TSC_* return code. */
+const char* tsc_status_string(int32_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t tsc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSC_H_ */

@@ -1,0 +1,78 @@
+"""Comparison of a library call's outputs with the oracle's, element by element.
+
+The bar (north star of the sampler): support ids, lengths and order bit-exact, tokens equal,
+logprobs within 1e-5 absolute, except on rows the oracle reports as near a decision boundary
+(top-p mass within 1e-5 of top_p, min-p within 1e-6, top-two race scores within 1e-6), which are
+counted and only checked for invariants.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LOGPROB_ATOL = 1e-5
+
+
+def to_numpy_outputs(out) -> dict:
+    """SampleOutput (torch) -> dict of numpy arrays."""
+    return {
+        "tokens": out.tokens.cpu().numpy(),
+        "row_status": out.row_status.cpu().numpy(),
+        "packed_ids": out.packed_ids.cpu().numpy(),
+        "lengths": out.lengths.cpu().numpy(),
+        "logprobs": None if out.logprobs is None else out.logprobs.cpu().numpy(),
+        "selected_logprob": out.selected_logprob.cpu().numpy(),
+    }
+
+
+def compare(got: dict, ref, optin_rows, rows=None):
+    """Return (errors, stats). ``ref`` is an ``oracle.BatchResult``; ``rows`` limits the check
+    to the rows the oracle computed."""
+    errs = []
+    stats = {"rows": 0, "flagged": 0, "overflow": 0, "exact_lp": 0, "lp_entries": 0,
+             "max_lp_err": 0.0}
+    B = len(got["tokens"])
+    todo = range(B) if rows is None else [int(r) for r in rows]
+    slot = {int(optin_rows[j]): j for j in range(len(optin_rows)) if ref.slot_valid[j]}
+    for j in range(len(optin_rows)):
+        if not ref.slot_valid[j]:
+            if got["lengths"][j] != 0 or not np.isnan(got["selected_logprob"][j]):
+                errs.append(f"invalid slot {j}: length {got['lengths'][j]}")
+    for r in todo:
+        rr = ref.rows[r]
+        stats["rows"] += 1
+        if int(got["row_status"][r]) != int(ref.row_status[r]):
+            errs.append(f"row {r}: status {got['row_status'][r]} != {ref.row_status[r]}")
+            continue
+        if ref.row_status[r] == 1:
+            stats["overflow"] += 1
+        if rr.flagged:
+            stats["flagged"] += 1
+            continue
+        if int(got["tokens"][r]) != int(ref.tokens[r]):
+            errs.append(f"row {r}: token {got['tokens'][r]} != {ref.tokens[r]} (gap {rr.race_gap:.3g})")
+        j = slot.get(r)
+        if j is None:
+            continue
+        n = int(ref.lengths[j])
+        if int(got["lengths"][j]) != n:
+            errs.append(f"row {r}: length {got['lengths'][j]} != {n} (L={rr.L})")
+            continue
+        gi = got["packed_ids"][j, :n]
+        if not np.array_equal(gi, ref.packed_ids[j, :n]):
+            bad = int(np.nonzero(gi != ref.packed_ids[j, :n])[0][0])
+            errs.append(f"row {r}: packed ids differ first at {bad}: {gi[bad]} != {ref.packed_ids[j, bad]}")
+            continue
+        if got["logprobs"] is not None and n:
+            d = np.abs(got["logprobs"][j, :n].astype(np.float64) - ref.logprobs[j, :n].astype(np.float64))
+            stats["max_lp_err"] = max(stats["max_lp_err"], float(d.max()))
+            stats["exact_lp"] += int(np.count_nonzero(d == 0))
+            stats["lp_entries"] += n
+            if d.max() > LOGPROB_ATOL or not np.all(np.isfinite(got["logprobs"][j, :n]) == np.isfinite(ref.logprobs[j, :n])):
+                errs.append(f"row {r}: logprob error {d.max():.3g}")
+        gs, rs = float(got["selected_logprob"][j]), float(ref.selected_logprob[j])
+        if np.isnan(rs) or np.isnan(gs):
+            if not (np.isnan(rs) and np.isnan(gs)):
+                errs.append(f"row {r}: selected logprob {gs} vs {rs}")
+        elif not abs(gs - rs) <= LOGPROB_ATOL:
+            errs.append(f"row {r}: selected logprob error {abs(gs - rs):.3g}")
+    return errs, stats

@@ -1,0 +1,69 @@
+"""The C-ABI library loads and exports every entry point the header declares; host-side
+argument checks return their documented codes without touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsc.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsc_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import top_support_capture_amd as tsc
+    return tsc.library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["tsc_sample_with_mask", "tsc_status_string", "tsc_version",
+                                    "tsc_workspace_size"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tsc_status_string(0) == b"TSC_OK"
+    assert lib.tsc_status_string(3) == b"TSC_ERR_WORKSPACE"
+    assert lib.tsc_status_string(99) == b"TSC_UNKNOWN_STATUS"
+    assert lib.tsc_version() >= 100
+    assert lib.tsc_workspace_size(256, 151936, 256, 2048, 1) == 0
+
+
+def _call(lib, **kw):
+    args = dict(logits=0x1000, dtype=1, B=4, V=100, ld=100, temperature=8, top_k=8, top_p=8,
+                min_p=8, optin_rows=8, R=2, seeds=8, positions=8, W=16, tokens=8, row_status=8,
+                packed_ids=8, logprobs=8, lengths=8, selected_logprob=8, workspace=None, wsb=0,
+                stream=None)
+    args.update(kw)
+    return lib.tsc_sample_with_mask(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 1), (dict(B=-1), 1), (dict(V=0), 1), (dict(ld=99), 1), (dict(R=5), 1),
+    (dict(R=-1), 1), (dict(W=0), 1), (dict(W=16385), 2), (dict(logits=0x1001), 1),
+    (dict(logits=None), 1), (dict(seeds=None), 1), (dict(tokens=None), 1),
+    (dict(optin_rows=None), 1), (dict(lengths=None), 1), (dict(B=0, R=0), 0),
+])
+def test_host_argument_checks(lib, kw, code):
+    # Every case returns before any HIP call, so this runs without a GPU.
+    assert _call(lib, **kw) == code
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import top_support_capture_amd as tsc
+    x = torch.zeros((2, 8), dtype=torch.float16)
+    z = torch.zeros(2)
+    with pytest.raises(ValueError):
+        tsc.sample_with_mask(x, z, z.int(), z, z, z.int(), z.long(), z.long(), 4)

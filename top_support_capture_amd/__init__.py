@@ -1,0 +1,134 @@
+"""MI355X-native batched top-k / top-p / min-p sampler with exact support capture.
+
+Python binding of the C-ABI library ``libtsc.so`` (declared in ``include/tsc.h``). This module
+only marshals arguments: it checks tensor devices and dtypes, allocates the output tensors with
+PyTorch on the logits' device, and calls ``tsc_sample_with_mask`` on the current HIP stream.
+Every step of the sampling runs in the library's HIP kernels; there is no fallback, and the
+import fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch  # must come first: the library binds to the HIP runtime PyTorch has loaded
+
+__all__ = ["sample_with_mask", "SampleOutput", "workspace_size", "library", "LIB_PATH",
+           "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
+           "MAX_PACKED_WIDTH", "TscError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsc.so")
+
+TSC_DTYPE_F32, TSC_DTYPE_BF16 = 0, 1
+ROW_OK, ROW_OVERFLOW, ROW_NO_SUPPORT, ROW_NONFINITE, ROW_INVALID_PARAM = 0, 1, 2, 3, 4
+MAX_PACKED_WIDTH = 16384
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class TscError(RuntimeError):
+    def __init__(self, code: int, name: str):
+        super().__init__(f"tsc_sample_with_mask failed: {name} ({code})")
+        self.code = code
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libtsc.so`` (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m top_support_capture_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.tsc_sample_with_mask.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P, I64, P, P, I32,
+                                         P, P, P, P, P, P, P, SZ, P]
+    lib.tsc_sample_with_mask.restype = I32
+    lib.tsc_workspace_size.argtypes = [I64, I64, I64, I32, I32]
+    lib.tsc_workspace_size.restype = SZ
+    lib.tsc_status_string.argtypes = [I32]
+    lib.tsc_status_string.restype = ctypes.c_char_p
+    lib.tsc_version.argtypes = []
+    lib.tsc_version.restype = I32
+    _lib = lib
+    return lib
+
+
+class SampleOutput(NamedTuple):
+    tokens: torch.Tensor            # int32 [B]
+    packed_ids: torch.Tensor        # int32 [R, W]
+    lengths: torch.Tensor           # int32 [R]
+    logprobs: Optional[torch.Tensor]  # float32 [R, W] (None in selected mode)
+    selected_logprob: torch.Tensor  # float32 [R]
+    row_status: torch.Tensor        # int8 [B]
+
+
+def workspace_size(B: int, V: int, R: int, W: int, dtype: torch.dtype) -> int:
+    dt = TSC_DTYPE_BF16 if dtype == torch.bfloat16 else TSC_DTYPE_F32
+    return int(library().tsc_workspace_size(B, V, R, W, dt))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, dtype, n: int, dev) -> None:
+    if t.device != dev or t.dtype != dtype or t.dim() != 1 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape [{n}] on {dev}")
+
+
+def sample_with_mask(logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
+                     top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
+                     seeds: torch.Tensor, positions: torch.Tensor, W: int,
+                     return_logprobs: bool = True, out: Optional[SampleOutput] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> SampleOutput:
+    """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16, unit column stride)
+    and capture the support of the rows listed in ``optin_rows`` (int32, ascending).
+
+    ``temperature``/``top_p``/``min_p`` are float32 [B], ``top_k`` int32 [B], ``seeds`` and
+    ``positions`` int64 [B] holding the uint64 bit patterns. Outputs are allocated on the
+    logits' device unless ``out`` supplies them. Runs asynchronously on ``stream`` (default: the
+    current stream)."""
+    lib = library()
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B, V] with unit column stride")
+    if logits.dtype == torch.float32:
+        dt = TSC_DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = TSC_DTYPE_BF16
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    dev = logits.device
+    B, V = logits.shape
+    ld = logits.stride(0) if B > 1 else V
+    R = int(optin_rows.numel())
+    _check(temperature, "temperature", torch.float32, B, dev)
+    _check(top_k, "top_k", torch.int32, B, dev)
+    _check(top_p, "top_p", torch.float32, B, dev)
+    _check(min_p, "min_p", torch.float32, B, dev)
+    _check(optin_rows, "optin_rows", torch.int32, R, dev)
+    _check(seeds, "seeds", torch.int64, B, dev)
+    _check(positions, "positions", torch.int64, B, dev)
+    if out is None:
+        Wc = max(int(W), 1)
+        out = SampleOutput(
+            tokens=torch.empty(B, dtype=torch.int32, device=dev),
+            packed_ids=torch.empty((R, Wc), dtype=torch.int32, device=dev),
+            lengths=torch.empty(R, dtype=torch.int32, device=dev),
+            logprobs=torch.empty((R, Wc), dtype=torch.float32, device=dev) if return_logprobs else None,
+            selected_logprob=torch.empty(R, dtype=torch.float32, device=dev),
+            row_status=torch.empty(B, dtype=torch.int8, device=dev))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    code = lib.tsc_sample_with_mask(
+        logits.data_ptr(), dt, B, V, ld, temperature.data_ptr(), top_k.data_ptr(),
+        top_p.data_ptr(), min_p.data_ptr(), _ptr(optin_rows) if R else None, R,
+        seeds.data_ptr(), positions.data_ptr(), int(W), out.tokens.data_ptr(),
+        out.row_status.data_ptr(), _ptr(out.packed_ids) if R else None,
+        _ptr(out.logprobs) if (R and out.logprobs is not None) else None,
+        _ptr(out.lengths) if R else None, _ptr(out.selected_logprob) if R else None,
+        None, 0, s.cuda_stream)
+    if code != 0:
+        raise TscError(code, lib.tsc_status_string(code).decode())
+    return out

@@ -1,0 +1,86 @@
+// Host side of the C ABI declared in include/tsc.h: argument validation and kernel launch on the
+// caller's stream. Nothing here allocates device memory or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "tsc.h"
+#include "tsc_general.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+template <int DT>
+hipError_t launch_general(const tsc::SampleArgs& a, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_general_kernel<DT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)tsc::kGeneralDynLds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(tsc::sample_general_kernel<DT>, dim3((unsigned)a.B), dim3(tsc::kThreads),
+                     tsc::kGeneralDynLds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tsc_version(void) { return kVersion; }
+
+const char* tsc_status_string(int32_t status) {
+  switch (status) {
+    case TSC_OK: return "TSC_OK";
+    case TSC_ERR_INVALID_ARGUMENT: return "TSC_ERR_INVALID_ARGUMENT";
+    case TSC_ERR_UNSUPPORTED: return "TSC_ERR_UNSUPPORTED";
+    case TSC_ERR_WORKSPACE: return "TSC_ERR_WORKSPACE";
+    case TSC_ERR_HIP: return "TSC_ERR_HIP";
+    default: return "TSC_UNKNOWN_STATUS";
+  }
+}
+
+size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dtype) {
+  (void)B, (void)V, (void)R, (void)W, (void)dtype;
+  return 0;
+}
+
+int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64_t V, int64_t ld,
+                             const float* temperature, const int32_t* top_k, const float* top_p,
+                             const float* min_p, const int32_t* optin_rows, int64_t R,
+                             const uint64_t* seeds, const uint64_t* positions, int32_t W,
+                             int32_t* tokens, int8_t* row_status, int32_t* packed_ids,
+                             float* logprobs, int32_t* lengths, float* selected_logprob,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  if (dtype != TSC_DTYPE_F32 && dtype != TSC_DTYPE_BF16) return TSC_ERR_INVALID_ARGUMENT;
+  if (B < 0 || V < 1 || V > INT32_MAX - 16 || ld < V || R < 0 || R > B)
+    return TSC_ERR_INVALID_ARGUMENT;
+  if (B > 0x7FFFFFFF) return TSC_ERR_UNSUPPORTED;
+  if (B == 0) return TSC_OK;
+  const size_t esize = dtype == TSC_DTYPE_F32 ? 4 : 2;
+  if (!logits || (reinterpret_cast<uintptr_t>(logits) % esize) != 0)
+    return TSC_ERR_INVALID_ARGUMENT;
+  if (!temperature || !top_k || !top_p || !min_p || !seeds || !positions || !tokens || !row_status)
+    return TSC_ERR_INVALID_ARGUMENT;
+  if (R > 0) {
+    if (!optin_rows || !packed_ids || !lengths || !selected_logprob) return TSC_ERR_INVALID_ARGUMENT;
+    if (W < 1) return TSC_ERR_INVALID_ARGUMENT;
+    if (W > TSC_MAX_PACKED_WIDTH) return TSC_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < tsc_workspace_size(B, V, R, W, dtype)) return TSC_ERR_WORKSPACE;
+
+  tsc::SampleArgs a{logits, B, V, ld, temperature, top_k, top_p, min_p, optin_rows, R,
+                    seeds, positions, R > 0 ? W : 1, tokens, row_status, packed_ids,
+                    logprobs, lengths, selected_logprob};
+  (void)hipGetLastError();  // start from a clean error state so a launch error is ours
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t err = dtype == TSC_DTYPE_F32 ? launch_general<TSC_DTYPE_F32>(a, s)
+                                                : launch_general<TSC_DTYPE_BF16>(a, s);
+  return err == hipSuccess ? TSC_OK : TSC_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Device helpers shared by the sampler kernels: orderable keys, the Philox4x32-10 generator and
+// block-wide reductions for 1024-thread workgroups of 64-wide wavefronts (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsc.h"
+
+namespace tsc {
+
+constexpr int kThreads = 1024;
+constexpr int kWaveSize = 64;
+constexpr int kWaves = kThreads / kWaveSize;
+
+// ---- Logit element types -------------------------------------------------------------------
+// A key is an unsigned integer image of a logit whose order is the order of the values, with -0
+// and +0 mapped to one key (ties are judged on the value, so the two zeros tie).
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<TSC_DTYPE_BF16> {
+  using Bits = uint16_t;
+  static constexpr int kVec = 8;  // elements per 16-byte load
+  static constexpr int kKeyBits = 16;
+  static constexpr uint32_t kSign = 0x8000u, kMask = 0xFFFFu, kExpMask = 0x7F80u;
+  static constexpr uint32_t kNegInf = 0xFF80u;
+  __device__ static inline float to_float(uint32_t b) { return __uint_as_float(b << 16); }
+};
+
+template <>
+struct Elem<TSC_DTYPE_F32> {
+  using Bits = uint32_t;
+  static constexpr int kVec = 4;
+  static constexpr int kKeyBits = 32;
+  static constexpr uint32_t kSign = 0x80000000u, kMask = 0xFFFFFFFFu, kExpMask = 0x7F800000u;
+  static constexpr uint32_t kNegInf = 0xFF800000u;
+  __device__ static inline float to_float(uint32_t b) { return __uint_as_float(b); }
+};
+
+template <class E>
+__device__ inline uint32_t key_of(uint32_t b) {
+  if (b == E::kSign) b = 0;  // -0 -> +0
+  return (b & E::kSign) ? (~b & E::kMask) : (b | E::kSign);
+}
+
+template <class E>
+__device__ inline uint32_t bits_of_key(uint32_t k) {
+  return (k & E::kSign) ? (k ^ E::kSign) : (~k & E::kMask);
+}
+
+template <class E>
+__device__ inline bool is_finite_bits(uint32_t b) {
+  return (b & E::kExpMask) != E::kExpMask;
+}
+
+// ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11, section 4) ---------------------------
+// Per round, with (hi_a, lo_a) = M0 * X0 and (hi_b, lo_b) = M1 * X2 as 64-bit products:
+// X' = (hi_b ^ X1 ^ K0, lo_b, hi_a ^ X3 ^ K1, lo_a); the key advances by the Weyl constants.
+__device__ inline uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint32_t hi_a = __umulhi(M0, x.x), lo_a = M0 * x.x;
+    const uint32_t hi_b = __umulhi(M1, x.z), lo_b = M1 * x.z;
+    x = make_uint4(hi_b ^ x.y ^ k0, lo_b, hi_a ^ x.w ^ k1, lo_a);
+  }
+  return x;
+}
+
+// The race uniform of token `id` in a row: Philox keyed by the seed, counter (id / 4, 0,
+// position), output word id % 4; the 23 high bits k give u = (2k + 1) / 2^24 in (0, 1).
+__device__ inline uint32_t race_word(uint32_t id, uint64_t seed, uint64_t position) {
+  const uint4 r = philox4x32_10(
+      make_uint4(id >> 2, 0u, (uint32_t)position, (uint32_t)(position >> 32)),
+      (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t j = id & 3u;
+  return j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
+}
+
+__device__ inline double race_uniform(uint32_t id, uint64_t seed, uint64_t position) {
+  return (double)(2u * (race_word(id, seed, position) >> 9) + 1u) * 0x1p-24;
+}
+
+// ---- Block reductions (fixed order, hence deterministic) -----------------------------------
+template <class T, class Op>
+__device__ inline T wave_reduce(T v, Op op) {
+#pragma unroll
+  for (int o = kWaveSize / 2; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o, kWaveSize));
+  return v;
+}
+
+// Reduces `v` over the workgroup; every thread receives the result. `scratch` is shared memory
+// of at least kWaves * 8 bytes; the leading barrier makes back-to-back calls safe.
+template <class T, class Op>
+__device__ inline T block_reduce(T v, Op op, uint64_t* scratch) {
+  v = wave_reduce(v, op);
+  T* s = reinterpret_cast<T*>(scratch);
+  __syncthreads();
+  if ((threadIdx.x & (kWaveSize - 1)) == 0) s[threadIdx.x / kWaveSize] = v;
+  __syncthreads();
+  T r = s[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = op(r, s[i]);
+  return r;
+}
+
+struct MaxOp {
+  template <class T>
+  __device__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+struct MinOp {
+  template <class T>
+  __device__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+struct SumOp {
+  template <class T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+
+}  // namespace tsc
