@@ -171,14 +171,17 @@ def sample_row(x: np.ndarray, T: float, top_k: int, top_p: float, min_p: float,
     else:
         race_gap = np.inf
 
-    # Boundary reports (near-threshold rows are counted, not failed).
+    # Boundary reports (near-threshold rows are counted, not failed). The first tie group is
+    # never near a boundary: no mass precedes it and its weight is exactly 1 in any arithmetic,
+    # so top-p and min-p keep it exactly whatever the rounding.
+    later = np.arange(starts.size) > 0
     top_p_flag = False
     if top_p < 1.0:
-        cand = pass_k & pass_m
+        cand = pass_k & pass_m & later
         top_p_flag = bool(np.any(np.abs(C[starts][cand] / Z - top_p) <= TOP_P_EPS))
     min_p_flag = False
     if min_p > 0.0:
-        cand = pass_k & pass_p
+        cand = pass_k & pass_p & later
         min_p_flag = bool(np.any(np.abs(scaled[starts][cand] - np.log(min_p)) <= MIN_P_EPS))
 
     return RowResult(ROW_OK, token, ids[:L].astype(np.int64), lp, race_gap, top_p_flag, min_p_flag)

@@ -153,3 +153,14 @@ def test_pins_catch_planted_mistake(name):
     if not fails:
         fails = pins.pin_race_distribution(fn, draws=3000)
     assert fails, f"no pin detects mutation {name}"
+
+
+def test_first_tie_group_is_never_reported_as_near_a_boundary():
+    x = np.array([1.0, 1.0, 0.5, -0.25, -2.0])
+    for (p, mp) in ((0.0, 0.0), (1.0, 1.0), (0.0, 1.0)):
+        r = oracle.sample_row(x, 1.0, -1, p, mp, 3, 0)
+        assert r.support.tolist() == [0, 1] and not r.top_p_flag and not r.min_p_flag
+    # A later group within the window still is.
+    w = np.exp(np.array([0.0, -0.5]))
+    r = oracle.sample_row(np.array([0.0, -0.5]), 1.0, -1, float(np.float32(w[0] / w.sum())), 0.0, 3, 0)
+    assert r.top_p_flag
