@@ -233,3 +233,71 @@ def test_repeated_calls_are_bit_identical():
     for j, n in enumerate(a["lengths"]):
         assert a["packed_ids"][j, :n].tobytes() == b["packed_ids"][j, :n].tobytes()
         assert a["logprobs"][j, :n].tobytes() == b["logprobs"][j, :n].tobytes()
+
+
+def _fast_rows(rng, V):
+    """bf16-representable rows for the single-read path (V in its range, k small)."""
+    grid = np.round(rng.standard_normal(V) * 2.5 * 8) / 8          # many ties, like workload 3
+    gauss = rng.standard_normal(V) * 1.5
+    neg = gauss.copy(); neg[rng.choice(V, V // 4, replace=False)] = -np.inf
+    nan = gauss.copy(); nan[V - 3] = np.nan
+    pinf = gauss.copy(); pinf[V // 3] = np.inf
+    allneg = np.full(V, -np.inf)
+    # Top values hidden away from the first load of every wave segment: the early cutoff is too
+    # low, the stash overflows and the row must take the general path.
+    seg = V // 16
+    hidden = rng.standard_normal(V)
+    for w in range(16):
+        hidden[w * seg + 512:(w + 1) * seg] += 6.0
+    # The first loads hold the row's largest values but fewer than k of them: cutoff too high,
+    # fewer than k candidates, general path.
+    front = rng.standard_normal(V) - 5.0
+    for w in range(16):
+        front[w * seg:w * seg + 16] = 8.0 + rng.standard_normal(16)
+    # A support of more than 256 distinct keys within the histogram's key span (values spread
+    # over six binades above a dense filler): the capture tables are too small, general path.
+    spread = rng.uniform(1.0, 1.9, V)
+    spread[rng.choice(V, 900, replace=False)] = np.geomspace(2.0, 60.0, 900)
+    return dict(grid=grid, gauss=gauss, neg=neg, nan=nan, pinf=pinf, allneg=allneg,
+                hidden=hidden, front=front, spread=spread)
+
+
+FAST_PARAMS = [
+    # (label, row, T, k, p, min_p)
+    ("grid_k1024_p95", "grid", 0.8, 1024, 0.95, 0.0),
+    ("grid_k64_p1", "grid", 1.0, 64, 1.0, 0.0),
+    ("grid_k1_ties", "grid", 1.0, 1, 1.0, 0.0),
+    ("grid_k1536", "grid", 1.2, 1536, 0.9, 0.0),
+    ("gauss_k300_p5", "gauss", 0.7, 300, 0.5, 0.0),
+    ("gauss_k1000_p0", "gauss", 1.0, 1000, 0.0, 0.0),
+    ("gauss_minp", "gauss", 1.0, 1200, 1.0, 0.2),
+    ("gauss_minp_p", "gauss", 0.9, 800, 0.8, 0.05),
+    ("neg_inf", "neg", 1.0, 500, 0.9, 0.0),
+    ("nan_p", "nan", 1.0, 100, 0.9, 0.0),
+    ("nan_nop", "nan", 1.0, 100, 1.0, 0.0),
+    ("pos_inf", "pinf", 1.0, 100, 1.0, 0.0),
+    ("all_neg_inf", "allneg", 1.0, 100, 0.9, 0.0),
+    ("hidden_top", "hidden", 1.0, 1024, 0.95, 0.0),
+    ("front_loaded", "front", 1.0, 1024, 1.0, 0.0),
+    ("spread_keys", "spread", 5.0, 1000, 1.0, 0.0),
+    ("tiny_T", "gauss", 1e-3, 50, 0.9, 0.0),
+    ("greedy", "grid", 0.0, 50, 0.9, 0.0),
+]
+
+
+@pytest.mark.parametrize("V", [32768, 151936])
+def test_single_read_path_rows(V):
+    rng = np.random.default_rng(77)
+    rows = _fast_rows(rng, V)
+    names = [e[0] for e in FAST_PARAMS]
+    x = [rows[e[1]] for e in FAST_PARAMS]
+    cols = list(zip(*[e[2:] for e in FAST_PARAMS]))
+    for W in (2048, 16):
+        wl = make(f"fast_V{V}_W{W}", x, "bf16", T=np.array(cols[0]), k=np.array(cols[1]),
+                  p=np.array(cols[2]), mp=np.array(cols[3]), W=W)
+        log(f"case single-read path V={V} W={W}: {names}")
+        got = run_gpu(wl)
+        ref = oracle_of(wl)
+        errs, stats = compare(got, ref, wl.optin_rows)
+        assert errs == [], [(e, names[int(e.split()[1].rstrip(':'))]) if e.startswith("row") else e for e in errs]
+        check(wl, got, ref, max_flagged_frac=0.2)

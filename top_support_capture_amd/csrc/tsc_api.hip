@@ -5,24 +5,26 @@
 #include <mutex>
 
 #include "tsc.h"
-#include "tsc_general.h"
+#include "tsc_fast.h"
 
 namespace {
 
 constexpr int32_t kVersion = 100;  // 0.1.0
 
+// One workgroup per row. Rows the single-read path serves run there; every other row runs the
+// general multi-pass algorithm inside the same launch.
 template <int DT>
-hipError_t launch_general(const tsc::SampleArgs& a, hipStream_t stream) {
+hipError_t launch_sampler(const tsc::SampleArgs& a, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_general_kernel<DT>),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_fast_kernel<DT>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)tsc::kGeneralDynLds);
+                                   (int)tsc::kFastDynLds);
   });
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(tsc::sample_general_kernel<DT>, dim3((unsigned)a.B), dim3(tsc::kThreads),
-                     tsc::kGeneralDynLds, stream, a);
+  hipLaunchKernelGGL(tsc::sample_fast_kernel<DT>, dim3((unsigned)a.B), dim3(tsc::kThreads),
+                     tsc::kFastDynLds, stream, a);
   return hipGetLastError();
 }
 
@@ -78,8 +80,8 @@ int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64
                     logprobs, lengths, selected_logprob};
   (void)hipGetLastError();  // start from a clean error state so a launch error is ours
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t err = dtype == TSC_DTYPE_F32 ? launch_general<TSC_DTYPE_F32>(a, s)
-                                                : launch_general<TSC_DTYPE_BF16>(a, s);
+  const hipError_t err = dtype == TSC_DTYPE_F32 ? launch_sampler<TSC_DTYPE_F32>(a, s)
+                                                : launch_sampler<TSC_DTYPE_BF16>(a, s);
   return err == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
 

@@ -88,23 +88,88 @@ __device__ inline double race_uniform(uint32_t id, uint64_t seed, uint64_t posit
   return (double)(2u * (race_word(id, seed, position) >> 9) + 1u) * 0x1p-24;
 }
 
-// ---- Block reductions (fixed order, hence deterministic) -----------------------------------
+// Workgroup barrier that orders LDS only: global loads still in flight stay in flight. Every
+// block-level exchange in these kernels goes through LDS, so this is the barrier they use.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---- Wavefront primitives on DPP (gfx9 encodings; every lane of the wave must be active) -----
+// A DPP move reads another lane's register in the same VALU instruction, without the LDS round
+// trip of a ds_bpermute shuffle. `old` is what lanes without a valid source keep.
+namespace dpp {
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF, class T>
+__device__ inline T dpp_mov(T old, T src) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                             __builtin_bit_cast(int, src), CTRL,
+                                                             ROW_MASK, 0xF, false));
+  } else {
+    const uint64_t o = __builtin_bit_cast(uint64_t, old), v = __builtin_bit_cast(uint64_t, src);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)v,
+                                                              CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32),
+                                                              (int)(uint32_t)(v >> 32), CTRL,
+                                                              ROW_MASK, 0xF, false);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+template <class T>
+__device__ inline T read_lane(T v, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+// op over the 64 lanes; every lane receives the result. op must be commutative and associative
+// (the combination order is fixed, so a floating-point sum is reproducible).
 template <class T, class Op>
 __device__ inline T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int o = kWaveSize / 2; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o, kWaveSize));
+  v = op(v, dpp_mov<dpp::kQuadSwap1>(v, v));
+  v = op(v, dpp_mov<dpp::kQuadSwap2>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor4>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor8>(v, v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
+// Inclusive scan under op with identity `id` (lane i receives op over lanes 0..i).
+template <class T, class Op>
+__device__ inline T wave_incl_scan(T v, Op op, T id) {
+  v = op(v, dpp_mov<dpp::kRowShr1>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr2>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr4>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr8>(id, v));
+  v = op(v, dpp_mov<dpp::kRowBcast15, 0xA>(id, v));
+  v = op(v, dpp_mov<dpp::kRowBcast31, 0xC>(id, v));
   return v;
 }
 
+// ---- Block reductions (fixed order, hence deterministic) -----------------------------------
 // Reduces `v` over the workgroup; every thread receives the result. `scratch` is shared memory
 // of at least kWaves * 8 bytes; the leading barrier makes back-to-back calls safe.
 template <class T, class Op>
 __device__ inline T block_reduce(T v, Op op, uint64_t* scratch) {
   v = wave_reduce(v, op);
   T* s = reinterpret_cast<T*>(scratch);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWaveSize - 1)) == 0) s[threadIdx.x / kWaveSize] = v;
-  __syncthreads();
+  lds_barrier();
   T r = s[0];
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) r = op(r, s[i]);

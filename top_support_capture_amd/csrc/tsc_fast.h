@@ -1,0 +1,688 @@
+// Single-read sampler kernel for bfloat16 rows (one 1024-thread workgroup per row).
+//
+// HBM is the bound: a row is read exactly once, with every 16-byte load of the row in flight at
+// once, and all per-element work happens while the loads land. Wave w owns a contiguous segment
+// of the row (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
+//
+//   1. Issue all loads. When the first one lands, a block-wide radix select over the lane maxima
+//      picks a cutoff theta that about twice top_k tokens of the row should exceed (the first
+//      loads of the 16 segments are a sample spread over the whole row).
+//   2. As each load lands: running maximum and (top_p < 1) an online sum of exp((x - max) / T)
+//      per lane; a ballot over "this load's maximum >= theta" stashes the whole 16-byte load in
+//      the wave's LDS stash, in id order.
+//   3. After the last load: row maximum m and total mass Z (block reductions), then the stash is
+//      expanded into candidate words (d << 18 | id) with d = key(m) - key(x), still in id order.
+//   4. A histogram over d of candidate counts and fixed-point masses, and one block scan, give
+//      the joint threshold exactly: the largest d with fewer than k tokens strictly above and
+//      (top_p < 1) mass strictly above <= top_p * Z; min-p drops candidates below its cutoff.
+//      theta was a true lower bound iff at least k candidates were found (checked here).
+//   5. Race over the survivors (Philox4x32-10 uniforms; float32 scores, float64 for the few within
+//      1e-4 of the best), then, for opt-in rows, the ordered capture: bins give each tie group's
+//      base position and a ballot multisplit ranks the group's members by id.
+// Any row this path cannot serve exactly (capacities, theta above the k-th value, greedy rows,
+// other dtypes or layouts) runs through general_row in the same workgroup.
+#pragma once
+
+#include "tsc_general.h"
+
+namespace tsc {
+
+constexpr int kFastLoads = 20;        // 16-byte loads per lane (segment of at most 20 * 512 values)
+constexpr int kLoadsFirst = 2;        // loads issued before the first one is awaited
+constexpr int kLoadsAhead = 4;        // software pipeline depth afterwards (loads in flight per lane)
+constexpr int kStashPerWave = 256;    // stashed loads per wave
+constexpr int kCandPerWave = 512;     // candidate words per wave
+constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
+constexpr int kMaxGroups = 256;       // distinct keys in a captured support
+constexpr int64_t kFastMinV = 16384;
+constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
+constexpr int32_t kFastMaxK = 1536;
+constexpr int kFixShift = 48;         // fixed-point weights: 2^48 * w, candidates <= 8192
+constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
+
+// LDS layout of the fast path (bytes from the dynamic buffer base).
+constexpr int kOffStash = 0;                                          // uint4 [16][256]
+constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16][256]
+constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
+constexpr int kOffCnt = kOffCand + kWaves * kCandPerWave * 4;         // u32 [1024]
+constexpr int kFastLdsEnd = kOffCnt + kDBins * 4;
+// Overlays of the stash region once it has been expanded:
+constexpr int kOffNoise = 0;                                      // f32 [16][512] race noise
+constexpr int kOffExclCnt = kOffNoise + kWaves * kCandPerWave * 4;    // u32 [1024] by d
+constexpr int kOffGroup = kOffExclCnt + kDBins * 4;               // u16 [1024] by d
+constexpr int kOffGrpCnt = kOffGroup + kDBins * 2;                // u32 [16][256] members per wave
+constexpr int kOffCursor = kOffGrpCnt + kWaves * kMaxGroups * 4;  // u32 [16][256] write cursors
+constexpr int kOffGrpBase = kOffCursor + kWaves * kMaxGroups * 4; // u32 [256]
+constexpr int kOffLpTab = kOffGrpBase + kMaxGroups * 4;           // f32 [256]
+constexpr int kOffOverlayEnd = kOffLpTab + kMaxGroups * 4;
+static_assert(kOffOverlayEnd <= kOffCand, "overlays must fit in the stash region");
+
+constexpr size_t kFastDynLds =
+    (size_t)kGeneralDynLds + sizeof(GeneralShared) > (size_t)kFastLdsEnd
+        ? (size_t)kGeneralDynLds + sizeof(GeneralShared)
+        : (size_t)kFastLdsEnd;
+
+// Per-wave partial results exchanged through LDS (one barrier per exchange).
+struct FastShared {
+  uint64_t red[kWaves];
+  uint32_t sel_cnt[2][kWaves][16];
+  int32_t slot_wmax[kWaves];
+  int32_t slot_hit[kWaves];
+  float wave_m[kWaves];
+  double wave_z[kWaves];
+  uint32_t wave_nan[kWaves];
+  uint32_t wave_stash[kWaves];
+  uint32_t wave_cand[kWaves];
+  uint32_t scan_c[kWaves], scan_g[kWaves];
+  uint64_t scan_m[kWaves];
+  float race_b1[kWaves], race_b2[kWaves];
+  int32_t race_id[kWaves];
+  uint32_t race_d[kWaves];
+  double ref_top[kWaves];
+  int32_t ref_id[kWaves];
+  uint32_t ref_d[kWaves];
+  int32_t dstar_w[kWaves];
+  uint32_t L_w[kWaves], G_w[kWaves];
+  uint64_t zs_w[kWaves];
+};
+
+__device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
+
+// Wave index, known to the compiler as wave-uniform (held in a scalar register).
+__device__ inline uint32_t wave_id() {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+struct SumU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct SumU64 {
+  __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a + b; }
+};
+struct MaxI32 {
+  __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; }
+};
+
+// Exclusive prefix sum over the wave (DPP); `total` receives the wave's sum.
+__device__ inline uint32_t wave_excl_sum(uint32_t v, uint32_t& total) {
+  const uint32_t inc = wave_incl_scan(v, SumU32(), 0u);
+  total = read_lane(inc, kWaveSize - 1);
+  return inc - v;
+}
+
+// max(a, b) of non-NaN floats as one v_max3_f32 (no NaN canonicalisation of bit-cast inputs;
+// a NaN row is detected separately and never reaches a decision).
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline float max2(float a, float b) { return max3f(a, b, b); }
+
+// Largest 16-bit value v such that at least r of the block's keys (one per thread) are >= v.
+// Four rounds resolve 4 bits each: 15 ballots per wave, one LDS table, one barrier.
+__device__ inline uint32_t block_rth_largest16(uint32_t key, uint32_t r, FastShared& fs) {
+  const uint32_t lane = lane_id(), wid = wave_id();
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int round = 0; round < 4; ++round) {
+    const int shift = 12 - 4 * round;
+    uint32_t counts = 0;  // lane dv holds the wave's count of keys >= prefix | dv << shift
+#pragma unroll
+    for (int dv = 1; dv < 16; ++dv) {
+      const uint64_t m = __ballot(key >= (prefix | ((uint32_t)dv << shift)));
+      counts = lane == (uint32_t)dv ? (uint32_t)__popcll(m) : counts;
+    }
+    uint32_t(&tab)[kWaves][16] = fs.sel_cnt[round & 1];  // double-buffered across rounds
+    if (lane < 16) tab[wid][lane] = counts;
+    lds_barrier();
+    uint32_t tot = 0;
+    if (lane < 16) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += tab[w][lane];
+    }
+    const uint64_t ok = __ballot(lane >= 1 && lane < 16 && tot >= r);
+    const uint32_t best = ok ? 63u - (uint32_t)__builtin_clzll(ok) : 0u;
+    prefix |= best << shift;
+  }
+  return prefix;
+}
+
+// Race noise g = -ln(-ln u) in float32 with the hardware log2. Measured over all 2^23 uniforms
+// of the race: -ln u has relative error <= 1.7e-7 (also for u next to 1) and g absolute error
+// <= 1.7e-6, so a float32 score (x - m)/T + g is within ~3e-6 of exact for every competitive
+// candidate (|x - m|/T < 20), far inside kRaceMargin.
+__device__ inline float race_noise(float u) {
+  const float e = -__builtin_amdgcn_logf(u) * 0.6931471805599453f;
+  return -__builtin_amdgcn_logf(e) * 0.6931471805599453f;
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Capture slot of row b from the first 1024 opt-in entries (e = optin_rows[tid] or INT32_MIN,
+// loaded before the row): an entry is valid iff in range and above every earlier entry.
+// Marks slot b invalid when it is. Rows with R > 1024 use find_capture_slot instead.
+__device__ inline int64_t slot_from_prefetch(const SampleArgs& a, int64_t b, int32_t e,
+                                             FastShared& fs) {
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+  const int32_t shifted = dpp_mov<0x138>(INT32_MIN, e);  // wave_shr:1, lane 0 gets INT32_MIN
+  const int32_t excl_w = wave_incl_scan(shifted, MaxI32(), INT32_MIN);
+  if (lane == kWaveSize - 1) fs.slot_wmax[wid] = excl_w > e ? excl_w : e;
+  lds_barrier();
+  int32_t before = INT32_MIN;
+  for (uint32_t w = 0; w < wid; ++w) before = before > fs.slot_wmax[w] ? before : fs.slot_wmax[w];
+  const int32_t excl = excl_w > before ? excl_w : before;
+  const bool in = (int64_t)tid < a.R;
+  const bool valid = in && e >= 0 && (int64_t)e < a.B && e > excl;
+  if (in && !valid && (int64_t)tid == b) {
+    a.lengths[b] = 0;
+    a.selected_logprob[b] = __builtin_nanf("");
+  }
+  const int32_t hit = wave_reduce(valid && (int64_t)e == b ? (int32_t)tid : -1, MaxI32());
+  if (lane == 0) fs.slot_hit[wid] = hit;
+  lds_barrier();
+  int32_t slot = -1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) slot = slot > fs.slot_hit[w] ? slot : fs.slot_hit[w];
+  return slot;
+}
+
+// Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
+// go through the general path instead; `slot` is then already set.
+template <bool NEED_P>
+__device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
+                                              float T, int32_t k, float p, float mp,
+                                              unsigned char* lds, FastShared& fs) {
+  using E = Elem<TSC_DTYPE_BF16>;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+  const uint16_t* row = reinterpret_cast<const uint16_t*>(a.logits) + b * a.ld;
+  const uint4* rowv = reinterpret_cast<const uint4*>(row);
+  const int64_t V = a.V;
+  const uint32_t nch = (uint32_t)(V / 8);
+  const uint32_t cw = (nch + kWaves - 1) / kWaves;        // chunks per wave segment
+  const uint32_t seg0 = wid * cw;
+  const uint32_t seg1 = seg0 + cw < nch ? seg0 + cw : nch;
+  const uint32_t id0 = seg0 * 8u;                         // first token id of the segment
+
+  // Rank of theta among the 1024 lane maxima of the first loads: aim for about 2k + 64 tokens
+  // above theta; a maximum of 8 values exceeds the quantile 1 - q with probability 1 - (1-q)^8.
+  uint32_t theta_rank;
+  {
+    const float q = fminf(1.0f, (2.0f * (float)k + 64.0f) / (float)V);
+    const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
+    const float pr = 1.0f - t4 * t4;
+    const int rr = (int)ceilf(pr * (float)kThreads);
+    theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kThreads ? kThreads : rr));
+  }
+
+  // ---- 1. Loads: the opt-in entry first (loads complete in issue order, so waiting for it never
+  // waits for row data), then a shallow pipeline over the wave's segment. A shallow pipeline
+  // loses almost no bandwidth here and lets every wave's first load land within ~2 us.
+  const int32_t opt_e = (a.R <= kThreads && (int64_t)tid < a.R) ? a.optin_rows[tid] : INT32_MIN;
+  // Buffer loads: the wave's segment is one scalar resource descriptor (loads past its end return
+  // zero and are replaced below), one shared VGPR offset, and a scalar offset per load.
+  uint4 r[kFastLoads];
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(rowv + seg0), (short)0, (int)((seg1 - seg0) * 16u), 0x00020000);
+  const int voff = (int)(lane * 16u);
+  auto issue = [&](int j) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, j * kWaveSize * 16, 0);
+    r[j] = make_uint4(v.x, v.y, v.z, v.w);
+  };
+#pragma unroll
+  for (int j = 0; j < kLoadsFirst; ++j) issue(j);
+  // Keep the loads here: nothing orders global loads against the LDS-only barriers that follow,
+  // and the scheduler would otherwise sink them towards their first use.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto valid_load = [&](int j) { return seg0 + (uint32_t)j * kWaveSize + lane < seg1; };
+  auto load_max = [&](const uint4& q) {
+    const float a0 = max3f(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y));
+    const float a1 = max3f(bf16_hi(q.y), bf16_lo(q.z), bf16_hi(q.z));
+    return max3f(a0, a1, max2(bf16_lo(q.w), bf16_hi(q.w)));
+  };
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
+  hcnt[tid] = 0u;  // published by the barriers of the cutoff selection
+
+  // ---- Cutoff from the first loads of every segment, then the capture slot ------------------
+  uint32_t theta_key;
+  {
+    const float lm0 = valid_load(0) ? load_max(r[0]) : -__builtin_inff();
+    // Once the first load has landed, deepen the pipeline so that HBM stays busy during the
+    // block-wide selection (issuing these earlier would delay the first load itself).
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = kLoadsFirst; j < kLoadsAhead; ++j) issue(j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t key0 = key_of<E>(__float_as_uint(lm0) >> 16);
+    theta_key = block_rth_largest16(key0, theta_rank, fs);
+  }
+  const float theta = E::to_float(bits_of_key<E>(theta_key));
+  slot = a.R <= kThreads ? slot_from_prefetch(a, b, opt_e, fs) : find_capture_slot(a, b, fs.red);
+
+  // ---- 2. Stream: max, online mass, stash --------------------------------------------------
+  const float c = 1.4426950408889634f / T;  // log2(e) / T
+  float m_l = -__builtin_inff();  // lane maximum
+  float s_l = 0.0f;               // lane mass relative to max(m_l, -FLT_MAX)
+  uint32_t nan_or = 0;            // NaN detection when the mass (which would carry it) is skipped
+  uint32_t wcnt = 0;              // wave's stashed loads (wave-uniform)
+  uint4* stash = reinterpret_cast<uint4*>(lds + kOffStash) + wid * kStashPerWave;
+  uint32_t* stash_ch = reinterpret_cast<uint32_t*>(lds + kOffStashCh) + wid * kStashPerWave;
+#pragma unroll
+  for (int j = 0; j < kFastLoads; ++j) {
+    if (j + kLoadsAhead < kFastLoads) issue(j + kLoadsAhead);
+    uint4 q = r[j];
+    if (!valid_load(j)) q = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    const float lm = load_max(q);
+    if constexpr (NEED_P) {
+      const float m_new = max2(m_l, lm);
+      const float ref_old = max2(m_l, -3.4028234663852886e38f);
+      const float ref = max2(m_new, -3.4028234663852886e38f);
+      float acc = s_l * __builtin_amdgcn_exp2f((ref_old - ref) * c);
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += __builtin_amdgcn_exp2f((bf16_lo(w4[e]) - ref) * c);
+        acc += __builtin_amdgcn_exp2f((bf16_hi(w4[e]) - ref) * c);
+      }
+      s_l = acc;
+      m_l = m_new;
+    } else {
+      m_l = max2(m_l, lm);
+      // NaN has all exponent bits set and a nonzero mantissa: |bits| > 0x7F80 in either half.
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nan_or |= ((w4[e] & 0x7FFFu) > 0x7F80u) | (((w4[e] >> 16) & 0x7FFFu) > 0x7F80u);
+      }
+    }
+    // Keep each load's work at its own step: without this the compiler may sink the whole exp
+    // chain (which only feeds the final sum) past the loop and keep every load's data alive.
+    asm volatile("" : "+v"(s_l), "+v"(m_l), "+v"(nan_or));
+    const bool flag = lm >= theta;
+    const uint64_t mask = __ballot(flag);
+    if (mask) {
+      if (flag) {
+        const uint32_t at = wcnt + mbcnt(mask);
+        if (at < (uint32_t)kStashPerWave) {
+          stash[at] = q;
+          stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
+        }
+      }
+      wcnt += (uint32_t)__popcll(mask);
+    }
+  }
+
+  // ---- 3. Row maximum, mass, status: per-wave partials, one exchange ------------------------
+  {
+    const float wm = wave_reduce(m_l, [](float x, float y) { return x > y ? x : y; });
+    double wz = 0.0;
+    if constexpr (NEED_P) {
+      const float ref_l = max2(m_l, -3.4028234663852886e38f);
+      const float ref_w = max2(wm, -3.4028234663852886e38f);
+      wz = wave_reduce((double)(s_l * __builtin_amdgcn_exp2f((ref_l - ref_w) * c)),
+                       [](double x, double y) { return x + y; });
+    }
+    const uint32_t wn = wave_reduce(nan_or, [](uint32_t x, uint32_t y) { return x | y; });
+    if (lane == 0) {
+      fs.wave_m[wid] = wm;
+      fs.wave_z[wid] = wz;
+      fs.wave_nan[wid] = wn;
+      fs.wave_stash[wid] = wcnt;
+    }
+  }
+  lds_barrier();
+  float m = -__builtin_inff();
+  uint32_t nan_any = 0, over = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
+    nan_any |= fs.wave_nan[w];
+    over |= fs.wave_stash[w] > (uint32_t)kStashPerWave;
+  }
+  double Z = 0.0;
+  if constexpr (NEED_P) {
+    const float ref = max2(m, -3.4028234663852886e38f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float ref_w = max2(fs.wave_m[w], -3.4028234663852886e38f);
+      Z += fs.wave_z[w] * (double)__builtin_amdgcn_exp2f((ref_w - ref) * c);
+    }
+    nan_any |= !(Z == Z);
+  }
+  if (nan_any || m == __builtin_inff()) {
+    finish_empty_row(a, b, slot, TSC_ROW_NONFINITE);
+    return true;
+  }
+  if (m == -__builtin_inff()) {
+    finish_empty_row(a, b, slot, TSC_ROW_NO_SUPPORT);
+    return true;
+  }
+  // Capacities: every wave's stash, and the key span the histogram covers. Keys of candidates
+  // run from theta_key to kmax; d = kmax - key is the distance from the maximum.
+  const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
+  const uint32_t dspan = kmax - theta_key;
+  if (over || dspan >= (uint32_t)kDBins) return false;
+
+  // ---- 3b. Expand the stash into id-ordered candidate words and histogram them --------------
+  // Word: bf16 bits << 16 | offset of the token in the segment (< 2^14). Histogram bin: d.
+  uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
+  uint32_t ncand = 0;  // wave-uniform
+  for (uint32_t base = 0; base < wcnt; base += kWaveSize) {
+    const uint32_t i = base + lane;
+    const bool ok = i < wcnt;
+    const uint4 q = ok ? stash[i] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    const uint32_t off = ok ? stash_ch[i] * 8u : 0u;
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+    uint32_t words[8];
+    uint32_t is = 0, n = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+      const float x = __uint_as_float(hi);
+      const bool c_e = x >= theta && x > -__builtin_inff();  // -0 ties +0; -inf and NaN fail
+      words[e] = hi | (off + e);
+      is |= (uint32_t)c_e << e;
+      n += c_e;
+    }
+    uint32_t total;
+    uint32_t at = ncand + wave_excl_sum(n, total);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((is >> e) & 1u) {
+        if (at < (uint32_t)kCandPerWave) cand[at] = words[e];
+        ++at;
+      }
+    }
+    ncand += total;
+  }
+  const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
+  auto d_of = [&](uint32_t word) { return kmax - key_of<E>(word >> 16); };
+  for (uint32_t i = lane; i < nc_here; i += kWaveSize) atomicAdd(&hcnt[d_of(cand[i])], 1u);
+  if (lane == 0) fs.wave_cand[wid] = ncand;
+  lds_barrier();
+  uint32_t ntot = 0;
+  over = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    ntot += fs.wave_cand[w];
+    over |= fs.wave_cand[w] > (uint32_t)kCandPerWave;
+  }
+  // theta is a lower bound of the k-th largest value iff at least k candidates exist.
+  if (over || ntot < (uint32_t)k) return false;
+
+  // ---- 4. Joint threshold over the bins d = 0..dspan (thread d owns bin d) ------------------
+  // Every member of a bin has the same weight, so a bin's mass is its count times that weight;
+  // min-p drops whole bins (it is a per-value predicate, monotone in d).
+  const bool need_m = mp > 0.0f;
+  const double tln_mp = need_m ? (double)T * log((double)mp) : 0.0;
+  auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
+  uint32_t bc = 0;
+  uint64_t bm = 0;
+  if (tid <= dspan) {
+    const float x = value_of_d(tid);
+    // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
+    if (!need_m || ((double)x - (double)m) >= tln_mp) {
+      bc = hcnt[tid];
+      const float w = __builtin_amdgcn_exp2f((x - m) * c);
+      bm = (uint64_t)bc * (uint64_t)((double)w * 0x1p48);
+    }
+  }
+  uint32_t ex_c, ex_g;
+  uint64_t ex_m;
+  {
+    const uint32_t ic = wave_incl_scan(bc, SumU32(), 0u);
+    const uint32_t ig = wave_incl_scan((uint32_t)(bc > 0u), SumU32(), 0u);
+    const uint64_t im = wave_incl_scan(bm, SumU64(), (uint64_t)0);
+    if (lane == kWaveSize - 1) {
+      fs.scan_c[wid] = ic;
+      fs.scan_g[wid] = ig;
+      fs.scan_m[wid] = im;
+    }
+    lds_barrier();
+    uint32_t pc = 0, pg = 0;
+    uint64_t pm = 0;
+    for (uint32_t w = 0; w < wid; ++w) {
+      pc += fs.scan_c[w];
+      pg += fs.scan_g[w];
+      pm += fs.scan_m[w];
+    }
+    ex_c = pc + ic - bc;
+    ex_g = pg + ig - (bc > 0u);
+    ex_m = pm + im - bm;
+  }
+  uint32_t* excl_cnt = reinterpret_cast<uint32_t*>(lds + kOffExclCnt);
+  uint16_t* group = reinterpret_cast<uint16_t*>(lds + kOffGroup);
+  excl_cnt[tid] = ex_c;
+  group[tid] = (uint16_t)ex_g;
+  // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
+  // strictly above <= top_p * Z.
+  const bool qual = bc > 0u && ex_c < (uint32_t)k && (!NEED_P || (double)ex_m * 0x1p-48 <= (double)p * Z);
+  {
+    // Each wave's largest qualifying bin publishes its prefix results; one exchange.
+    const int32_t wd = wave_reduce(qual ? (int32_t)tid : -1, MaxI32());
+    if (lane == 0) fs.dstar_w[wid] = wd;
+    if (qual && (int32_t)tid == wd) {
+      fs.L_w[wid] = ex_c + bc;
+      fs.G_w[wid] = ex_g + 1u;
+      fs.zs_w[wid] = ex_m + bm;
+    }
+  }
+  lds_barrier();
+  int32_t dstar = -1;
+  uint32_t dwave = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (fs.dstar_w[w] > dstar) {
+      dstar = fs.dstar_w[w];
+      dwave = w;
+    }
+  }
+  const bool capture = slot >= 0;
+  const bool in_support = (int32_t)tid <= dstar && bc > 0u;  // this thread's bin is a support group
+  const uint32_t L = fs.L_w[dwave], G = fs.G_w[dwave];
+  const double lnzs = log((double)fs.zs_w[dwave]) - kFixShift * 0.6931471805599453;
+  if (capture && G > (uint32_t)kMaxGroups) return false;  // capture too spread for the tables
+  // Group tables for the capture: base position and logprob of every support group.
+  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
+  float* lp_tab = reinterpret_cast<float*>(lds + kOffLpTab);
+  if (capture && in_support) {
+    grp_base[ex_g] = ex_c;
+    lp_tab[ex_g] = logprob_of(value_of_d(tid), m, T, lnzs);
+  }
+
+  // ---- 5a. Race over the survivors (and per-wave group member counts) ------------------------
+  // A candidate survives iff d <= d* (bins failing min-p lie beyond d*).
+  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
+  uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(lds + kOffGrpCnt) + wid * kMaxGroups;
+  if (capture) {
+    for (uint32_t g = lane; g < (uint32_t)kMaxGroups; g += kWaveSize) grp_cnt[g] = 0u;
+  }
+  const uint64_t seed = a.seeds[b], pos = a.positions[b];
+  const float invT = 1.0f / T;
+  float b1 = -__builtin_inff(), b2 = -__builtin_inff();  // lane's best two float32 scores
+  int32_t b1_id = 0x7FFFFFFF;
+  uint32_t b1_d = 0;
+  for (uint32_t i = lane; i < ncand; i += kWaveSize) {
+    const uint32_t wd = cand[i];
+    const uint32_t d = d_of(wd);
+    if ((int32_t)d <= dstar) {
+      const uint32_t id = id0 + (wd & 0x3FFFu);
+      const float u = (float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f;
+      const float gn = race_noise(u);
+      noise[i] = gn;
+      const float sc = (value_of_d(d) - m) * invT + gn;
+      if (sc > b1) {
+        b2 = b1;
+        b1 = sc;
+        b1_id = (int32_t)id;
+        b1_d = d;
+      } else if (sc > b2) {
+        b2 = sc;
+      }
+      if (capture) atomicAdd(&grp_cnt[group[d]], 1u);
+    } else {
+      noise[i] = -__builtin_inff();
+    }
+  }
+  {
+    const float wb1 = wave_reduce(b1, [](float x, float y) { return x > y ? x : y; });
+    const uint64_t at_max = __ballot(b1 == wb1);
+    const uint32_t src = (uint32_t)__builtin_ctzll(at_max);
+    const float l2 = lane == src ? b2 : b1;  // the best lane's second, or other lanes' best
+    const float wb2 = wave_reduce(l2, [](float x, float y) { return x > y ? x : y; });
+    if (lane == src) {
+      fs.race_b1[wid] = wb1;
+      fs.race_b2[wid] = wb2;
+      fs.race_id[wid] = b1_id;
+      fs.race_d[wid] = b1_d;
+    }
+  }
+  lds_barrier();
+  float t1 = -__builtin_inff(), t2 = -__builtin_inff();
+  int32_t token = 0x7FFFFFFF;
+  uint32_t token_d = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float x1 = fs.race_b1[w], x2 = fs.race_b2[w];
+    if (x1 > t1) {
+      t2 = t1 > x2 ? t1 : x2;
+      t1 = x1;
+      token = fs.race_id[w];
+      token_d = fs.race_d[w];
+    } else {
+      t2 = t2 > x1 ? t2 : x1;
+    }
+  }
+  if (!(t1 - t2 > kRaceMargin)) {
+    // Near tie in float32: rescore every candidate within the margin in float64, ties -> lowest id.
+    double bs = -__builtin_inf();
+    int32_t bid = 0x7FFFFFFF;
+    uint32_t bd = 0;
+    for (uint32_t i = lane; i < ncand; i += kWaveSize) {
+      if (noise[i] == -__builtin_inff()) continue;
+      const uint32_t wd = cand[i];
+      const uint32_t d = d_of(wd);
+      if ((value_of_d(d) - m) * invT + noise[i] < t1 - kRaceMargin) continue;
+      const int32_t id = (int32_t)(id0 + (wd & 0x3FFFu));
+      const double sv = ((double)value_of_d(d) - (double)m) / (double)T;
+      const double sc = sv - log(-log(race_uniform((uint32_t)id, seed, pos)));
+      if (sc > bs || (sc == bs && id < bid)) {
+        bs = sc;
+        bid = id;
+        bd = d;
+      }
+    }
+    const double wt = wave_reduce(bs, [](double x, double y) { return x > y ? x : y; });
+    const int32_t wi = wave_reduce(bs == wt ? bid : 0x7FFFFFFF,
+                                   [](int32_t x, int32_t y) { return x < y ? x : y; });
+    if (bs == wt && bid == wi) {  // one lane, or every lane when the wave has no candidate
+      fs.ref_top[wid] = wt;
+      fs.ref_id[wid] = wi;
+      fs.ref_d[wid] = bd;
+    }
+    lds_barrier();
+    double top = -__builtin_inf();
+    token = 0x7FFFFFFF;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const double t = fs.ref_top[w];
+      const int32_t i = fs.ref_id[w];
+      if (t > top || (t == top && i < token)) {
+        top = t;
+        token = i;
+        token_d = fs.ref_d[w];
+      }
+    }
+  }
+  if (tid == 0) {
+    a.tokens[b] = token;
+    a.row_status[b] = (capture && L > (uint32_t)a.W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
+  }
+  if (!capture) return true;
+
+  // ---- 5b. Ordered capture -----------------------------------------------------------------
+  // Wave w's cursor in group g: the group's base (members with larger keys) plus the group's
+  // members in earlier segments (smaller ids). Each wave builds its own row of cursors.
+  uint32_t* cursor = reinterpret_cast<uint32_t*>(lds + kOffCursor) + wid * kMaxGroups;
+  const uint32_t* all_cnt = reinterpret_cast<const uint32_t*>(lds + kOffGrpCnt);
+  for (uint32_t g = lane; g < G; g += kWaveSize) {
+    uint32_t acc = grp_base[g];
+    for (uint32_t w = 0; w < wid; ++w) acc += all_cnt[w * kMaxGroups + g];
+    cursor[g] = acc;
+  }
+  const uint32_t W = (uint32_t)a.W;
+  int32_t* out_ids = a.packed_ids + slot * a.W;
+  float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+  for (uint32_t base = 0; base < ncand; base += kWaveSize) {
+    const uint32_t i = base + lane;
+    uint32_t wd = 0, g = 0;
+    bool live = false;
+    if (i < ncand) {
+      wd = cand[i];
+      live = noise[i] != -__builtin_inff();
+      if (live) g = group[d_of(wd)];
+    }
+    // Members of my group among the lanes of this chunk: intersect, over the 8 bits of g, the
+    // ballot of lanes whose bit matches mine.
+    uint64_t same = __ballot(live);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot(live && ((g >> bit) & 1u));
+      same &= ((g >> bit) & 1u) ? ones : ~ones;
+    }
+    if (live) {
+      const uint32_t rank = mbcnt(same);
+      const uint32_t at = cursor[g] + rank;
+      if (at < W) {
+        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
+        if (out_lp) out_lp[at] = lp_tab[g];
+      }
+      if (rank == 0) cursor[g] += (uint32_t)__popcll(same);  // the group's first lane advances it
+    }
+  }
+  if (tid == 0) {
+    a.lengths[slot] = (int32_t)(L < W ? L : W);
+    a.selected_logprob[slot] = lp_tab[group[token_d]];
+  }
+  return true;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
+  extern __shared__ uint64_t dyn[];
+  __shared__ FastShared fs;
+  unsigned char* lds = reinterpret_cast<unsigned char*>(dyn);
+  const int64_t b = blockIdx.x;
+  int64_t slot = -2;  // looked up inside the fast path, after its loads are issued
+  if constexpr (DT == TSC_DTYPE_BF16) {
+    const float T = a.temperature[b];
+    const int32_t k = a.top_k[b];
+    const float p = a.top_p[b];
+    const float mp = a.min_p[b];
+    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f && k >= 1 && k <= kFastMaxK &&
+                          a.V >= kFastMinV && a.V <= kFastMaxV && (a.V & 7) == 0 &&
+                          (a.ld & 7) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
+    if (eligible) {
+      const bool done = p < 1.0f ? fast_row_bf16<true>(a, b, slot, T, k, p, mp, lds, fs)
+                                 : fast_row_bf16<false>(a, b, slot, T, k, p, mp, lds, fs);
+      if (done) return;
+      __syncthreads();  // the general path reuses the LDS
+    }
+  }
+  if (slot == -2) slot = find_capture_slot(a, b, fs.red);
+  GeneralShared* sh = reinterpret_cast<GeneralShared*>(lds + kGeneralDynLds);
+  general_row<DT>(a, b, slot, dyn, *sh);
+}
+
+}  // namespace tsc

@@ -88,7 +88,7 @@ struct GeneralShared {
 // finds the smallest present value v with #(values > v) < kk and, when use_mass, mass(> v) <= pz,
 // where mass sums wfix(bits). Requires at least one element and kk >= 1, pz >= 0.
 template <class E, int NBITS, class Pred, class Val, class Mass>
-__device__ DescentState radix_descent(const typename E::Bits* row, int64_t V, Pred pred, Val val,
+__device__ __forceinline__ DescentState radix_descent(const typename E::Bits* row, int64_t V, Pred pred, Val val,
                                       uint32_t kk, bool use_mass, double pz, Mass wfix,
                                       GeneralShared& sh) {
   DescentState st{0u, 0u, 0ull};
@@ -173,81 +173,88 @@ __device__ inline float logprob_of(float x, float m, float T, double lnzs) {
   return (float)(s - lnzs);
 }
 
-template <int DT>
-__global__ void __launch_bounds__(kThreads) sample_general_kernel(SampleArgs a) {
-  using E = Elem<DT>;
-  extern __shared__ uint64_t sortbuf[];
-  __shared__ GeneralShared sh;
+// Capture slot of row b (-1 if it has none) under the slot-validity rule: slot j is valid iff
+// 0 <= optin_rows[j] < B and it exceeds every earlier entry. The workgroup of row b also owns slot
+// b's validity and marks it (length 0, NaN selected logprob) when it is invalid.
+__device__ inline int64_t find_capture_slot(const SampleArgs& a, int64_t b, uint64_t* red) {
+  const int tid = threadIdx.x;
+  int32_t my_slot = -1;
+  bool slot_b_invalid = false;
+  int32_t carry = INT32_MIN;
+  for (int64_t base = 0; base < a.R; base += kThreads) {
+    const int64_t j = base + tid;
+    const int32_t e = j < a.R ? a.optin_rows[j] : INT32_MIN;
+    // Inclusive max-scan over the chunk: wave scan, then wave totals.
+    int32_t inc = e;
+    const int lane = tid & (kWaveSize - 1);
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+      const int32_t t = __shfl_up(inc, o, kWaveSize);
+      if (lane >= o) inc = inc > t ? inc : t;
+    }
+    int32_t* wt = reinterpret_cast<int32_t*>(red);
+    lds_barrier();
+    if (lane == kWaveSize - 1) wt[tid / kWaveSize] = inc;
+    lds_barrier();
+    int32_t before = carry;
+    for (int w = 0; w < tid / kWaveSize; ++w) before = before > wt[w] ? before : wt[w];
+    int32_t excl = __shfl_up(inc, 1, kWaveSize);
+    if (lane == 0) excl = INT32_MIN;
+    excl = excl > before ? excl : before;
+    int32_t chunk_max = carry;
+    for (int w = 0; w < kWaves; ++w) chunk_max = chunk_max > wt[w] ? chunk_max : wt[w];
+    if (j < a.R) {
+      const bool valid = e >= 0 && (int64_t)e < a.B && e > excl;
+      if (valid && (int64_t)e == b) my_slot = (int32_t)j;
+      if (!valid && j == b) slot_b_invalid = true;
+    }
+    carry = chunk_max;
+  }
+  my_slot = block_reduce(my_slot, MaxOp(), red);
+  if (slot_b_invalid) {
+    a.lengths[b] = 0;
+    a.selected_logprob[b] = __builtin_nanf("");
+  }
+  return my_slot;
+}
 
-  const int64_t b = blockIdx.x;
+// Writes the outputs of a row that has no support (status >= 2): token -1, empty capture.
+__device__ inline void finish_empty_row(const SampleArgs& a, int64_t b, int64_t slot, int8_t status) {
+  if (threadIdx.x == 0) {
+    a.tokens[b] = -1;
+    a.row_status[b] = status;
+    if (slot >= 0) {
+      a.lengths[slot] = 0;
+      a.selected_logprob[slot] = __builtin_nanf("");
+    }
+  }
+}
+
+// Temperature 0 or a normal positive finite float; top_p and min_p in [0, 1] (false for NaN).
+__device__ inline bool row_params_valid(float T, float p, float mp) {
+  const bool t_ok = __builtin_isfinite(T) && T >= 0.0f && (T == 0.0f || T >= 1.1754943508222875e-38f);
+  return t_ok && p >= 0.0f && p <= 1.0f && mp >= 0.0f && mp <= 1.0f;
+}
+
+// The whole sampling of row b by the general multi-pass algorithm. `sortbuf` holds kSortCap
+// u64 entries of LDS. Every thread of the workgroup calls it; it returns with the row done.
+template <int DT>
+__device__ __forceinline__ void general_row(const SampleArgs& a, int64_t b, int64_t slot, uint64_t* sortbuf,
+                            GeneralShared& sh) {
+  using E = Elem<DT>;
   const int tid = threadIdx.x;
   const auto* row = reinterpret_cast<const typename E::Bits*>(a.logits) + b * a.ld;
   const int64_t V = a.V;
-
-  // ---- Capture slot of this row, and validity of slot b (owned by this workgroup) ----------
-  int32_t my_slot = -1;
-  bool slot_b_invalid = false;
-  {
-    int32_t carry = INT32_MIN;
-    for (int64_t base = 0; base < a.R; base += kThreads) {
-      const int64_t j = base + tid;
-      const int32_t e = j < a.R ? a.optin_rows[j] : INT32_MIN;
-      // Inclusive max-scan over the chunk: wave scan, then wave totals.
-      int32_t inc = e;
-      const int lane = tid & (kWaveSize - 1);
-#pragma unroll
-      for (int o = 1; o < kWaveSize; o <<= 1) {
-        const int32_t t = __shfl_up(inc, o, kWaveSize);
-        if (lane >= o) inc = inc > t ? inc : t;
-      }
-      int32_t* wt = reinterpret_cast<int32_t*>(sh.red);
-      __syncthreads();
-      if (lane == kWaveSize - 1) wt[tid / kWaveSize] = inc;
-      __syncthreads();
-      int32_t before = carry;
-      for (int w = 0; w < tid / kWaveSize; ++w) before = before > wt[w] ? before : wt[w];
-      int32_t excl = __shfl_up(inc, 1, kWaveSize);
-      if (lane == 0) excl = INT32_MIN;
-      excl = excl > before ? excl : before;
-      int32_t chunk_max = carry;
-      for (int w = 0; w < kWaves; ++w) chunk_max = chunk_max > wt[w] ? chunk_max : wt[w];
-      if (j < a.R) {
-        const bool valid = e >= 0 && (int64_t)e < a.B && e > excl;
-        if (valid && (int64_t)e == b) my_slot = (int32_t)j;
-        if (!valid && j == b) slot_b_invalid = true;
-      }
-      carry = chunk_max;
-    }
-    my_slot = block_reduce(my_slot, MaxOp(), sh.red);
-    if (slot_b_invalid) {
-      a.lengths[b] = 0;
-      a.selected_logprob[b] = __builtin_nanf("");
-    }
-  }
-  const int64_t slot = my_slot;
-
-  auto finish_empty = [&](int8_t status) {
-    if (tid == 0) {
-      a.tokens[b] = -1;
-      a.row_status[b] = status;
-      if (slot >= 0) {
-        a.lengths[slot] = 0;
-        a.selected_logprob[slot] = __builtin_nanf("");
-      }
-    }
-  };
 
   // ---- Parameters ---------------------------------------------------------------------------
   const float T = a.temperature[b];
   const int32_t k = a.top_k[b];
   const float p = a.top_p[b];
   const float mp = a.min_p[b];
-  const bool t_ok = __builtin_isfinite(T) && T >= 0.0f && (T == 0.0f || T >= 1.1754943508222875e-38f);
-  if (!t_ok || !(p >= 0.0f && p <= 1.0f) || !(mp >= 0.0f && mp <= 1.0f)) {
-    finish_empty(TSC_ROW_INVALID_PARAM);
+  if (!row_params_valid(T, p, mp)) {
+    finish_empty_row(a, b, slot, TSC_ROW_INVALID_PARAM);
     return;
   }
-
   // ---- 1. Stats pass ------------------------------------------------------------------------
   uint64_t best_packed = 0;  // (key << 32) | (0x7FFFFFFF - id): max = largest key, first id
   uint32_t nfin = 0, bad = 0, kmin = 0xFFFFFFFFu;
@@ -267,11 +274,11 @@ __global__ void __launch_bounds__(kThreads) sample_general_kernel(SampleArgs a) 
   bad = block_reduce(bad, MaxOp(), sh.red);
   kmin = block_reduce(kmin, MinOp(), sh.red);
   if (bad) {
-    finish_empty(TSC_ROW_NONFINITE);
+    finish_empty_row(a, b, slot, TSC_ROW_NONFINITE);
     return;
   }
   if (nfin == 0) {
-    finish_empty(TSC_ROW_NO_SUPPORT);
+    finish_empty_row(a, b, slot, TSC_ROW_NO_SUPPORT);
     return;
   }
   const uint32_t kmax = (uint32_t)(best_packed >> 32);
@@ -436,6 +443,15 @@ __global__ void __launch_bounds__(kThreads) sample_general_kernel(SampleArgs a) 
     a.lengths[slot] = (int32_t)len;
     a.selected_logprob[slot] = logprob_of(E::to_float((uint32_t)row[token]), m, T, lnzs);
   }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) sample_general_kernel(SampleArgs a) {
+  extern __shared__ uint64_t sortbuf[];
+  __shared__ GeneralShared sh;
+  const int64_t b = blockIdx.x;
+  const int64_t slot = find_capture_slot(a, b, sh.red);
+  general_row<DT>(a, b, slot, sortbuf, sh);
 }
 
 }  // namespace tsc
