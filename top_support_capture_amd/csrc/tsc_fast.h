@@ -4,9 +4,10 @@
 // once, and all per-element work happens while the loads land. Wave w owns a contiguous segment
 // of the row (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
 //
-//   1. Issue all loads. When the first one lands, a block-wide radix select over the lane maxima
-//      picks a cutoff theta that about twice top_k tokens of the row should exceed (the first
-//      loads of the 16 segments are a sample spread over the whole row).
+//   1. Stream the loads through a shallow pipeline. The lane maxima of the first load of every
+//      segment (a sample spread over the whole row) pick a cutoff theta that about twice top_k
+//      tokens of the row should exceed: an LDS histogram of their key distances to the sample's
+//      maximum, built over the first stream steps so that the loads keep flowing.
 //   2. As each load lands: running maximum and (top_p < 1) an online sum of exp((x - max) / T)
 //      per lane; a ballot over "this load's maximum >= theta" stashes the whole 16-byte load in
 //      the wave's LDS stash, in id order.
@@ -45,10 +46,10 @@ constexpr int kOffStash = 0;                                          // uint4 [
 constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16][256]
 constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
 constexpr int kOffCnt = kOffCand + kWaves * kCandPerWave * 4;         // u32 [1024]
-constexpr int kFastLdsEnd = kOffCnt + kDBins * 4;
+constexpr int kOffNoise = kOffCnt + kDBins * 4;                       // f32 [16][512] race noise
+constexpr int kFastLdsEnd = kOffNoise + kWaves * kCandPerWave * 4;
 // Overlays of the stash region once it has been expanded:
-constexpr int kOffNoise = 0;                                      // f32 [16][512] race noise
-constexpr int kOffExclCnt = kOffNoise + kWaves * kCandPerWave * 4;    // u32 [1024] by d
+constexpr int kOffExclCnt = 0;                                    // u32 [1024] by d
 constexpr int kOffGroup = kOffExclCnt + kDBins * 4;               // u16 [1024] by d
 constexpr int kOffGrpCnt = kOffGroup + kDBins * 2;                // u32 [16][256] members per wave
 constexpr int kOffCursor = kOffGrpCnt + kWaves * kMaxGroups * 4;  // u32 [16][256] write cursors
@@ -63,9 +64,13 @@ constexpr size_t kFastDynLds =
         : (size_t)kFastLdsEnd;
 
 // Per-wave partial results exchanged through LDS (one barrier per exchange).
+constexpr int kThetaBins = 256;       // key distances from the block's first-load maximum
+
 struct FastShared {
   uint64_t red[kWaves];
-  uint32_t sel_cnt[2][kWaves][16];
+  uint32_t theta_hist[kThetaBins];
+  uint32_t kmax0_w[kWaves];
+  uint32_t theta_key;
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
   float wave_m[kWaves];
@@ -125,35 +130,6 @@ __device__ inline float max3f(float a, float b, float c) {
 }
 __device__ inline float max2(float a, float b) { return max3f(a, b, b); }
 
-// Largest 16-bit value v such that at least r of the block's keys (one per thread) are >= v.
-// Four rounds resolve 4 bits each: 15 ballots per wave, one LDS table, one barrier.
-__device__ inline uint32_t block_rth_largest16(uint32_t key, uint32_t r, FastShared& fs) {
-  const uint32_t lane = lane_id(), wid = wave_id();
-  uint32_t prefix = 0;
-#pragma unroll
-  for (int round = 0; round < 4; ++round) {
-    const int shift = 12 - 4 * round;
-    uint32_t counts = 0;  // lane dv holds the wave's count of keys >= prefix | dv << shift
-#pragma unroll
-    for (int dv = 1; dv < 16; ++dv) {
-      const uint64_t m = __ballot(key >= (prefix | ((uint32_t)dv << shift)));
-      counts = lane == (uint32_t)dv ? (uint32_t)__popcll(m) : counts;
-    }
-    uint32_t(&tab)[kWaves][16] = fs.sel_cnt[round & 1];  // double-buffered across rounds
-    if (lane < 16) tab[wid][lane] = counts;
-    lds_barrier();
-    uint32_t tot = 0;
-    if (lane < 16) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) tot += tab[w][lane];
-    }
-    const uint64_t ok = __ballot(lane >= 1 && lane < 16 && tot >= r);
-    const uint32_t best = ok ? 63u - (uint32_t)__builtin_clzll(ok) : 0u;
-    prefix |= best << shift;
-  }
-  return prefix;
-}
-
 // Race noise g = -ln(-ln u) in float32 with the hardware log2. Measured over all 2^23 uniforms
 // of the race: -ln u has relative error <= 1.7e-7 (also for u next to 1) and g absolute error
 // <= 1.7e-6, so a float32 score (x - m)/T + g is within ~3e-6 of exact for every competitive
@@ -167,27 +143,36 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Capture slot of row b from the first 1024 opt-in entries (e = optin_rows[tid] or INT32_MIN,
-// loaded before the row): an entry is valid iff in range and above every earlier entry.
-// Marks slot b invalid when it is. Rows with R > 1024 use find_capture_slot instead.
-__device__ inline int64_t slot_from_prefetch(const SampleArgs& a, int64_t b, int32_t e,
-                                             FastShared& fs) {
-  const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+// loaded before the row): an entry is valid iff in range and above every earlier entry. Done in
+// two steps that share the barriers of the cutoff selection. Marks slot b invalid when it is.
+struct SlotScan {
+  int32_t e, excl_w;
+};
+__device__ inline SlotScan slot_step1(int32_t e, FastShared& fs) {
+  const uint32_t lane = lane_id(), wid = wave_id();
   const int32_t shifted = dpp_mov<0x138>(INT32_MIN, e);  // wave_shr:1, lane 0 gets INT32_MIN
   const int32_t excl_w = wave_incl_scan(shifted, MaxI32(), INT32_MIN);
   if (lane == kWaveSize - 1) fs.slot_wmax[wid] = excl_w > e ? excl_w : e;
-  lds_barrier();
+  return {e, excl_w};
+}
+// After a barrier that follows slot_step1.
+__device__ inline void slot_step2(const SampleArgs& a, int64_t b, const SlotScan& sc,
+                                  FastShared& fs) {
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
   int32_t before = INT32_MIN;
   for (uint32_t w = 0; w < wid; ++w) before = before > fs.slot_wmax[w] ? before : fs.slot_wmax[w];
-  const int32_t excl = excl_w > before ? excl_w : before;
+  const int32_t excl = sc.excl_w > before ? sc.excl_w : before;
   const bool in = (int64_t)tid < a.R;
-  const bool valid = in && e >= 0 && (int64_t)e < a.B && e > excl;
+  const bool valid = in && sc.e >= 0 && (int64_t)sc.e < a.B && sc.e > excl;
   if (in && !valid && (int64_t)tid == b) {
     a.lengths[b] = 0;
     a.selected_logprob[b] = __builtin_nanf("");
   }
-  const int32_t hit = wave_reduce(valid && (int64_t)e == b ? (int32_t)tid : -1, MaxI32());
+  const int32_t hit = wave_reduce(valid && (int64_t)sc.e == b ? (int32_t)tid : -1, MaxI32());
   if (lane == 0) fs.slot_hit[wid] = hit;
-  lds_barrier();
+}
+// After a barrier that follows slot_step2.
+__device__ inline int64_t slot_step3(const FastShared& fs) {
   int32_t slot = -1;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) slot = slot > fs.slot_hit[w] ? slot : fs.slot_hit[w];
@@ -223,8 +208,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
 
   // ---- 1. Loads: the opt-in entry first (loads complete in issue order, so waiting for it never
-  // waits for row data), then a shallow pipeline over the wave's segment. A shallow pipeline
-  // loses almost no bandwidth here and lets every wave's first load land within ~2 us.
+  // waits for row data), then a shallow pipeline over the wave's segment: two loads at first, so
+  // that every wave's first load lands within ~2 us, then kLoadsAhead.
   const int32_t opt_e = (a.R <= kThreads && (int64_t)tid < a.R) ? a.optin_rows[tid] : INT32_MIN;
   // Buffer loads: the wave's segment is one scalar resource descriptor (loads past its end return
   // zero and are replaced below), one shared VGPR offset, and a scalar offset per load.
@@ -250,27 +235,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     return max3f(a0, a1, max2(bf16_lo(q.w), bf16_hi(q.w)));
   };
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
-  hcnt[tid] = 0u;  // published by the barriers of the cutoff selection
+  hcnt[tid] = 0u;  // published by the first exchange below
+  if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
 
-  // ---- Cutoff from the first loads of every segment, then the capture slot ------------------
-  uint32_t theta_key;
-  {
-    const float lm0 = valid_load(0) ? load_max(r[0]) : -__builtin_inff();
-    // Once the first load has landed, deepen the pipeline so that HBM stays busy during the
-    // block-wide selection (issuing these earlier would delay the first load itself).
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = kLoadsFirst; j < kLoadsAhead; ++j) issue(j);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t key0 = key_of<E>(__float_as_uint(lm0) >> 16);
-    theta_key = block_rth_largest16(key0, theta_rank, fs);
-  }
-  const float theta = E::to_float(bits_of_key<E>(theta_key));
-  slot = a.R <= kThreads ? slot_from_prefetch(a, b, opt_e, fs) : find_capture_slot(a, b, fs.red);
-
-  // ---- 2. Stream: max, online mass, stash --------------------------------------------------
+  // ---- 2. Stream: max, online mass, cutoff, stash --------------------------------------------
+  // The cutoff theta comes from the lane maxima of the first load of every segment: the
+  // theta_rank-th largest of them (their distances to the block's maximum are histogrammed in
+  // LDS; wave 0 scans the histogram). Its three exchanges ride on the first stream steps, so the
+  // loads keep flowing; the first loads wait in registers until theta is known. The capture slot
+  // lookup shares the same exchanges.
   const float c = 1.4426950408889634f / T;  // log2(e) / T
   float m_l = -__builtin_inff();  // lane maximum
   float s_l = 0.0f;               // lane mass relative to max(m_l, -FLT_MAX)
@@ -278,12 +251,37 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   uint32_t wcnt = 0;              // wave's stashed loads (wave-uniform)
   uint4* stash = reinterpret_cast<uint4*>(lds + kOffStash) + wid * kStashPerWave;
   uint32_t* stash_ch = reinterpret_cast<uint32_t*>(lds + kOffStashCh) + wid * kStashPerWave;
-#pragma unroll
-  for (int j = 0; j < kFastLoads; ++j) {
-    if (j + kLoadsAhead < kFastLoads) issue(j + kLoadsAhead);
-    uint4 q = r[j];
-    if (!valid_load(j)) q = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  float theta = __builtin_inff();
+  auto stash_load = [&](int j, const uint4& q, float lm) {
+    const bool flag = lm >= theta;
+    const uint64_t mask = __ballot(flag);
+    if (mask) {
+      if (flag) {
+        const uint32_t at = wcnt + mbcnt(mask);
+        if (at < (uint32_t)kStashPerWave) {
+          stash[at] = q;
+          stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
+        }
+      }
+      wcnt += (uint32_t)__popcll(mask);
+    }
+  };
+  // One stream step: the load's maximum and (NEED_P) its mass; returns the maximum.
+  auto consume = [&](int j) -> float {
+    if (!valid_load(j)) r[j] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    const uint4 q = r[j];
     const float lm = load_max(q);
+    if (j == 0) {
+      // The first load has landed: only now deepen the pipeline (issuing earlier would delay it).
+      asm volatile("" :: "v"(lm));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = kLoadsFirst; jj <= kLoadsAhead && jj < kFastLoads; ++jj) issue(jj);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    } else if (j + kLoadsAhead < kFastLoads) {
+      issue(j + kLoadsAhead);
+    }
     if constexpr (NEED_P) {
       const float m_new = max2(m_l, lm);
       const float ref_old = max2(m_l, -3.4028234663852886e38f);
@@ -309,18 +307,63 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     // Keep each load's work at its own step: without this the compiler may sink the whole exp
     // chain (which only feeds the final sum) past the loop and keep every load's data alive.
     asm volatile("" : "+v"(s_l), "+v"(m_l), "+v"(nan_or));
-    const bool flag = lm >= theta;
-    const uint64_t mask = __ballot(flag);
-    if (mask) {
-      if (flag) {
-        const uint32_t at = wcnt + mbcnt(mask);
-        if (at < (uint32_t)kStashPerWave) {
-          stash[at] = q;
-          stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
-        }
-      }
-      wcnt += (uint32_t)__popcll(mask);
+    return lm;
+  };
+
+  // Step 0, exchange 1: wave maxima of the first-load lane maxima; slot scan, step 1.
+  const float lm0 = consume(0);
+  const uint32_t key0 = key_of<E>(__float_as_uint(lm0) >> 16);
+  {
+    const uint32_t wk = wave_reduce(key0, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    if (lane == 0) fs.kmax0_w[wid] = wk;
+  }
+  const SlotScan sscan = slot_step1(opt_e, fs);
+  lds_barrier();
+  // Step 1, exchange 2: histogram of distances to the block's first-load maximum; slot step 2.
+  const float lm1 = consume(1);
+  uint32_t kmax0 = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) kmax0 = kmax0 > fs.kmax0_w[w] ? kmax0 : fs.kmax0_w[w];
+  {
+    const uint32_t dist = kmax0 - key0;  // keys below 0x80 are -inf or NaN: not counted
+    if (dist < (uint32_t)kThetaBins && (key0 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist], 1u);
+  }
+  if (a.R <= kThreads) slot_step2(a, b, sscan, fs);
+  lds_barrier();
+  // Step 2, exchange 3: wave 0 finds the smallest distance whose cumulative count reaches the rank
+  // (when fewer maxima are within reach, the deepest reachable key).
+  const float lm2 = consume(2);
+  if (wid == 0) {
+    uint32_t hc[4];
+    uint32_t lsum = 0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      hc[q4] = fs.theta_hist[lane * 4 + q4];
+      lsum += hc[q4];
     }
+    uint32_t tot;
+    uint32_t run = wave_excl_sum(lsum, tot);
+    uint32_t found = 0xFFFFFFFFu;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      run += hc[q4];
+      if (found == 0xFFFFFFFFu && run >= theta_rank) found = lane * 4 + q4;
+    }
+    const uint32_t dmin = wave_reduce(found, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    const uint32_t dsel = dmin != 0xFFFFFFFFu ? dmin : (uint32_t)kThetaBins - 1u;
+    if (lane == 0) fs.theta_key = kmax0 > dsel ? kmax0 - dsel : 0u;
+  }
+  lds_barrier();
+  const uint32_t theta_key = fs.theta_key;
+  theta = E::to_float(bits_of_key<E>(theta_key));
+  slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
+  stash_load(0, r[0], lm0);
+  stash_load(1, r[1], lm1);
+  stash_load(2, r[2], lm2);
+#pragma unroll
+  for (int j = 3; j < kFastLoads; ++j) {
+    const float lm = consume(j);
+    stash_load(j, r[j], lm);
   }
 
   // ---- 3. Row maximum, mass, status: per-wave partials, one exchange ------------------------
@@ -408,7 +451,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
   auto d_of = [&](uint32_t word) { return kmax - key_of<E>(word >> 16); };
-  for (uint32_t i = lane; i < nc_here; i += kWaveSize) atomicAdd(&hcnt[d_of(cand[i])], 1u);
+  // Count histogram, and the race noise of every candidate (computed here, while the block
+  // waits for its slowest wave, rather than after the threshold).
+  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
+  const uint64_t seed = a.seeds[b], pos = a.positions[b];
+  for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
+    const uint32_t wd = cand[i];
+    atomicAdd(&hcnt[d_of(wd)], 1u);
+    const uint32_t id = id0 + (wd & 0x3FFFu);
+    noise[i] = race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
+  }
   if (lane == 0) fs.wave_cand[wid] = ncand;
   lds_barrier();
   uint32_t ntot = 0;
@@ -503,12 +555,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   // ---- 5a. Race over the survivors (and per-wave group member counts) ------------------------
   // A candidate survives iff d <= d* (bins failing min-p lie beyond d*).
-  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
   uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(lds + kOffGrpCnt) + wid * kMaxGroups;
   if (capture) {
     for (uint32_t g = lane; g < (uint32_t)kMaxGroups; g += kWaveSize) grp_cnt[g] = 0u;
   }
-  const uint64_t seed = a.seeds[b], pos = a.positions[b];
   const float invT = 1.0f / T;
   float b1 = -__builtin_inff(), b2 = -__builtin_inff();  // lane's best two float32 scores
   int32_t b1_id = 0x7FFFFFFF;
@@ -518,10 +568,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const uint32_t d = d_of(wd);
     if ((int32_t)d <= dstar) {
       const uint32_t id = id0 + (wd & 0x3FFFu);
-      const float u = (float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f;
-      const float gn = race_noise(u);
-      noise[i] = gn;
-      const float sc = (value_of_d(d) - m) * invT + gn;
+      const float sc = (value_of_d(d) - m) * invT + noise[i];
       if (sc > b1) {
         b2 = b1;
         b1 = sc;
