@@ -51,18 +51,86 @@ def measured_traffic(bytes_per_launch_alg: float):
 
 
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample: rows of the batch in order, cycling,
+    until the time budget is spent."""
     import oracle
+    decoded = {}
     rows, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and rows < wl.B:
-        r = rows
-        oracle.sample_row(oracle.decode_logits(wl.logits[r], wl.dtype), wl.temperature[r],
-                          wl.top_k[r], wl.top_p[r], wl.min_p[r], int(wl.seeds[r]),
-                          int(wl.positions[r]))
+    while time.perf_counter() - t0 < budget_s:
+        r = rows % wl.B
+        if r not in decoded:
+            decoded[r] = oracle.decode_logits(wl.logits[r], wl.dtype)
+        oracle.sample_row(decoded[r], wl.temperature[r], wl.top_k[r], wl.top_p[r], wl.min_p[r],
+                          int(wl.seeds[r]), int(wl.positions[r]))
         rows += 1
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of the B={wl.B}, V={wl.V} bf16 batch, one process "
-                      f"(numpy sort-based float64 oracle), {dt:.1f} s"}
+            "sample": f"{rows} rows (rows 0..{min(rows, wl.B) - 1} of the B={wl.B}, V={wl.V} "
+                      f"{wl.dtype} batch, cycled) through oracle.sample_row in one process and "
+                      f"one thread, {dt:.1f} s; bf16 decoding done once per row outside the clock"}
+
+
+def copy_calibration(dev, nbytes: int, reps: int = 5) -> None:
+    """A plain streaming kernel of known traffic for scaling the HBM counters: torch.neg over a
+    bfloat16 buffer reads nbytes and writes nbytes once per launch."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+# How the counter CSVs that --ingest-pmc reads are made (run from /tmp with TMPDIR=/tmp; R is the
+# repository root).
+PMC_COMMANDS = [
+    'timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$R/gpurun_out/prof/fetch" '
+    '-o fetch -- python3 "$R/bench.py" --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration',
+    'timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$R/gpurun_out/prof/write" '
+    '-o write -- python3 "$R/bench.py" --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration',
+    'python3 bench.py --ingest-pmc gpurun_out/prof/fetch/fetch_counter_collection.csv '
+    'gpurun_out/prof/write/write_counter_collection.csv <JSON line of a bench run of the same kernel>',
+]
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) -> dict:
+    """Per-launch HBM traffic of the sampler kernel from two rocprofv3 --pmc counter CSVs
+    (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter
+    reads for the copy calibration kernel of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row.get("Dispatch_Id", row.get("Correlation_Id")))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+        out = {}
+        for (name, _), v in vals.items():
+            out.setdefault(name, []).append(v)
+        return out
+
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        k = per_kernel(path, counter)
+        samp = [v for n, v in k.items() if "sample_fast_kernel" in n]
+        copy = [v for n, v in k.items() if "neg_kernel" in n]
+        if not samp or not copy:
+            raise SystemExit(f"{path}: no sampler or calibration dispatches for {counter}")
+        s_kib = statistics.median([x for v in samp for x in v])
+        c_kib = statistics.median([x for v in copy for x in v])
+        factor = copy_bytes / (c_kib * 1024.0)
+        res[counter] = {"kernel_kib_median": s_kib, "copy_kib_median": c_kib,
+                        "copy_known_bytes": copy_bytes, "scale": factor,
+                        "kernel_bytes_scaled": s_kib * 1024.0 * factor,
+                        "kernel_dispatches": sum(len(v) for v in samp)}
+    total = res["FETCH_SIZE"]["kernel_bytes_scaled"] + res["WRITE_SIZE"]["kernel_bytes_scaled"]
+    return {"commands": PMC_COMMANDS, "counters": res, "hbm_bytes_per_launch": total,
+            "algorithmic_bytes_per_launch": alg_bytes, "ratio_to_algorithmic": total / alg_bytes,
+            "kernel_source_hash": kernel_source_hash()}
 
 
 def main() -> int:
@@ -72,6 +140,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run the known-size copy kernel that scales the HBM counters")
+    ap.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LINE"),
+                    help="write the traffic summary from two rocprofv3 --pmc counter CSVs and "
+                         "the JSON line of a bench run of the same kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: rows are independent, so the sampler shards by "
@@ -79,24 +152,35 @@ def main() -> int:
         return 2
 
     import numpy as np
-    import torch
-    import top_support_capture_amd as tsc
     from workloads import make_workload
-    from tests.gpu_helpers import device_inputs
+    if not args.ingest_pmc:
+        import torch
+        import top_support_capture_amd as tsc
+        from tests.gpu_helpers import device_inputs
 
     wl = make_workload(args.workload)
+    in_bytes = wl.B * wl.V * (2 if wl.dtype == "bf16" else 4)
+    if args.ingest_pmc:
+        with open(args.ingest_pmc[2]) as f:
+            bench_line = json.loads(f.read().strip().splitlines()[-1])
+        alg = int(bench_line["algorithmic_bytes_per_launch"])
+        t = ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], alg, in_bytes)
+        path = os.path.join(ROOT, "profiles", f"traffic_b{wl.B}_v{wl.V}_{wl.dtype}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
     dev = torch.device("cuda:0")
     d = device_inputs(wl)
-    in_bytes = wl.B * wl.V * (2 if wl.dtype == "bf16" else 4)
     ncopies = max(1, -(-512 * 2**20 // in_bytes) + 1)
     copies = [d["logits"]] + [d["logits"].clone() for _ in range(ncopies - 1)]
-    out = tsc.sample_with_mask(copies[0], d["temperature"], d["top_k"], d["top_p"], d["min_p"],
-                               d["optin_rows"], d["seeds"], d["positions"], wl.W)
     stream = torch.cuda.current_stream(dev)
+    call = tsc.prepare(copies[0], d["temperature"], d["top_k"], d["top_p"], d["min_p"],
+                       d["optin_rows"], d["seeds"], d["positions"], wl.W, stream=stream)
+    out = call.out
 
     def step(i):
-        tsc.sample_with_mask(copies[i % ncopies], d["temperature"], d["top_k"], d["top_p"],
-                             d["min_p"], d["optin_rows"], d["seeds"], d["positions"], wl.W, out=out)
+        call(copies[i % ncopies], check=False)
 
     for i in range(args.warmup):
         step(i)
@@ -114,6 +198,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     durs_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if args.copy_calibration:
+        copy_calibration(dev, in_bytes)
 
     lengths = out.lengths.cpu().numpy().astype(np.int64)
     status = out.row_status.cpu().numpy()

@@ -14,7 +14,8 @@ from typing import NamedTuple, Optional
 
 import torch  # must come first: the library binds to the HIP runtime PyTorch has loaded
 
-__all__ = ["sample_with_mask", "SampleOutput", "workspace_size", "library", "LIB_PATH",
+__all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "workspace_size",
+           "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
            "MAX_PACKED_WIDTH", "TscError"]
 
@@ -79,6 +80,97 @@ def _check(t: torch.Tensor, name: str, dtype, n: int, dev) -> None:
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape [{n}] on {dev}")
 
 
+def _check_out(out: "SampleOutput", B: int, R: int, W: int, dev) -> None:
+    Wc = max(int(W), 1)
+    _check(out.tokens, "out.tokens", torch.int32, B, dev)
+    _check(out.row_status, "out.row_status", torch.int8, B, dev)
+    _check(out.lengths, "out.lengths", torch.int32, R, dev)
+    _check(out.selected_logprob, "out.selected_logprob", torch.float32, R, dev)
+    for name, t, dt in (("packed_ids", out.packed_ids, torch.int32),
+                        ("logprobs", out.logprobs, torch.float32)):
+        if t is None and name == "logprobs":
+            continue
+        if (t.device != dev or t.dtype != dt or tuple(t.shape) != (R, Wc)
+                or not t.is_contiguous()):
+            raise ValueError(f"out.{name} must be a contiguous {dt} tensor of shape [{R}, {Wc}] "
+                             f"on {dev}")
+
+
+class PreparedSample:
+    """A validated argument set for repeated calls that differ only in the logits tensor (same
+    shape, dtype, device and strides): each call is one library call with cached pointers."""
+
+    def __init__(self, logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
+                 top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
+                 seeds: torch.Tensor, positions: torch.Tensor, W: int,
+                 return_logprobs: bool = True, out: Optional[SampleOutput] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self._lib = library()
+        if logits.dim() != 2 or logits.stride(1) != 1:
+            raise ValueError("logits must be [B, V] with unit column stride")
+        if logits.dtype == torch.float32:
+            dt = TSC_DTYPE_F32
+        elif logits.dtype == torch.bfloat16:
+            dt = TSC_DTYPE_BF16
+        else:
+            raise ValueError("logits must be float32 or bfloat16")
+        dev = logits.device
+        B, V = logits.shape
+        ld = logits.stride(0) if B > 1 else V
+        R = int(optin_rows.numel())
+        _check(temperature, "temperature", torch.float32, B, dev)
+        _check(top_k, "top_k", torch.int32, B, dev)
+        _check(top_p, "top_p", torch.float32, B, dev)
+        _check(min_p, "min_p", torch.float32, B, dev)
+        _check(optin_rows, "optin_rows", torch.int32, R, dev)
+        _check(seeds, "seeds", torch.int64, B, dev)
+        _check(positions, "positions", torch.int64, B, dev)
+        if out is None:
+            Wc = max(int(W), 1)
+            out = SampleOutput(
+                tokens=torch.empty(B, dtype=torch.int32, device=dev),
+                packed_ids=torch.empty((R, Wc), dtype=torch.int32, device=dev),
+                lengths=torch.empty(R, dtype=torch.int32, device=dev),
+                logprobs=(torch.empty((R, Wc), dtype=torch.float32, device=dev)
+                          if return_logprobs else None),
+                selected_logprob=torch.empty(R, dtype=torch.float32, device=dev),
+                row_status=torch.empty(B, dtype=torch.int8, device=dev))
+        else:
+            _check_out(out, B, R, W, dev)
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.out = out
+        self._shape = (tuple(logits.shape), tuple(logits.stride()), logits.dtype, dev)
+        # Keep the argument tensors alive as long as their pointers are cached.
+        self._keep = (temperature, top_k, top_p, min_p, optin_rows, seeds, positions, s)
+        self._tail = (
+            dt, B, V, ld, temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(),
+            min_p.data_ptr(), _ptr(optin_rows) if R else None, R, seeds.data_ptr(),
+            positions.data_ptr(), int(W), out.tokens.data_ptr(), out.row_status.data_ptr(),
+            _ptr(out.packed_ids) if R else None,
+            _ptr(out.logprobs) if (R and out.logprobs is not None) else None,
+            _ptr(out.lengths) if R else None, _ptr(out.selected_logprob) if R else None,
+            None, 0, s.cuda_stream)
+
+    def __call__(self, logits: torch.Tensor, check: bool = True) -> SampleOutput:
+        if check and (tuple(logits.shape), tuple(logits.stride()), logits.dtype,
+                      logits.device) != self._shape:
+            raise ValueError("logits must match the prepared shape, strides, dtype and device")
+        code = self._lib.tsc_sample_with_mask(logits.data_ptr(), *self._tail)
+        if code != 0:
+            raise TscError(code, self._lib.tsc_status_string(code).decode())
+        return self.out
+
+
+def prepare(logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
+            top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
+            seeds: torch.Tensor, positions: torch.Tensor, W: int, return_logprobs: bool = True,
+            out: Optional[SampleOutput] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> PreparedSample:
+    """Validate the arguments once; the returned object samples a logits tensor per call."""
+    return PreparedSample(logits, temperature, top_k, top_p, min_p, optin_rows, seeds, positions,
+                          W, return_logprobs, out, stream)
+
+
 def sample_with_mask(logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
                      top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
                      seeds: torch.Tensor, positions: torch.Tensor, W: int,
@@ -91,44 +183,5 @@ def sample_with_mask(logits: torch.Tensor, temperature: torch.Tensor, top_k: tor
     ``positions`` int64 [B] holding the uint64 bit patterns. Outputs are allocated on the
     logits' device unless ``out`` supplies them. Runs asynchronously on ``stream`` (default: the
     current stream)."""
-    lib = library()
-    if logits.dim() != 2 or logits.stride(1) != 1:
-        raise ValueError("logits must be [B, V] with unit column stride")
-    if logits.dtype == torch.float32:
-        dt = TSC_DTYPE_F32
-    elif logits.dtype == torch.bfloat16:
-        dt = TSC_DTYPE_BF16
-    else:
-        raise ValueError("logits must be float32 or bfloat16")
-    dev = logits.device
-    B, V = logits.shape
-    ld = logits.stride(0) if B > 1 else V
-    R = int(optin_rows.numel())
-    _check(temperature, "temperature", torch.float32, B, dev)
-    _check(top_k, "top_k", torch.int32, B, dev)
-    _check(top_p, "top_p", torch.float32, B, dev)
-    _check(min_p, "min_p", torch.float32, B, dev)
-    _check(optin_rows, "optin_rows", torch.int32, R, dev)
-    _check(seeds, "seeds", torch.int64, B, dev)
-    _check(positions, "positions", torch.int64, B, dev)
-    if out is None:
-        Wc = max(int(W), 1)
-        out = SampleOutput(
-            tokens=torch.empty(B, dtype=torch.int32, device=dev),
-            packed_ids=torch.empty((R, Wc), dtype=torch.int32, device=dev),
-            lengths=torch.empty(R, dtype=torch.int32, device=dev),
-            logprobs=torch.empty((R, Wc), dtype=torch.float32, device=dev) if return_logprobs else None,
-            selected_logprob=torch.empty(R, dtype=torch.float32, device=dev),
-            row_status=torch.empty(B, dtype=torch.int8, device=dev))
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
-    code = lib.tsc_sample_with_mask(
-        logits.data_ptr(), dt, B, V, ld, temperature.data_ptr(), top_k.data_ptr(),
-        top_p.data_ptr(), min_p.data_ptr(), _ptr(optin_rows) if R else None, R,
-        seeds.data_ptr(), positions.data_ptr(), int(W), out.tokens.data_ptr(),
-        out.row_status.data_ptr(), _ptr(out.packed_ids) if R else None,
-        _ptr(out.logprobs) if (R and out.logprobs is not None) else None,
-        _ptr(out.lengths) if R else None, _ptr(out.selected_logprob) if R else None,
-        None, 0, s.cuda_stream)
-    if code != 0:
-        raise TscError(code, lib.tsc_status_string(code).decode())
-    return out
+    return PreparedSample(logits, temperature, top_k, top_p, min_p, optin_rows, seeds, positions,
+                          W, return_logprobs, out, stream)(logits, check=False)
