@@ -67,9 +67,10 @@ __device__ inline uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
       k0 += W0;
       k1 += W1;
     }
-    const uint32_t hi_a = __umulhi(M0, x.x), lo_a = M0 * x.x;
-    const uint32_t hi_b = __umulhi(M1, x.z), lo_b = M1 * x.z;
-    x = make_uint4(hi_b ^ x.y ^ k0, lo_b, hi_a ^ x.w ^ k1, lo_a);
+    // One full 32x32 -> 64-bit product per multiplier (v_mad_u64_u32) gives both halves.
+    const uint64_t pa = (uint64_t)M0 * x.x, pb = (uint64_t)M1 * x.z;
+    x = make_uint4((uint32_t)(pb >> 32) ^ x.y ^ k0, (uint32_t)pb, (uint32_t)(pa >> 32) ^ x.w ^ k1,
+                   (uint32_t)pa);
   }
   return x;
 }

@@ -1,27 +1,28 @@
 // Single-read sampler kernel for bfloat16 rows (one 1024-thread workgroup per row).
 //
-// HBM is the bound: a row is read exactly once, with every 16-byte load of the row in flight at
-// once, and all per-element work happens while the loads land. Wave w owns a contiguous segment
-// of the row (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
+// HBM is the bound: a row is read exactly once through a shallow pipeline of 16-byte loads, and
+// all per-element work happens while the loads land. Wave w owns a contiguous segment of the row
+// (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
 //
-//   1. Stream the loads through a shallow pipeline. The lane maxima of the first load of every
-//      segment (a sample spread over the whole row) pick a cutoff theta that about twice top_k
-//      tokens of the row should exceed: an LDS histogram of their key distances to the sample's
-//      maximum, built over the first stream steps so that the loads keep flowing.
-//   2. As each load lands: running maximum and (top_p < 1) an online sum of exp((x - max) / T)
-//      per lane; a ballot over "this load's maximum >= theta" stashes the whole 16-byte load in
-//      the wave's LDS stash, in id order.
-//   3. After the last load: row maximum m and total mass Z (block reductions), then the stash is
-//      expanded into candidate words (d << 18 | id) with d = key(m) - key(x), still in id order.
-//   4. A histogram over d of candidate counts and fixed-point masses, and one block scan, give
-//      the joint threshold exactly: the largest d with fewer than k tokens strictly above and
-//      (top_p < 1) mass strictly above <= top_p * Z; min-p drops candidates below its cutoff.
+//   1. Stream. The lane maxima of the first load of every segment (a sample spread over the whole
+//      row) give a reference R for the mass and a cutoff theta that about twice top_k tokens of
+//      the row should exceed: an LDS histogram of their key distances to the sample's maximum,
+//      built over the first stream steps so that the loads keep flowing.
+//   2. As each load lands: running maximum (NaN-propagating, so it also detects NaN), for
+//      top_p < 1 the lane sum of exp2(x * log2(e) / T - R * log2(e) / T), and a ballot on "this
+//      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash.
+//   3. Each wave, as soon as its segment is done: expands its stash into candidate words
+//      (bf16 bits << 16 | offset in the segment), still in id order, counts them into a
+//      histogram over key - key(theta), and draws their race noise (Philox4x32-10).
+//   4. One wave reads the per-wave results and scans the histogram bins from the maximum down:
+//      the joint threshold is the largest distance d from the maximum with fewer than k tokens
+//      strictly above and (top_p < 1) mass strictly above <= top_p * Z; min-p drops whole bins.
 //      theta was a true lower bound iff at least k candidates were found (checked here).
-//   5. Race over the survivors (Philox4x32-10 uniforms; float32 scores, float64 for the few within
-//      1e-4 of the best), then, for opt-in rows, the ordered capture: bins give each tie group's
-//      base position and a ballot multisplit ranks the group's members by id.
-// Any row this path cannot serve exactly (capacities, theta above the k-th value, greedy rows,
-// other dtypes or layouts) runs through general_row in the same workgroup.
+//   5. Race over the survivors (float32 scores, float64 for the few within 1e-4 of the best),
+//      then, for opt-in rows, the ordered capture: the bin scan gives each tie group's base
+//      position and a ballot multisplit ranks the group's members by id.
+// Any row this path cannot serve exactly (capacities, theta above the k-th value, overflow of
+// the mass, greedy rows, other dtypes or layouts) runs through general_row in the same workgroup.
 #pragma once
 
 #include "tsc_general.h"
@@ -35,6 +36,7 @@ constexpr int kStashPerWave = 256;    // stashed loads per wave
 constexpr int kCandPerWave = 512;     // candidate words per wave
 constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
 constexpr int kMaxGroups = 256;       // distinct keys in a captured support
+constexpr int kThetaBins = 256;       // key distances of the sampled maxima below their maximum
 constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
 constexpr int32_t kFastMaxK = 1536;
@@ -45,27 +47,27 @@ constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of
 constexpr int kOffStash = 0;                                          // uint4 [16][256]
 constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16][256]
 constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
-constexpr int kOffCnt = kOffCand + kWaves * kCandPerWave * 4;         // u32 [1024]
-constexpr int kOffNoise = kOffCnt + kDBins * 4;                       // f32 [16][512] race noise
-constexpr int kFastLdsEnd = kOffNoise + kWaves * kCandPerWave * 4;
-// Overlays of the stash region once it has been expanded:
-constexpr int kOffExclCnt = 0;                                    // u32 [1024] by d
-constexpr int kOffGroup = kOffExclCnt + kDBins * 4;               // u16 [1024] by d
-constexpr int kOffGrpCnt = kOffGroup + kDBins * 2;                // u32 [16][256] members per wave
+constexpr int kOffNoise = kOffCand + kWaves * kCandPerWave * 4;       // f32 [16][512] race noise
+constexpr int kOffCnt = kOffNoise + kWaves * kCandPerWave * 4;        // u32 [1024] by key - theta
+constexpr int kFastLdsEnd = kOffCnt + kDBins * 4;
+// Overlays of the stash region, written once every wave has expanded its stash:
+constexpr int kOffGroupOfD = 0;                                   // u16 [1024] tie group of bin d
+constexpr int kOffGrpCnt = kOffGroupOfD + kDBins * 2;             // u32 [16][256] members per wave
 constexpr int kOffCursor = kOffGrpCnt + kWaves * kMaxGroups * 4;  // u32 [16][256] write cursors
 constexpr int kOffGrpBase = kOffCursor + kWaves * kMaxGroups * 4; // u32 [256]
 constexpr int kOffLpTab = kOffGrpBase + kMaxGroups * 4;           // f32 [256]
 constexpr int kOffOverlayEnd = kOffLpTab + kMaxGroups * 4;
-static_assert(kOffOverlayEnd <= kOffCand, "overlays must fit in the stash region");
+static_assert(kOffOverlayEnd <= kOffStashCh, "overlays must fit in the stash region");
 
 constexpr size_t kFastDynLds =
     (size_t)kGeneralDynLds + sizeof(GeneralShared) > (size_t)kFastLdsEnd
         ? (size_t)kGeneralDynLds + sizeof(GeneralShared)
         : (size_t)kFastLdsEnd;
 
-// Per-wave partial results exchanged through LDS (one barrier per exchange).
-constexpr int kThetaBins = 256;       // key distances from the block's first-load maximum
+// Outcome of the status checks and the bin scan, published by wave 0.
+enum FastDecision : int32_t { kProceed = 0, kNonfinite = 1, kNoSupport = 2, kFallback = 3 };
 
+// Per-wave partial results exchanged through LDS (one barrier per exchange).
 struct FastShared {
   uint64_t red[kWaves];
   uint32_t theta_hist[kThetaBins];
@@ -75,20 +77,17 @@ struct FastShared {
   int32_t slot_hit[kWaves];
   float wave_m[kWaves];
   double wave_z[kWaves];
-  uint32_t wave_nan[kWaves];
   uint32_t wave_stash[kWaves];
   uint32_t wave_cand[kWaves];
-  uint32_t scan_c[kWaves], scan_g[kWaves];
-  uint64_t scan_m[kWaves];
+  int32_t decision;
+  int32_t dstar;
+  uint32_t L, G;
   float race_b1[kWaves], race_b2[kWaves];
   int32_t race_id[kWaves];
   uint32_t race_d[kWaves];
   double ref_top[kWaves];
   int32_t ref_id[kWaves];
   uint32_t ref_d[kWaves];
-  int32_t dstar_w[kWaves];
-  uint32_t L_w[kWaves], G_w[kWaves];
-  uint64_t zs_w[kWaves];
 };
 
 __device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -96,6 +95,14 @@ __device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
 // Wave index, known to the compiler as wave-uniform (held in a scalar register).
 __device__ inline uint32_t wave_id() {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
+}
+
+// A value every lane holds alike, moved to a scalar register.
+__device__ inline float uniform_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ inline uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -110,25 +117,41 @@ struct SumU32 {
 struct SumU64 {
   __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a + b; }
 };
+struct SumF64 {
+  __device__ double operator()(double a, double b) const { return a + b; }
+};
 struct MaxI32 {
   __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; }
 };
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct OrU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
+};
 
 // Exclusive prefix sum over the wave (DPP); `total` receives the wave's sum.
-__device__ inline uint32_t wave_excl_sum(uint32_t v, uint32_t& total) {
-  const uint32_t inc = wave_incl_scan(v, SumU32(), 0u);
+template <class T, class Op>
+__device__ inline T wave_excl_scan(T v, Op op, T& total) {
+  const T inc = wave_incl_scan(v, op, (T)0);
   total = read_lane(inc, kWaveSize - 1);
   return inc - v;
 }
+__device__ inline uint32_t wave_excl_sum(uint32_t v, uint32_t& total) {
+  return wave_excl_scan(v, SumU32(), total);
+}
 
-// max(a, b) of non-NaN floats as one v_max3_f32 (no NaN canonicalisation of bit-cast inputs;
-// a NaN row is detected separately and never reaches a decision).
-__device__ inline float max3f(float a, float b, float c) {
+// IEEE 754-2019 maximum of three floats in one instruction: NaN in any input gives NaN (so a
+// running maximum also detects NaN logits), and -0 < +0 (both map to one key later).
+__device__ inline float maximum3f(float a, float b, float c) {
   float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-__device__ inline float max2(float a, float b) { return max3f(a, b, b); }
+__device__ inline float maximum2f(float a, float b) { return maximum3f(a, b, b); }
+struct MaximumF32 {
+  __device__ float operator()(float a, float b) const { return maximum2f(a, b); }
+};
 
 // Race noise g = -ln(-ln u) in float32 with the hardware log2. Measured over all 2^23 uniforms
 // of the race: -ln u has relative error <= 1.7e-7 (also for u next to 1) and g absolute error
@@ -144,7 +167,7 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 
 // Capture slot of row b from the first 1024 opt-in entries (e = optin_rows[tid] or INT32_MIN,
 // loaded before the row): an entry is valid iff in range and above every earlier entry. Done in
-// two steps that share the barriers of the cutoff selection. Marks slot b invalid when it is.
+// three steps that share the barriers of the cutoff selection. Marks slot b invalid when it is.
 struct SlotScan {
   int32_t e, excl_w;
 };
@@ -179,12 +202,111 @@ __device__ inline int64_t slot_step3(const FastShared& fs) {
   return slot;
 }
 
+// Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d;
+// hcnt is indexed by key - theta_key = dspan - d. Lane l owns the nb consecutive bins from l * nb.
+// Publishes the threshold d*, the support size and group count, and for capture rows fills the
+// tie-group tables (group of each bin, base position and logprob of each group).
+template <bool NEED_P>
+__device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
+                                      int32_t k, float p, float mp, double Z, bool capture,
+                                      const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
+  using E = Elem<TSC_DTYPE_BF16>;
+  const uint32_t lane = lane_id();
+  const uint32_t nb = (dspan + kWaveSize) / kWaveSize;  // 1..16
+  const bool need_m = mp > 0.0f;
+  const double tln_mp = need_m ? (double)T * log((double)mp) : 0.0;
+  auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
+  // Count and fixed-point mass of bin d after min-p (a per-value predicate, monotone in d).
+  auto bin = [&](uint32_t d, uint32_t& bc, uint64_t& bm) {
+    bc = 0;
+    bm = 0;
+    if (d <= dspan) {
+      const float x = value_of_d(d);
+      // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
+      if (!need_m || ((double)x - (double)m) >= tln_mp) {
+        bc = hcnt[dspan - d];
+        const float w = __builtin_amdgcn_exp2f((x - m) * c);
+        bm = (uint64_t)bc * (uint64_t)((double)w * 0x1p48);
+      }
+    }
+  };
+  uint32_t lc = 0, lg = 0;
+  uint64_t lmass = 0;
+  for (uint32_t t = 0; t < nb; ++t) {
+    uint32_t bc;
+    uint64_t bm;
+    bin(lane * nb + t, bc, bm);
+    lc += bc;
+    lg += bc > 0u;
+    lmass += bm;
+  }
+  uint32_t tc, tg;
+  uint64_t tm;
+  uint32_t ec = wave_excl_scan(lc, SumU32(), tc);
+  uint32_t eg = wave_excl_scan(lg, SumU32(), tg);
+  uint64_t em = wave_excl_scan(lmass, SumU64(), tm);
+  const double pz = (double)p * Z;
+  // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
+  // strictly above <= top_p * Z. Each predicate is monotone in d, so this is the last qualifying
+  // bin of the last lane that has one.
+  int32_t best = -1;
+  uint32_t bL = 0, bG = 0;
+  uint64_t bZ = 0;
+  uint16_t* group_of_d = reinterpret_cast<uint16_t*>(lds + kOffGroupOfD);
+  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
+  for (uint32_t t = 0; t < nb; ++t) {
+    const uint32_t d = lane * nb + t;
+    uint32_t bc;
+    uint64_t bm;
+    bin(d, bc, bm);
+    if (bc > 0u) {
+      const bool qual = ec < (uint32_t)k && (!NEED_P || (double)em * 0x1p-48 <= pz);
+      if (qual) {
+        best = (int32_t)d;
+        bL = ec + bc;
+        bG = eg + 1u;
+        bZ = em + bm;
+      }
+      if (capture && eg < (uint32_t)kMaxGroups) {
+        group_of_d[d] = (uint16_t)eg;
+        grp_base[eg] = ec;
+      }
+    }
+    ec += bc;
+    eg += bc > 0u;
+    em += bm;
+  }
+  // d* >= 0 always: bin 0 holds the maximum, which passes every predicate.
+  const int32_t dstar = wave_reduce(best, MaxI32());
+  const int owner = (int)((uint32_t)dstar / nb);
+  const uint32_t L = read_lane(bL, owner), G = read_lane(bG, owner);
+  const uint64_t zs = read_lane(bZ, owner);
+  int32_t decision = kProceed;
+  if (capture && G > (uint32_t)kMaxGroups) decision = kFallback;  // too spread for the tables
+  if (capture && decision == kProceed) {
+    const double lnzs = log((double)zs) - kFixShift * 0.6931471805599453;
+    float* lp_tab = reinterpret_cast<float*>(lds + kOffLpTab);
+    for (uint32_t t = 0; t < nb; ++t) {
+      const uint32_t d = lane * nb + t;
+      if ((int32_t)d <= dstar && hcnt[dspan - d] > 0u)
+        lp_tab[group_of_d[d]] = logprob_of(value_of_d(d), m, T, lnzs);
+    }
+  }
+  if (lane == 0) {
+    fs.decision = decision;
+    fs.dstar = dstar;
+    fs.L = L;
+    fs.G = G;
+  }
+}
+
 // Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
 // go through the general path instead; `slot` is then already set.
 template <bool NEED_P>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
                                               float T, int32_t k, float p, float mp,
-                                              unsigned char* lds, FastShared& fs) {
+                                              uint64_t seed, uint64_t pos, unsigned char* lds,
+                                              FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
   const uint16_t* row = reinterpret_cast<const uint16_t*>(a.logits) + b * a.ld;
@@ -194,6 +316,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t cw = (nch + kWaves - 1) / kWaves;        // chunks per wave segment
   const uint32_t seg0 = wid * cw;
   const uint32_t seg1 = seg0 + cw < nch ? seg0 + cw : nch;
+  const uint32_t nseg = seg1 - seg0;                      // chunks in this wave's segment
   const uint32_t id0 = seg0 * 8u;                         // first token id of the segment
 
   // Rank of theta among the 1024 lane maxima of the first loads: aim for about 2k + 64 tokens
@@ -215,7 +338,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // zero and are replaced below), one shared VGPR offset, and a scalar offset per load.
   uint4 r[kFastLoads];
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint4*>(rowv + seg0), (short)0, (int)((seg1 - seg0) * 16u), 0x00020000);
+      const_cast<uint4*>(rowv + seg0), (short)0, (int)(nseg * 16u), 0x00020000);
   const int voff = (int)(lane * 16u);
   auto issue = [&](int j) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, j * kWaveSize * 16, 0);
@@ -228,27 +351,44 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
-  auto valid_load = [&](int j) { return seg0 + (uint32_t)j * kWaveSize + lane < seg1; };
-  auto load_max = [&](const uint4& q) {
-    const float a0 = max3f(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y));
-    const float a1 = max3f(bf16_hi(q.y), bf16_lo(q.z), bf16_hi(q.z));
-    return max3f(a0, a1, max2(bf16_lo(q.w), bf16_hi(q.w)));
-  };
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
   hcnt[tid] = 0u;  // published by the first exchange below
   if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
 
-  // ---- 2. Stream: max, online mass, cutoff, stash --------------------------------------------
-  // The cutoff theta comes from the lane maxima of the first load of every segment: the
-  // theta_rank-th largest of them (their distances to the block's maximum are histogrammed in
-  // LDS; wave 0 scans the histogram). Its three exchanges ride on the first stream steps, so the
-  // loads keep flowing; the first loads wait in registers until theta is known. The capture slot
-  // lookup shares the same exchanges.
+  // Lanes past the segment's end read zeros: only loads that reach the end need the test.
+  auto mask_tail = [&](int j) {
+    if ((uint32_t)(j + 1) * kWaveSize > nseg && (uint32_t)j * kWaveSize + lane >= nseg)
+      r[j] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  };
+  auto unpack = [](const uint4& q, float (&f)[8]) {
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_lo(w4[e]);
+      f[2 * e + 1] = bf16_hi(w4[e]);
+    }
+  };
+  auto load_max = [](const float (&f)[8]) {
+    const float a0 = maximum3f(f[0], f[1], f[2]);
+    const float a1 = maximum3f(f[3], f[4], f[5]);
+    return maximum3f(a0, a1, maximum2f(f[6], f[7]));
+  };
+
+  // ---- 2. Stream: max, mass, cutoff, stash ---------------------------------------------------
   const float c = 1.4426950408889634f / T;  // log2(e) / T
-  float m_l = -__builtin_inff();  // lane maximum
-  float s_l = 0.0f;               // lane mass relative to max(m_l, -FLT_MAX)
-  uint32_t nan_or = 0;            // NaN detection when the mass (which would carry it) is skipped
-  uint32_t wcnt = 0;              // wave's stashed loads (wave-uniform)
+  float nrc = 0.0f;               // -R * c, R the reference of the mass (set after exchange 1)
+  float m_l = -__builtin_inff();  // lane maximum (NaN if the lane saw a NaN)
+  float s_a = 0.0f, s_b = 0.0f;   // lane mass: sums of exp2(x * c - R * c), two chains
+  auto add_mass = [&](const float (&f)[8]) {
+    if constexpr (NEED_P) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        s_a += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, nrc));
+        s_b += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e + 1], c, nrc));
+      }
+    }
+  };
+  uint32_t wcnt = 0;  // wave's stashed loads (wave-uniform)
   uint4* stash = reinterpret_cast<uint4*>(lds + kOffStash) + wid * kStashPerWave;
   uint32_t* stash_ch = reinterpret_cast<uint32_t*>(lds + kOffStashCh) + wid * kStashPerWave;
   float theta = __builtin_inff();
@@ -266,64 +406,50 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       wcnt += (uint32_t)__popcll(mask);
     }
   };
-  // One stream step: the load's maximum and (NEED_P) its mass; returns the maximum.
-  auto consume = [&](int j) -> float {
-    if (!valid_load(j)) r[j] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-    const uint4 q = r[j];
-    const float lm = load_max(q);
-    if (j == 0) {
-      // The first load has landed: only now deepen the pipeline (issuing earlier would delay it).
-      asm volatile("" :: "v"(lm));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int jj = kLoadsFirst; jj <= kLoadsAhead && jj < kFastLoads; ++jj) issue(jj);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-    } else if (j + kLoadsAhead < kFastLoads) {
-      issue(j + kLoadsAhead);
-    }
-    if constexpr (NEED_P) {
-      const float m_new = max2(m_l, lm);
-      const float ref_old = max2(m_l, -3.4028234663852886e38f);
-      const float ref = max2(m_new, -3.4028234663852886e38f);
-      float acc = s_l * __builtin_amdgcn_exp2f((ref_old - ref) * c);
-      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += __builtin_amdgcn_exp2f((bf16_lo(w4[e]) - ref) * c);
-        acc += __builtin_amdgcn_exp2f((bf16_hi(w4[e]) - ref) * c);
-      }
-      s_l = acc;
-      m_l = m_new;
-    } else {
-      m_l = max2(m_l, lm);
-      // NaN has all exponent bits set and a nonzero mantissa: |bits| > 0x7F80 in either half.
-      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        nan_or |= ((w4[e] & 0x7FFFu) > 0x7F80u) | (((w4[e] >> 16) & 0x7FFFu) > 0x7F80u);
-      }
-    }
-    // Keep each load's work at its own step: without this the compiler may sink the whole exp
-    // chain (which only feeds the final sum) past the loop and keep every load's data alive.
-    asm volatile("" : "+v"(s_l), "+v"(m_l), "+v"(nan_or));
-    return lm;
-  };
+  // Keep each load's work at its own step: without this the compiler may sink the exp chain
+  // (which only feeds the final sum) past the loop and keep every load's data alive.
+  auto pin = [&]() { asm volatile("" : "+v"(s_a), "+v"(s_b), "+v"(m_l)); };
 
   // Step 0, exchange 1: wave maxima of the first-load lane maxima; slot scan, step 1.
-  const float lm0 = consume(0);
+  float f[8];
+  mask_tail(0);
+  unpack(r[0], f);
+  const float lm0 = load_max(f);
+  m_l = maximum2f(m_l, lm0);
+  // The first load has landed: only now deepen the pipeline (issuing earlier would delay it).
+  asm volatile("" ::"v"(lm0));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jj = kLoadsFirst; jj <= kLoadsAhead && jj < kFastLoads; ++jj) issue(jj);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   const uint32_t key0 = key_of<E>(__float_as_uint(lm0) >> 16);
   {
-    const uint32_t wk = wave_reduce(key0, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    const uint32_t wk = wave_reduce(key0, MaxU32());
     if (lane == 0) fs.kmax0_w[wid] = wk;
   }
   const SlotScan sscan = slot_step1(opt_e, fs);
   lds_barrier();
-  // Step 1, exchange 2: histogram of distances to the block's first-load maximum; slot step 2.
-  const float lm1 = consume(1);
+  // Step 1, exchange 2: the mass reference R = the sample's maximum; histogram of the distances
+  // to it; slot step 2.
   uint32_t kmax0 = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) kmax0 = kmax0 > fs.kmax0_w[w] ? kmax0 : fs.kmax0_w[w];
+  kmax0 = uniform_u32(kmax0);
+  {
+    const float R = E::to_float(bits_of_key<E>(kmax0));
+    // A non-finite sample maximum (all -inf, or +inf/NaN: the row is then nonfinite anyway)
+    // takes R = 0; a mass that overflows sends the row to the general path.
+    nrc = uniform_f32(__builtin_isfinite(R) ? -R * c : 0.0f);
+  }
+  add_mass(f);
+  issue(kLoadsAhead + 1);
+  mask_tail(1);
+  unpack(r[1], f);
+  const float lm1 = load_max(f);
+  m_l = maximum2f(m_l, lm1);
+  add_mass(f);
+  pin();
   {
     const uint32_t dist = kmax0 - key0;  // keys below 0x80 are -inf or NaN: not counted
     if (dist < (uint32_t)kThetaBins && (key0 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist], 1u);
@@ -332,7 +458,13 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   lds_barrier();
   // Step 2, exchange 3: wave 0 finds the smallest distance whose cumulative count reaches the rank
   // (when fewer maxima are within reach, the deepest reachable key).
-  const float lm2 = consume(2);
+  issue(kLoadsAhead + 2);
+  mask_tail(2);
+  unpack(r[2], f);
+  const float lm2 = load_max(f);
+  m_l = maximum2f(m_l, lm2);
+  add_mass(f);
+  pin();
   if (wid == 0) {
     uint32_t hc[4];
     uint32_t lsum = 0;
@@ -354,7 +486,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (lane == 0) fs.theta_key = kmax0 > dsel ? kmax0 - dsel : 0u;
   }
   lds_barrier();
-  const uint32_t theta_key = fs.theta_key;
+  const uint32_t theta_key = uniform_u32(fs.theta_key);
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
   stash_load(0, r[0], lm0);
@@ -362,68 +494,35 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   stash_load(2, r[2], lm2);
 #pragma unroll
   for (int j = 3; j < kFastLoads; ++j) {
-    const float lm = consume(j);
+    if (j + kLoadsAhead < kFastLoads) issue(j + kLoadsAhead);
+    mask_tail(j);
+    unpack(r[j], f);
+    const float lm = load_max(f);
+    m_l = maximum2f(m_l, lm);
+    add_mass(f);
+    pin();
     stash_load(j, r[j], lm);
   }
 
-  // ---- 3. Row maximum, mass, status: per-wave partials, one exchange ------------------------
+  // ---- 3. Per wave, as soon as its segment is done: partials, expansion, histogram, noise ------
   {
-    const float wm = wave_reduce(m_l, [](float x, float y) { return x > y ? x : y; });
+    const float wm = wave_reduce(m_l, MaximumF32());
     double wz = 0.0;
-    if constexpr (NEED_P) {
-      const float ref_l = max2(m_l, -3.4028234663852886e38f);
-      const float ref_w = max2(wm, -3.4028234663852886e38f);
-      wz = wave_reduce((double)(s_l * __builtin_amdgcn_exp2f((ref_l - ref_w) * c)),
-                       [](double x, double y) { return x + y; });
-    }
-    const uint32_t wn = wave_reduce(nan_or, [](uint32_t x, uint32_t y) { return x | y; });
+    if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
     if (lane == 0) {
       fs.wave_m[wid] = wm;
       fs.wave_z[wid] = wz;
-      fs.wave_nan[wid] = wn;
       fs.wave_stash[wid] = wcnt;
     }
   }
-  lds_barrier();
-  float m = -__builtin_inff();
-  uint32_t nan_any = 0, over = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
-    nan_any |= fs.wave_nan[w];
-    over |= fs.wave_stash[w] > (uint32_t)kStashPerWave;
-  }
-  double Z = 0.0;
-  if constexpr (NEED_P) {
-    const float ref = max2(m, -3.4028234663852886e38f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float ref_w = max2(fs.wave_m[w], -3.4028234663852886e38f);
-      Z += fs.wave_z[w] * (double)__builtin_amdgcn_exp2f((ref_w - ref) * c);
-    }
-    nan_any |= !(Z == Z);
-  }
-  if (nan_any || m == __builtin_inff()) {
-    finish_empty_row(a, b, slot, TSC_ROW_NONFINITE);
-    return true;
-  }
-  if (m == -__builtin_inff()) {
-    finish_empty_row(a, b, slot, TSC_ROW_NO_SUPPORT);
-    return true;
-  }
-  // Capacities: every wave's stash, and the key span the histogram covers. Keys of candidates
-  // run from theta_key to kmax; d = kmax - key is the distance from the maximum.
-  const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
-  const uint32_t dspan = kmax - theta_key;
-  if (over || dspan >= (uint32_t)kDBins) return false;
-
-  // ---- 3b. Expand the stash into id-ordered candidate words and histogram them --------------
-  // Word: bf16 bits << 16 | offset of the token in the segment (< 2^14). Histogram bin: d.
+  // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14).
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
+  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
   uint32_t ncand = 0;  // wave-uniform
-  for (uint32_t base = 0; base < wcnt; base += kWaveSize) {
+  const uint32_t nstash = wcnt < (uint32_t)kStashPerWave ? wcnt : (uint32_t)kStashPerWave;
+  for (uint32_t base = 0; base < nstash; base += kWaveSize) {
     const uint32_t i = base + lane;
-    const bool ok = i < wcnt;
+    const bool ok = i < nstash;
     const uint4 q = ok ? stash[i] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
     const uint32_t off = ok ? stash_ch[i] * 8u : 0u;
     const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
@@ -450,111 +549,69 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     ncand += total;
   }
   const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
-  auto d_of = [&](uint32_t word) { return kmax - key_of<E>(word >> 16); };
-  // Count histogram, and the race noise of every candidate (computed here, while the block
-  // waits for its slowest wave, rather than after the threshold).
-  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
-  const uint64_t seed = a.seeds[b], pos = a.positions[b];
   for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
     const uint32_t wd = cand[i];
-    atomicAdd(&hcnt[d_of(wd)], 1u);
+    const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+    if (bi < (uint32_t)kDBins) atomicAdd(&hcnt[bi], 1u);  // wider spans fall back (span test)
     const uint32_t id = id0 + (wd & 0x3FFFu);
     noise[i] = race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
   }
   if (lane == 0) fs.wave_cand[wid] = ncand;
   lds_barrier();
-  uint32_t ntot = 0;
-  over = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    ntot += fs.wave_cand[w];
-    over |= fs.wave_cand[w] > (uint32_t)kCandPerWave;
-  }
-  // theta is a lower bound of the k-th largest value iff at least k candidates exist.
-  if (over || ntot < (uint32_t)k) return false;
 
-  // ---- 4. Joint threshold over the bins d = 0..dspan (thread d owns bin d) ------------------
-  // Every member of a bin has the same weight, so a bin's mass is its count times that weight;
-  // min-p drops whole bins (it is a per-value predicate, monotone in d).
-  const bool need_m = mp > 0.0f;
-  const double tln_mp = need_m ? (double)T * log((double)mp) : 0.0;
-  auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
-  uint32_t bc = 0;
-  uint64_t bm = 0;
-  if (tid <= dspan) {
-    const float x = value_of_d(tid);
-    // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
-    if (!need_m || ((double)x - (double)m) >= tln_mp) {
-      bc = hcnt[tid];
-      const float w = __builtin_amdgcn_exp2f((x - m) * c);
-      bm = (uint64_t)bc * (uint64_t)((double)w * 0x1p48);
+  // ---- 4. Status and the joint threshold (wave 0; the others wait at the next barrier) --------
+  const bool capture = slot >= 0;
+  if (wid == 0) {
+    const uint32_t w = lane & (kWaves - 1);
+    const bool first16 = lane < (uint32_t)kWaves;
+    const float m = wave_reduce(fs.wave_m[w], MaximumF32());
+    const uint32_t ntot = wave_reduce(first16 ? fs.wave_cand[w] : 0u, SumU32());
+    const uint32_t over = wave_reduce((uint32_t)(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
+                                                 fs.wave_cand[w] > (uint32_t)kCandPerWave),
+                                      OrU32());
+    int32_t decision = kProceed;
+    if (!(m == m) || m == __builtin_inff()) {
+      decision = kNonfinite;
+    } else if (m == -__builtin_inff()) {
+      decision = kNoSupport;
+    } else {
+      const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
+      double Z = 0.0;
+      if constexpr (NEED_P) {
+        // Z relative to the maximum: exp2(x c - m c) = exp2(x c - R c) * exp2(R c - m c), with
+        // the rounded R c of the stream, so that its rounding cancels.
+        const double zr = wave_reduce(first16 ? fs.wave_z[w] : 0.0, SumF64());
+        Z = zr * exp2(-(double)nrc - (double)m * (double)c);
+        if (!(zr <= 1.0e300)) decision = kFallback;  // a float32 lane sum overflowed
+      }
+      // theta is a lower bound of the k-th largest value iff at least k candidates exist.
+      if (over || ntot < (uint32_t)k || kmax < theta_key || kmax - theta_key >= (uint32_t)kDBins)
+        decision = kFallback;
+      if (decision == kProceed)
+        bin_scan_wave0<NEED_P>(kmax, kmax - theta_key, m, T, c, k, p, mp, Z, capture, hcnt, lds,
+                               fs);
     }
-  }
-  uint32_t ex_c, ex_g;
-  uint64_t ex_m;
-  {
-    const uint32_t ic = wave_incl_scan(bc, SumU32(), 0u);
-    const uint32_t ig = wave_incl_scan((uint32_t)(bc > 0u), SumU32(), 0u);
-    const uint64_t im = wave_incl_scan(bm, SumU64(), (uint64_t)0);
-    if (lane == kWaveSize - 1) {
-      fs.scan_c[wid] = ic;
-      fs.scan_g[wid] = ig;
-      fs.scan_m[wid] = im;
-    }
-    lds_barrier();
-    uint32_t pc = 0, pg = 0;
-    uint64_t pm = 0;
-    for (uint32_t w = 0; w < wid; ++w) {
-      pc += fs.scan_c[w];
-      pg += fs.scan_g[w];
-      pm += fs.scan_m[w];
-    }
-    ex_c = pc + ic - bc;
-    ex_g = pg + ig - (bc > 0u);
-    ex_m = pm + im - bm;
-  }
-  uint32_t* excl_cnt = reinterpret_cast<uint32_t*>(lds + kOffExclCnt);
-  uint16_t* group = reinterpret_cast<uint16_t*>(lds + kOffGroup);
-  excl_cnt[tid] = ex_c;
-  group[tid] = (uint16_t)ex_g;
-  // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
-  // strictly above <= top_p * Z.
-  const bool qual = bc > 0u && ex_c < (uint32_t)k && (!NEED_P || (double)ex_m * 0x1p-48 <= (double)p * Z);
-  {
-    // Each wave's largest qualifying bin publishes its prefix results; one exchange.
-    const int32_t wd = wave_reduce(qual ? (int32_t)tid : -1, MaxI32());
-    if (lane == 0) fs.dstar_w[wid] = wd;
-    if (qual && (int32_t)tid == wd) {
-      fs.L_w[wid] = ex_c + bc;
-      fs.G_w[wid] = ex_g + 1u;
-      fs.zs_w[wid] = ex_m + bm;
-    }
+    if (decision != kProceed && lane == 0) fs.decision = decision;
   }
   lds_barrier();
-  int32_t dstar = -1;
-  uint32_t dwave = 0;
+  const int32_t decision = fs.decision;
+  if (decision == kNonfinite || decision == kNoSupport) {
+    finish_empty_row(a, b, slot, decision == kNonfinite ? TSC_ROW_NONFINITE : TSC_ROW_NO_SUPPORT);
+    return true;
+  }
+  if (decision != kProceed) return false;
+  float m = -__builtin_inff();
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (fs.dstar_w[w] > dstar) {
-      dstar = fs.dstar_w[w];
-      dwave = w;
-    }
-  }
-  const bool capture = slot >= 0;
-  const bool in_support = (int32_t)tid <= dstar && bc > 0u;  // this thread's bin is a support group
-  const uint32_t L = fs.L_w[dwave], G = fs.G_w[dwave];
-  const double lnzs = log((double)fs.zs_w[dwave]) - kFixShift * 0.6931471805599453;
-  if (capture && G > (uint32_t)kMaxGroups) return false;  // capture too spread for the tables
-  // Group tables for the capture: base position and logprob of every support group.
-  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
-  float* lp_tab = reinterpret_cast<float*>(lds + kOffLpTab);
-  if (capture && in_support) {
-    grp_base[ex_g] = ex_c;
-    lp_tab[ex_g] = logprob_of(value_of_d(tid), m, T, lnzs);
-  }
+  for (int w = 0; w < kWaves; ++w) m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
+  const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
+  const int32_t dstar = fs.dstar;
+  const uint32_t L = fs.L, G = fs.G;
+  auto d_of = [&](uint32_t word) { return kmax - key_of<E>(word >> 16); };
+  auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
 
   // ---- 5a. Race over the survivors (and per-wave group member counts) ------------------------
   // A candidate survives iff d <= d* (bins failing min-p lie beyond d*).
+  const uint16_t* group_of_d = reinterpret_cast<const uint16_t*>(lds + kOffGroupOfD);
   uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(lds + kOffGrpCnt) + wid * kMaxGroups;
   if (capture) {
     for (uint32_t g = lane; g < (uint32_t)kMaxGroups; g += kWaveSize) grp_cnt[g] = 0u;
@@ -577,7 +634,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       } else if (sc > b2) {
         b2 = sc;
       }
-      if (capture) atomicAdd(&grp_cnt[group[d]], 1u);
+      if (capture) atomicAdd(&grp_cnt[group_of_d[d]], 1u);
     } else {
       noise[i] = -__builtin_inff();
     }
@@ -661,6 +718,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // ---- 5b. Ordered capture -----------------------------------------------------------------
   // Wave w's cursor in group g: the group's base (members with larger keys) plus the group's
   // members in earlier segments (smaller ids). Each wave builds its own row of cursors.
+  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + kOffGrpBase);
+  const float* lp_tab = reinterpret_cast<const float*>(lds + kOffLpTab);
   uint32_t* cursor = reinterpret_cast<uint32_t*>(lds + kOffCursor) + wid * kMaxGroups;
   const uint32_t* all_cnt = reinterpret_cast<const uint32_t*>(lds + kOffGrpCnt);
   for (uint32_t g = lane; g < G; g += kWaveSize) {
@@ -678,7 +737,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (i < ncand) {
       wd = cand[i];
       live = noise[i] != -__builtin_inff();
-      if (live) g = group[d_of(wd)];
+      if (live) g = group_of_d[d_of(wd)];
     }
     // Members of my group among the lanes of this chunk: intersect, over the 8 bits of g, the
     // ballot of lanes whose bit matches mine.
@@ -700,7 +759,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   if (tid == 0) {
     a.lengths[slot] = (int32_t)(L < W ? L : W);
-    a.selected_logprob[slot] = lp_tab[group[token_d]];
+    a.selected_logprob[slot] = lp_tab[group_of_d[token_d]];
   }
   return true;
 }
@@ -717,12 +776,14 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     const int32_t k = a.top_k[b];
     const float p = a.top_p[b];
     const float mp = a.min_p[b];
+    const uint64_t seed = a.seeds[b], pos = a.positions[b];
     const bool eligible = row_params_valid(T, p, mp) && T > 0.0f && k >= 1 && k <= kFastMaxK &&
                           a.V >= kFastMinV && a.V <= kFastMaxV && (a.V & 7) == 0 &&
                           (a.ld & 7) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
     if (eligible) {
-      const bool done = p < 1.0f ? fast_row_bf16<true>(a, b, slot, T, k, p, mp, lds, fs)
-                                 : fast_row_bf16<false>(a, b, slot, T, k, p, mp, lds, fs);
+      const bool done =
+          p < 1.0f ? fast_row_bf16<true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                   : fast_row_bf16<false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }
