@@ -50,14 +50,16 @@ constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16
 constexpr int kOffNoise = kOffCand + kWaves * kCandPerWave * 4;       // f32 [16][512] race noise
 constexpr int kOffCnt = kOffNoise + kWaves * kCandPerWave * 4;        // u32 [1024] by key - theta
 constexpr int kFastLdsEnd = kOffCnt + kDBins * 4;
-// Overlays of the stash region, written once every wave has expanded its stash:
-constexpr int kOffGroupOfD = 0;                                   // u16 [1024] tie group of bin d
-constexpr int kOffGrpCnt = kOffGroupOfD + kDBins * 2;             // u32 [16][256] members per wave
-constexpr int kOffCursor = kOffGrpCnt + kWaves * kMaxGroups * 4;  // u32 [16][256] write cursors
-constexpr int kOffGrpBase = kOffCursor + kWaves * kMaxGroups * 4; // u32 [256]
-constexpr int kOffLpTab = kOffGrpBase + kMaxGroups * 4;           // f32 [256]
-constexpr int kOffOverlayEnd = kOffLpTab + kMaxGroups * 4;
-static_assert(kOffOverlayEnd <= kOffStashCh, "overlays must fit in the stash region");
+// Reuse of a wave's stash slice (4 KB) once the wave has expanded it: the wave's count per bin
+// bi = key - theta_key as u16 pairs (2 KB; later the exclusive prefix over earlier waves), then
+// each candidate's rank among the wave's earlier candidates of its bin (u16 [512], 1 KB).
+constexpr int kOffBinCnt = kOffStash;
+static_assert(kDBins * 2 + kCandPerWave * 2 <= kStashPerWave * 16, "bin counts and ranks fit");
+// Reuse of the stash-chunk region once every wave has expanded (after the combine barrier):
+constexpr int kOffGroupOfBin = kOffStashCh;                           // u16 [1024] group by bin
+constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;              // u32 [256]
+constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;                // f64 [256] (x - m) / T
+static_assert(kOffGrpS + kMaxGroups * 8 <= kOffCand, "tables must fit in the chunk region");
 
 constexpr size_t kFastDynLds =
     (size_t)kGeneralDynLds + sizeof(GeneralShared) > (size_t)kFastLdsEnd
@@ -81,13 +83,14 @@ struct FastShared {
   uint32_t wave_cand[kWaves];
   int32_t decision;
   int32_t dstar;
-  uint32_t L, G;
+  uint32_t L;
+  double lnzs;
   float race_b1[kWaves], race_b2[kWaves];
   int32_t race_id[kWaves];
-  uint32_t race_d[kWaves];
+  float race_x[kWaves];
   double ref_top[kWaves];
   int32_t ref_id[kWaves];
-  uint32_t ref_d[kWaves];
+  float ref_x[kWaves];
 };
 
 __device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -202,10 +205,35 @@ __device__ inline int64_t slot_step3(const FastShared& fs) {
   return slot;
 }
 
-// Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d;
-// hcnt is indexed by key - theta_key = dspan - d. Lane l owns the nb consecutive bins from l * nb.
-// Publishes the threshold d*, the support size and group count, and for capture rows fills the
-// tie-group tables (group of each bin, base position and logprob of each group).
+// ln(v) for a positive finite double with an absolute error of about 3e-7: the binary exponent
+// exactly, the mantissa's logarithm with the hardware log2 in float32.
+__device__ inline double ln_fast(double v) {
+  int e;
+  const double mant = __builtin_frexp(v, &e);  // [0.5, 1)
+  return ((double)e + (double)__builtin_amdgcn_logf((float)mant)) * 0.6931471805599453;
+}
+// 2^a for a double argument with a relative error of about 2e-7 (float32 hardware exp2 on the
+// fractional part, the integer part exactly).
+__device__ inline double exp2_fast(double a) {
+  const double n = __builtin_floor(a);
+  return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
+}
+
+// Reduction over the first 16 lanes, for data that every row of 16 lanes holds alike (lane l
+// holding entry l % 16): four DPP steps inside each row, then lane 0.
+template <class T, class Op>
+__device__ inline T row16_reduce(T v, Op op) {
+  v = op(v, dpp_mov<dpp::kQuadSwap1>(v, v));
+  v = op(v, dpp_mov<dpp::kQuadSwap2>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor4>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor8>(v, v));
+  return read_lane(v, 0);
+}
+
+// Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d; they
+// were counted by bi = key - theta_key = dspan - d. Lane l owns the nb consecutive bins from
+// l * nb. Publishes the threshold d*, the support size, and for capture rows the tie-group tables:
+// the group of each support bin, each group's base position and (x - m) / T, and ln Z_S.
 template <bool NEED_P>
 __device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
@@ -214,91 +242,95 @@ __device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, fl
   const uint32_t lane = lane_id();
   const uint32_t nb = (dspan + kWaveSize) / kWaveSize;  // 1..16
   const bool need_m = mp > 0.0f;
-  const double tln_mp = need_m ? (double)T * log((double)mp) : 0.0;
+  // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
+  const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
   auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
-  // Count and fixed-point mass of bin d after min-p (a per-value predicate, monotone in d).
-  auto bin = [&](uint32_t d, uint32_t& bc, uint64_t& bm) {
-    bc = 0;
-    bm = 0;
+  // Count and mass of bin d after min-p (a per-value predicate, monotone in d). The count is
+  // packed with the group indicator as count << 11 | present (at most 8192 candidates and 1024
+  // bins), so that one integer scan gives both positions and group indices.
+  auto bin = [&](uint32_t d, uint32_t& packed, double& bm) {
+    packed = 0;
+    bm = 0.0;
     if (d <= dspan) {
       const float x = value_of_d(d);
-      // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
       if (!need_m || ((double)x - (double)m) >= tln_mp) {
-        bc = hcnt[dspan - d];
-        const float w = __builtin_amdgcn_exp2f((x - m) * c);
-        bm = (uint64_t)bc * (uint64_t)((double)w * 0x1p48);
+        const uint32_t bc = hcnt[dspan - d];
+        packed = (bc << 11) | (uint32_t)(bc > 0u);
+        if constexpr (NEED_P) bm = (double)bc * (double)__builtin_amdgcn_exp2f((x - m) * c);
+        else if (capture) bm = (double)bc * (double)__builtin_amdgcn_exp2f((x - m) * c);
       }
     }
   };
-  uint32_t lc = 0, lg = 0;
-  uint64_t lmass = 0;
+  uint32_t lp_ = 0;
+  double lmass = 0.0;
   for (uint32_t t = 0; t < nb; ++t) {
-    uint32_t bc;
-    uint64_t bm;
-    bin(lane * nb + t, bc, bm);
-    lc += bc;
-    lg += bc > 0u;
+    uint32_t pk;
+    double bm;
+    bin(lane * nb + t, pk, bm);
+    lp_ += pk;
     lmass += bm;
   }
-  uint32_t tc, tg;
-  uint64_t tm;
-  uint32_t ec = wave_excl_scan(lc, SumU32(), tc);
-  uint32_t eg = wave_excl_scan(lg, SumU32(), tg);
-  uint64_t em = wave_excl_scan(lmass, SumU64(), tm);
+  uint32_t tp;
+  double tm;
+  uint32_t ep = wave_excl_scan(lp_, SumU32(), tp);
+  double em = wave_excl_scan(lmass, SumF64(), tm);
   const double pz = (double)p * Z;
   // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
   // strictly above <= top_p * Z. Each predicate is monotone in d, so this is the last qualifying
   // bin of the last lane that has one.
   int32_t best = -1;
-  uint32_t bL = 0, bG = 0;
-  uint64_t bZ = 0;
-  uint16_t* group_of_d = reinterpret_cast<uint16_t*>(lds + kOffGroupOfD);
+  uint32_t bL = 0;
+  double bZ = 0.0;
+  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + kOffGroupOfBin);
   uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
+  double* grp_s = reinterpret_cast<double*>(lds + kOffGrpS);
+  const double invT = 1.0 / (double)T;
   for (uint32_t t = 0; t < nb; ++t) {
     const uint32_t d = lane * nb + t;
-    uint32_t bc;
-    uint64_t bm;
-    bin(d, bc, bm);
-    if (bc > 0u) {
-      const bool qual = ec < (uint32_t)k && (!NEED_P || (double)em * 0x1p-48 <= pz);
+    uint32_t pk;
+    double bm;
+    bin(d, pk, bm);
+    if (pk & 1u) {
+      const uint32_t ec = ep >> 11, eg = ep & 0x7FFu;
+      const bool qual = ec < (uint32_t)k && (!NEED_P || em <= pz);
       if (qual) {
         best = (int32_t)d;
-        bL = ec + bc;
-        bG = eg + 1u;
+        bL = ec + (pk >> 11);
         bZ = em + bm;
-      }
-      if (capture && eg < (uint32_t)kMaxGroups) {
-        group_of_d[d] = (uint16_t)eg;
-        grp_base[eg] = ec;
+        if (capture && eg < (uint32_t)kMaxGroups) {
+          group_of_bin[dspan - d] = (uint16_t)eg;
+          grp_base[eg] = ec;
+          grp_s[eg] = ((double)value_of_d(d) - (double)m) * invT;
+        }
       }
     }
-    ec += bc;
-    eg += bc > 0u;
+    ep += pk;
     em += bm;
   }
   // d* >= 0 always: bin 0 holds the maximum, which passes every predicate.
   const int32_t dstar = wave_reduce(best, MaxI32());
   const int owner = (int)((uint32_t)dstar / nb);
-  const uint32_t L = read_lane(bL, owner), G = read_lane(bG, owner);
-  const uint64_t zs = read_lane(bZ, owner);
-  int32_t decision = kProceed;
-  if (capture && G > (uint32_t)kMaxGroups) decision = kFallback;  // too spread for the tables
-  if (capture && decision == kProceed) {
-    const double lnzs = log((double)zs) - kFixShift * 0.6931471805599453;
-    float* lp_tab = reinterpret_cast<float*>(lds + kOffLpTab);
-    for (uint32_t t = 0; t < nb; ++t) {
-      const uint32_t d = lane * nb + t;
-      if ((int32_t)d <= dstar && hcnt[dspan - d] > 0u)
-        lp_tab[group_of_d[d]] = logprob_of(value_of_d(d), m, T, lnzs);
-    }
-  }
+  const uint32_t L = read_lane(bL, owner);
+  const double zs = read_lane(bZ, owner);
+  // Groups in the support: present bins up to d*.
+  const uint32_t G = wave_reduce(
+      [&] {
+        uint32_t g = 0;
+        for (uint32_t t = 0; t < nb; ++t) {
+          const uint32_t d = lane * nb + t;
+          g += (int32_t)d <= dstar && d <= dspan && hcnt[dspan - d] > 0u;
+        }
+        return g;
+      }(),
+      SumU32());
   if (lane == 0) {
-    fs.decision = decision;
+    fs.decision = (capture && G > (uint32_t)kMaxGroups) ? kFallback : kProceed;
     fs.dstar = dstar;
     fs.L = L;
-    fs.G = G;
+    fs.lnzs = ln_fast(zs);  // logprob = (x - m) / T - ln Z_S
   }
 }
+
 
 // Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
 // go through the general path instead; `slot` is then already set.
@@ -506,7 +538,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     stash_load(j, r[j], lm);
   }
 
-  // ---- 3. Per wave, as soon as its segment is done: partials, expansion, histogram, noise ------
+  // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts, ranks --------
   {
     const float wm = wave_reduce(m_l, MaximumF32());
     double wz = 0.0;
@@ -517,60 +549,88 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       fs.wave_stash[wid] = wcnt;
     }
   }
-  // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14).
+  // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
   float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
   uint32_t ncand = 0;  // wave-uniform
-  const uint32_t nstash = wcnt < (uint32_t)kStashPerWave ? wcnt : (uint32_t)kStashPerWave;
-  for (uint32_t base = 0; base < nstash; base += kWaveSize) {
-    const uint32_t i = base + lane;
-    const bool ok = i < nstash;
-    const uint4 q = ok ? stash[i] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-    const uint32_t off = ok ? stash_ch[i] * 8u : 0u;
-    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-    uint32_t words[8];
-    uint32_t is = 0, n = 0;
+  {
+    const uint32_t nstash = wcnt < (uint32_t)kStashPerWave ? wcnt : (uint32_t)kStashPerWave;
+    // theta is finite whenever the row can be served here; clamping it keeps -inf out.
+    const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
+    // Elements that are not candidates are written to a dummy slot of this lane (in the noise
+    // array, which is filled later), which keeps the scatter free of branches.
+    uint32_t* dummy = reinterpret_cast<uint32_t*>(noise) + lane;
+    for (uint32_t base = 0; base < nstash; base += kWaveSize) {
+      const uint32_t i = base + lane;
+      const bool ok = i < nstash;
+      const uint4 q = ok ? stash[i] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+      const uint32_t off = ok ? stash_ch[i] * 8u : 0u;
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+      uint32_t words[8];
+      bool isc[8];
+      uint32_t n = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
-      const float x = __uint_as_float(hi);
-      const bool c_e = x >= theta && x > -__builtin_inff();  // -0 ties +0; -inf and NaN fail
-      words[e] = hi | (off + e);
-      is |= (uint32_t)c_e << e;
-      n += c_e;
-    }
-    uint32_t total;
-    uint32_t at = ncand + wave_excl_sum(n, total);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if ((is >> e) & 1u) {
-        if (at < (uint32_t)kCandPerWave) cand[at] = words[e];
-        ++at;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+        isc[e] = __uint_as_float(hi) >= th;  // -0 ties +0; NaN fails
+        words[e] = hi | (off + (uint32_t)e);
+        n += isc[e];
       }
+      uint32_t total;
+      uint32_t at = ncand + wave_excl_sum(n, total);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t* dst = (isc[e] && at < (uint32_t)kCandPerWave) ? cand + at : dummy;
+        *dst = words[e];
+        at += isc[e];
+      }
+      ncand += total;
     }
-    ncand += total;
   }
+  // The stash slice of this wave is free now. It holds the wave's count per bin
+  // bi = key - theta_key (u16 pairs; later the exclusive prefix over earlier waves, the capture
+  // offsets) and each candidate's rank among the wave's earlier candidates of its bin.
+  uint32_t* bincnt = reinterpret_cast<uint32_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16);
+  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16 +
+                                                kDBins * 2);
+  for (uint32_t i = lane; i < (uint32_t)kDBins / 8; i += kWaveSize)
+    reinterpret_cast<uint4*>(bincnt)[i] = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
-  for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
-    const uint32_t wd = cand[i];
+  for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
+    const uint32_t i = base + lane;
+    const uint32_t wd = i < nc_here ? cand[i] : 0u;
     const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-    if (bi < (uint32_t)kDBins) atomicAdd(&hcnt[bi], 1u);  // wider spans fall back (span test)
-    const uint32_t id = id0 + (wd & 0x3FFFu);
-    noise[i] = race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
+    const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
+    // Lanes of this chunk with my bin: intersect, over the 10 bits of bi, the ballot of lanes
+    // whose bit matches mine. The bin's first lane adds the bin's count once.
+    uint64_t same = __ballot(in);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
+      same &= ((bi >> bit) & 1u) ? ones : ~ones;
+    }
+    const uint32_t first = (uint32_t)__builtin_ctzll(same | (1ull << 63));
+    uint32_t before = 0;
+    if (in && lane == first) {
+      const uint32_t cnt = (uint32_t)__popcll(same);
+      atomicAdd(&hcnt[bi], cnt);
+      const uint32_t sh = (bi & 1u) * 16u;
+      before = (atomicAdd(&bincnt[bi >> 1], cnt << sh) >> sh) & 0xFFFFu;
+    }
+    before = (uint32_t)__shfl((int)before, (int)first, kWaveSize);
+    if (in) rankw[i] = (uint16_t)(before + mbcnt(same));
   }
   if (lane == 0) fs.wave_cand[wid] = ncand;
   lds_barrier();
 
-  // ---- 4. Status and the joint threshold (wave 0; the others wait at the next barrier) --------
+  // ---- 4. Wave 0: status and the joint threshold. Waves 1-15: capture offsets, race noise -----
   const bool capture = slot >= 0;
   if (wid == 0) {
     const uint32_t w = lane & (kWaves - 1);
-    const bool first16 = lane < (uint32_t)kWaves;
-    const float m = wave_reduce(fs.wave_m[w], MaximumF32());
-    const uint32_t ntot = wave_reduce(first16 ? fs.wave_cand[w] : 0u, SumU32());
-    const uint32_t over = wave_reduce((uint32_t)(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
-                                                 fs.wave_cand[w] > (uint32_t)kCandPerWave),
-                                      OrU32());
+    const float m = row16_reduce(fs.wave_m[w], MaximumF32());
+    const uint32_t ntot = row16_reduce(fs.wave_cand[w], SumU32());
+    const bool over = __ballot(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
+                               fs.wave_cand[w] > (uint32_t)kCandPerWave) != 0;
     int32_t decision = kProceed;
     if (!(m == m) || m == __builtin_inff()) {
       decision = kNonfinite;
@@ -582,8 +642,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if constexpr (NEED_P) {
         // Z relative to the maximum: exp2(x c - m c) = exp2(x c - R c) * exp2(R c - m c), with
         // the rounded R c of the stream, so that its rounding cancels.
-        const double zr = wave_reduce(first16 ? fs.wave_z[w] : 0.0, SumF64());
-        Z = zr * exp2(-(double)nrc - (double)m * (double)c);
+        const double zr = row16_reduce(fs.wave_z[w], SumF64());
+        Z = zr * exp2_fast(-(double)nrc - (double)m * (double)c);
         if (!(zr <= 1.0e300)) decision = kFallback;  // a float32 lane sum overflowed
       }
       // theta is a lower bound of the k-th largest value iff at least k candidates exist.
@@ -594,6 +654,44 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
                                fs);
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
+  } else {
+    const uint32_t h = wid - 1;  // helper index 0..14
+    if (capture) {
+      // Exclusive prefix of every bin's count over the waves (u16 pairs, added as u32: totals
+      // stay below 2^16): wave w's first capture offset in each tie group.
+      const uint32_t* cnt0 = reinterpret_cast<const uint32_t*>(lds + kOffBinCnt);
+      for (uint32_t j = tid - kWaveSize; j < (uint32_t)kDBins / 2; j += kThreads - kWaveSize) {
+        uint32_t v[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * (kStashPerWave * 4) + j];
+        uint32_t acc = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const_cast<uint32_t*>(cnt0)[w * (kStashPerWave * 4) + j] = acc;
+          acc += v[w];
+        }
+      }
+    }
+    // Race noise of every candidate of every wave, 64 at a time, spread over the 15 helpers.
+    const uint32_t l16 = lane & (kWaves - 1);
+    const uint32_t nw = fs.wave_cand[l16];
+    const uint32_t nchunks = ((nw < (uint32_t)kCandPerWave ? nw : (uint32_t)kCandPerWave) +
+                              kWaveSize - 1) / kWaveSize;
+    const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? nchunks : 0u, SumU32(), 0u);
+    const uint32_t jobs = read_lane(incl, kWaves - 1);
+    const uint32_t cwv = cw;
+    for (uint32_t q = h; q < jobs; q += kWaves - 1) {
+      const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
+      const uint32_t c0 = read_lane(incl - nchunks, (int)ww);
+      const uint32_t nww = read_lane(nw, (int)ww);
+      const uint32_t i = (q - c0) * kWaveSize + lane;
+      if (i < nww && i < (uint32_t)kCandPerWave) {
+        const uint32_t wd = reinterpret_cast<const uint32_t*>(lds + kOffCand)[ww * kCandPerWave + i];
+        const uint32_t id = ww * cwv * 8u + (wd & 0x3FFFu);
+        reinterpret_cast<float*>(lds + kOffNoise)[ww * kCandPerWave + i] =
+            race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
+      }
+    }
   }
   lds_barrier();
   const int32_t decision = fs.decision;
@@ -607,38 +705,48 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   for (int w = 0; w < kWaves; ++w) m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
   const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
   const int32_t dstar = fs.dstar;
-  const uint32_t L = fs.L, G = fs.G;
-  auto d_of = [&](uint32_t word) { return kmax - key_of<E>(word >> 16); };
-  auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
+  const uint32_t L = fs.L;
+  const double lnzs = fs.lnzs;
+  // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
+  // value >= x_cut (-0 and +0 compare equal, as their keys do).
+  const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
 
-  // ---- 5a. Race over the survivors (and per-wave group member counts) ------------------------
-  // A candidate survives iff d <= d* (bins failing min-p lie beyond d*).
-  const uint16_t* group_of_d = reinterpret_cast<const uint16_t*>(lds + kOffGroupOfD);
-  uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(lds + kOffGrpCnt) + wid * kMaxGroups;
-  if (capture) {
-    for (uint32_t g = lane; g < (uint32_t)kMaxGroups; g += kWaveSize) grp_cnt[g] = 0u;
-  }
+  // ---- 5. Race over the survivors and, for opt-in rows, their ordered capture ----------------
+  // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
+  // members in earlier segments (smaller ids) + its rank among this wave's members.
+  const uint16_t* group_of_bin = reinterpret_cast<const uint16_t*>(lds + kOffGroupOfBin);
+  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + kOffGrpBase);
+  const double* grp_s = reinterpret_cast<const double*>(lds + kOffGrpS);
+  const uint32_t W = (uint32_t)a.W;
+  int32_t* out_ids = capture ? a.packed_ids + slot * a.W : nullptr;
+  float* out_lp = (capture && a.logprobs) ? a.logprobs + slot * a.W : nullptr;
   const float invT = 1.0f / T;
   float b1 = -__builtin_inff(), b2 = -__builtin_inff();  // lane's best two float32 scores
   int32_t b1_id = 0x7FFFFFFF;
-  uint32_t b1_d = 0;
+  float b1_x = 0.0f;
   for (uint32_t i = lane; i < ncand; i += kWaveSize) {
     const uint32_t wd = cand[i];
-    const uint32_t d = d_of(wd);
-    if ((int32_t)d <= dstar) {
-      const uint32_t id = id0 + (wd & 0x3FFFu);
-      const float sc = (value_of_d(d) - m) * invT + noise[i];
-      if (sc > b1) {
-        b2 = b1;
-        b1 = sc;
-        b1_id = (int32_t)id;
-        b1_d = d;
-      } else if (sc > b2) {
-        b2 = sc;
+    const float x = __uint_as_float(wd & 0xFFFF0000u);
+    if (!(x >= x_cut)) continue;
+    const uint32_t id = id0 + (wd & 0x3FFFu);
+    const float sc = (x - m) * invT + noise[i];
+    if (sc > b1) {
+      b2 = b1;
+      b1 = sc;
+      b1_id = (int32_t)id;
+      b1_x = x;
+    } else if (sc > b2) {
+      b2 = sc;
+    }
+    if (capture) {
+      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+      const uint32_t g = group_of_bin[bi];
+      const uint32_t pre = (bincnt[bi >> 1] >> ((bi & 1u) * 16u)) & 0xFFFFu;
+      const uint32_t at = grp_base[g] + pre + rankw[i];
+      if (at < W) {
+        out_ids[at] = (int32_t)id;
+        if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
       }
-      if (capture) atomicAdd(&grp_cnt[group_of_d[d]], 1u);
-    } else {
-      noise[i] = -__builtin_inff();
     }
   }
   {
@@ -651,42 +759,40 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       fs.race_b1[wid] = wb1;
       fs.race_b2[wid] = wb2;
       fs.race_id[wid] = b1_id;
-      fs.race_d[wid] = b1_d;
+      fs.race_x[wid] = b1_x;
     }
   }
   lds_barrier();
-  float t1 = -__builtin_inff(), t2 = -__builtin_inff();
-  int32_t token = 0x7FFFFFFF;
-  uint32_t token_d = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  // Winner over the waves, lane-parallel: lane l looks at wave l % 16.
+  int32_t token;
+  float token_x;
+  float t1, t2;
+  {
+    const uint32_t w = lane & (kWaves - 1);
     const float x1 = fs.race_b1[w], x2 = fs.race_b2[w];
-    if (x1 > t1) {
-      t2 = t1 > x2 ? t1 : x2;
-      t1 = x1;
-      token = fs.race_id[w];
-      token_d = fs.race_d[w];
-    } else {
-      t2 = t2 > x1 ? t2 : x1;
-    }
+    t1 = row16_reduce(x1, [](float x, float y) { return x > y ? x : y; });
+    const uint32_t win = (uint32_t)__builtin_ctzll(__ballot(x1 == t1));  // the first such wave
+    t2 = row16_reduce(w == win ? x2 : x1, [](float x, float y) { return x > y ? x : y; });
+    token = fs.race_id[win];
+    token_x = fs.race_x[win];
   }
   if (!(t1 - t2 > kRaceMargin)) {
-    // Near tie in float32: rescore every candidate within the margin in float64, ties -> lowest id.
+    // Near tie in float32: rescore every survivor within the margin in float64, ties -> lowest id.
     double bs = -__builtin_inf();
     int32_t bid = 0x7FFFFFFF;
-    uint32_t bd = 0;
+    float bx = 0.0f;
     for (uint32_t i = lane; i < ncand; i += kWaveSize) {
-      if (noise[i] == -__builtin_inff()) continue;
       const uint32_t wd = cand[i];
-      const uint32_t d = d_of(wd);
-      if ((value_of_d(d) - m) * invT + noise[i] < t1 - kRaceMargin) continue;
+      const float x = __uint_as_float(wd & 0xFFFF0000u);
+      if (!(x >= x_cut)) continue;
+      if ((x - m) * invT + noise[i] < t1 - kRaceMargin) continue;
       const int32_t id = (int32_t)(id0 + (wd & 0x3FFFu));
-      const double sv = ((double)value_of_d(d) - (double)m) / (double)T;
+      const double sv = ((double)x - (double)m) / (double)T;
       const double sc = sv - log(-log(race_uniform((uint32_t)id, seed, pos)));
       if (sc > bs || (sc == bs && id < bid)) {
         bs = sc;
         bid = id;
-        bd = d;
+        bx = x;
       }
     }
     const double wt = wave_reduce(bs, [](double x, double y) { return x > y ? x : y; });
@@ -695,7 +801,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (bs == wt && bid == wi) {  // one lane, or every lane when the wave has no candidate
       fs.ref_top[wid] = wt;
       fs.ref_id[wid] = wi;
-      fs.ref_d[wid] = bd;
+      fs.ref_x[wid] = bx;
     }
     lds_barrier();
     double top = -__builtin_inf();
@@ -707,64 +813,22 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (t > top || (t == top && i < token)) {
         top = t;
         token = i;
-        token_d = fs.ref_d[w];
+        token_x = fs.ref_x[w];
       }
     }
   }
   if (tid == 0) {
     a.tokens[b] = token;
-    a.row_status[b] = (capture && L > (uint32_t)a.W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
-  }
-  if (!capture) return true;
-
-  // ---- 5b. Ordered capture -----------------------------------------------------------------
-  // Wave w's cursor in group g: the group's base (members with larger keys) plus the group's
-  // members in earlier segments (smaller ids). Each wave builds its own row of cursors.
-  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + kOffGrpBase);
-  const float* lp_tab = reinterpret_cast<const float*>(lds + kOffLpTab);
-  uint32_t* cursor = reinterpret_cast<uint32_t*>(lds + kOffCursor) + wid * kMaxGroups;
-  const uint32_t* all_cnt = reinterpret_cast<const uint32_t*>(lds + kOffGrpCnt);
-  for (uint32_t g = lane; g < G; g += kWaveSize) {
-    uint32_t acc = grp_base[g];
-    for (uint32_t w = 0; w < wid; ++w) acc += all_cnt[w * kMaxGroups + g];
-    cursor[g] = acc;
-  }
-  const uint32_t W = (uint32_t)a.W;
-  int32_t* out_ids = a.packed_ids + slot * a.W;
-  float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
-  for (uint32_t base = 0; base < ncand; base += kWaveSize) {
-    const uint32_t i = base + lane;
-    uint32_t wd = 0, g = 0;
-    bool live = false;
-    if (i < ncand) {
-      wd = cand[i];
-      live = noise[i] != -__builtin_inff();
-      if (live) g = group_of_d[d_of(wd)];
+    a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
+    if (capture) {
+      a.lengths[slot] = (int32_t)(L < W ? L : W);
+      const uint32_t tbi = key_of<E>(__float_as_uint(token_x) >> 16) - theta_key;
+      a.selected_logprob[slot] = (float)(grp_s[group_of_bin[tbi]] - lnzs);
     }
-    // Members of my group among the lanes of this chunk: intersect, over the 8 bits of g, the
-    // ballot of lanes whose bit matches mine.
-    uint64_t same = __ballot(live);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const uint64_t ones = __ballot(live && ((g >> bit) & 1u));
-      same &= ((g >> bit) & 1u) ? ones : ~ones;
-    }
-    if (live) {
-      const uint32_t rank = mbcnt(same);
-      const uint32_t at = cursor[g] + rank;
-      if (at < W) {
-        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
-        if (out_lp) out_lp[at] = lp_tab[g];
-      }
-      if (rank == 0) cursor[g] += (uint32_t)__popcll(same);  // the group's first lane advances it
-    }
-  }
-  if (tid == 0) {
-    a.lengths[slot] = (int32_t)(L < W ? L : W);
-    a.selected_logprob[slot] = lp_tab[group_of_d[token_d]];
   }
   return true;
 }
+
 
 template <int DT>
 __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
