@@ -390,9 +390,12 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
+  const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
   auto mask_tail = [&](int j) {
-    if ((uint32_t)(j + 1) * kWaveSize > nseg && (uint32_t)j * kWaveSize + lane >= nseg)
-      r[j] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    if ((uint32_t)j >= nfull) {  // wave-uniform: a scalar branch, no vector work on full loads
+      if ((uint32_t)j * kWaveSize + lane >= nseg)
+        r[j] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    }
   };
   auto unpack = [](const uint4& q, float (&f)[8]) {
     const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
@@ -422,23 +425,26 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   };
-  uint32_t wcnt = 0;  // wave's stashed loads (wave-uniform)
+  uint32_t wcnt = 0;   // wave's flagged loads (wave-uniform)
+  uint32_t wfill = 0;  // stash slots written: wcnt until a load no longer fits
   uint4* stash = reinterpret_cast<uint4*>(lds + kOffStash) + wid * kStashPerWave;
   uint32_t* stash_ch = reinterpret_cast<uint32_t*>(lds + kOffStashCh) + wid * kStashPerWave;
   float theta = __builtin_inff();
-  auto stash_load = [&](int j, const uint4& q, float lm) {
-    const bool flag = lm >= theta;
+  auto stash_load = [&](int j, const uint4& q, bool flag) {
     const uint64_t mask = __ballot(flag);
-    if (mask) {
+    const uint32_t n = (uint32_t)__popcll(mask);
+    // Capacity is checked per load for the whole wave (scalar), so the flagged lanes only
+    // compute their slot; a load that does not fit is dropped and the row falls back.
+    if (n != 0u && wcnt + n <= (uint32_t)kStashPerWave) {
       if (flag) {
-        const uint32_t at = wcnt + mbcnt(mask);
-        if (at < (uint32_t)kStashPerWave) {
-          stash[at] = q;
-          stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
-        }
+        const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, wcnt));
+        stash[at] = q;
+        stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
       }
-      wcnt += (uint32_t)__popcll(mask);
+      wfill = wcnt + n;
     }
+    wcnt += n;
   };
   // Keep each load's work at its own step: without this the compiler may sink the exp chain
   // (which only feeds the final sum) past the loop and keep every load's data alive.
@@ -523,28 +529,43 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t theta_key = uniform_u32(fs.theta_key);
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
-  stash_load(0, r[0], lm0);
-  stash_load(1, r[1], lm1);
-  stash_load(2, r[2], lm2);
+  stash_load(0, r[0], lm0 >= theta);
+  stash_load(1, r[1], lm1 >= theta);
+  stash_load(2, r[2], lm2 >= theta);
+  // From here on, for top_p < 1, a load is stashed when the sum of its weights reaches the
+  // weight of theta (any element >= theta implies it; the small slack covers exp2 rounding), so
+  // the load's maximum is not needed: the row maximum is the largest candidate, and a NaN logit
+  // shows up in the mass.
+  // (A theta weight below 2^-100 would flag every load: the stash overflows and the row falls
+  // back, which happens only for extreme spreads of the logits at low temperature.)
+  const float wth = 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc));
 #pragma unroll
   for (int j = 3; j < kFastLoads; ++j) {
     if (j + kLoadsAhead < kFastLoads) issue(j + kLoadsAhead);
     mask_tail(j);
     unpack(r[j], f);
-    const float lm = load_max(f);
-    m_l = maximum2f(m_l, lm);
-    add_mass(f);
+    bool flag;
+    if constexpr (NEED_P) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[i], c, nrc));
+      const float ls = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      if (j & 1) s_b += ls; else s_a += ls;
+      flag = ls >= wth;
+    } else {
+      const float lm = load_max(f);
+      m_l = maximum2f(m_l, lm);
+      flag = lm >= theta;
+    }
     pin();
-    stash_load(j, r[j], lm);
+    stash_load(j, r[j], flag);
   }
 
   // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts, ranks --------
   {
-    const float wm = wave_reduce(m_l, MaximumF32());
     double wz = 0.0;
     if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
     if (lane == 0) {
-      fs.wave_m[wid] = wm;
       fs.wave_z[wid] = wz;
       fs.wave_stash[wid] = wcnt;
     }
@@ -554,7 +575,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
   uint32_t ncand = 0;  // wave-uniform
   {
-    const uint32_t nstash = wcnt < (uint32_t)kStashPerWave ? wcnt : (uint32_t)kStashPerWave;
+    const uint32_t nstash = wfill;  // never slots that were not written in this row
     // theta is finite whenever the row can be served here; clamping it keeps -inf out.
     const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
     // Elements that are not candidates are written to a dummy slot of this lane (in the noise
@@ -596,9 +617,13 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   for (uint32_t i = lane; i < (uint32_t)kDBins / 8; i += kWaveSize)
     reinterpret_cast<uint4*>(bincnt)[i] = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
+  // Maximum: for top_p < 1 the largest candidate (the row maximum is >= theta, so it is one);
+  // otherwise the running maximum of the stream (which also carries NaN).
+  float xm = NEED_P ? -__builtin_inff() : m_l;
   for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
     const uint32_t i = base + lane;
-    const uint32_t wd = i < nc_here ? cand[i] : 0u;
+    const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
+    if constexpr (NEED_P) xm = maximum2f(xm, __uint_as_float(wd & 0xFFFF0000u));
     const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
     const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
     // Lanes of this chunk with my bin: intersect, over the 10 bits of bi, the ballot of lanes
@@ -620,6 +645,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     before = (uint32_t)__shfl((int)before, (int)first, kWaveSize);
     if (in) rankw[i] = (uint16_t)(before + mbcnt(same));
   }
+  {
+    const float wm = wave_reduce(xm, MaximumF32());
+    if (lane == 0) fs.wave_m[wid] = wm;
+  }
   if (lane == 0) fs.wave_cand[wid] = ncand;
   lds_barrier();
 
@@ -631,9 +660,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const uint32_t ntot = row16_reduce(fs.wave_cand[w], SumU32());
     const bool over = __ballot(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
                                fs.wave_cand[w] > (uint32_t)kCandPerWave) != 0;
+    // A NaN logit: in the running maximum when top_p = 1, in the mass when top_p < 1.
+    double zr = 0.0;
+    if constexpr (NEED_P) zr = row16_reduce(fs.wave_z[w], SumF64());
     int32_t decision = kProceed;
-    if (!(m == m) || m == __builtin_inff()) {
+    // With top_p < 1 the maximum comes from the candidates: trusted when it is +inf (a candidate
+    // exists), but only without overflow otherwise.
+    if (!(m == m) || m == __builtin_inff() || !(zr == zr)) {
       decision = kNonfinite;
+    } else if (NEED_P && over) {
+      decision = kFallback;
     } else if (m == -__builtin_inff()) {
       decision = kNoSupport;
     } else {
@@ -642,7 +678,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if constexpr (NEED_P) {
         // Z relative to the maximum: exp2(x c - m c) = exp2(x c - R c) * exp2(R c - m c), with
         // the rounded R c of the stream, so that its rounding cancels.
-        const double zr = row16_reduce(fs.wave_z[w], SumF64());
         Z = zr * exp2_fast(-(double)nrc - (double)m * (double)c);
         if (!(zr <= 1.0e300)) decision = kFallback;  // a float32 lane sum overflowed
       }
