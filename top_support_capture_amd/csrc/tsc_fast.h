@@ -49,17 +49,20 @@ constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16
 constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
 constexpr int kOffNoise = kOffCand + kWaves * kCandPerWave * 4;       // f32 [16][512] race noise
 constexpr int kOffCnt = kOffNoise + kWaves * kCandPerWave * 4;        // u32 [1024] by key - theta
-constexpr int kFastLdsEnd = kOffCnt + kDBins * 4;
-// Reuse of a wave's stash slice (4 KB) once the wave has expanded it: the wave's count per bin
-// bi = key - theta_key as u16 pairs (2 KB; later the exclusive prefix over earlier waves), then
-// each candidate's rank among the wave's earlier candidates of its bin (u16 [512], 1 KB).
-constexpr int kOffBinCnt = kOffStash;
-static_assert(kDBins * 2 + kCandPerWave * 2 <= kStashPerWave * 16, "bin counts and ranks fit");
-// Reuse of the stash-chunk region once every wave has expanded (after the combine barrier):
-constexpr int kOffGroupOfBin = kOffStashCh;                           // u16 [1024] group by bin
+constexpr int kOffGroupOfBin = kOffCnt + kDBins * 4;                // u16 [1024] group by bin
 constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;              // u32 [256]
 constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;                // f64 [256] (x - m) / T
-static_assert(kOffGrpS + kMaxGroups * 8 <= kOffCand, "tables must fit in the chunk region");
+constexpr int kFastLdsEnd = kOffGrpS + kMaxGroups * 8;
+// Reuse of a wave's stash slices once the wave has expanded them: its count per bin
+// bi = key - theta_key (u16; later the exclusive prefix over earlier waves), 64-bit lane masks
+// for the first 256 bins (the ranking of one chunk), and each of its candidates' rank among its
+// earlier candidates of the same bin (u16).
+constexpr int kMaskBins = 256;
+constexpr int kOffBinCnt = kOffStash;                                 // u16 [1024], 4 KB apart
+constexpr int kOffBinMask = kOffStash + kDBins * 2;                   // u64 [256], per wave
+constexpr int kOffRank = kOffStashCh;                                 // u16 [16][512]
+static_assert(kDBins * 2 + kMaskBins * 8 == kStashPerWave * 16, "counts and masks fill a slice");
+static_assert(kCandPerWave * 2 <= kStashPerWave * 4, "a wave's ranks fit its chunk slice");
 
 constexpr size_t kFastDynLds =
     (size_t)kGeneralDynLds + sizeof(GeneralShared) > (size_t)kFastLdsEnd
@@ -74,6 +77,8 @@ struct FastShared {
   uint64_t red[kWaves];
   uint32_t theta_hist[kThetaBins];
   uint32_t kmax0_w[kWaves];
+  uint32_t ndone;              // waves whose stream has ended
+  uint32_t noise_done[kWaves];  // 1 if the wave drew its candidates' noise itself
   uint32_t theta_key;
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
@@ -362,6 +367,12 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kThreads ? kThreads : rr));
   }
 
+  // Wave priorities: streaming waves issue first (priority 3). A wave whose stream has ended
+  // works on at a priority set by how late it ended, so that the post-stream work of early waves
+  // fills the issue slots the streaming waves leave idle instead of delaying them (the
+  // instruction arbiter otherwise favours the oldest wave, which also ends first).
+  __builtin_amdgcn_s_setprio(3);
+
   // ---- 1. Loads: the opt-in entry first (loads complete in issue order, so waiting for it never
   // waits for row data), then a shallow pipeline over the wave's segment: two loads at first, so
   // that every wave's first load lands within ~2 us, then kLoadsAhead.
@@ -388,6 +399,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
   hcnt[tid] = 0u;  // published by the first exchange below
   if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
+  if (tid == 0) fs.ndone = 0u;
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
   const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
@@ -562,6 +574,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
 
   // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts, ranks --------
+  uint32_t order;  // 0 for the first wave whose stream ended, 15 for the last
+  {
+    uint32_t o = 0;
+    if (lane == 0) o = atomicAdd(&fs.ndone, 1u);
+    order = uniform_u32(read_lane(o, 0));
+  }
+  if (order < (uint32_t)kWaves - 8) __builtin_amdgcn_s_setprio(0);
+  else if (order < (uint32_t)kWaves - 4) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(2);
   {
     double wz = 0.0;
     if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
@@ -573,7 +594,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
   float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
-  uint32_t ncand = 0;  // wave-uniform
+  uint32_t ncand = 0;            // wave-uniform
+  float xcand = -__builtin_inff();  // lane maximum of the candidates
   {
     const uint32_t nstash = wfill;  // never slots that were not written in this row
     // theta is finite whenever the row can be served here; clamping it keeps -inf out.
@@ -581,22 +603,39 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     // Elements that are not candidates are written to a dummy slot of this lane (in the noise
     // array, which is filled later), which keeps the scatter free of branches.
     uint32_t* dummy = reinterpret_cast<uint32_t*>(noise) + lane;
-    for (uint32_t base = 0; base < nstash; base += kWaveSize) {
-      const uint32_t i = base + lane;
-      const bool ok = i < nstash;
-      const uint4 q = ok ? stash[i] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-      const uint32_t off = ok ? stash_ch[i] * 8u : 0u;
-      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+    // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
+    constexpr int kChunks = kStashPerWave / kWaveSize;
+    uint4 qs[kChunks];
+    uint32_t offs[kChunks];
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      const uint32_t i = (uint32_t)ch * kWaveSize + lane;
+      qs[ch] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+      offs[ch] = 0u;
+      if ((uint32_t)ch * kWaveSize < nstash && i < nstash) {
+        qs[ch] = stash[i];
+        offs[ch] = stash_ch[i] * 8u;
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      if ((uint32_t)ch * kWaveSize >= nstash) break;
+      const uint32_t w4[4] = {qs[ch].x, qs[ch].y, qs[ch].z, qs[ch].w};
+      const uint32_t off = offs[ch];
       uint32_t words[8];
       bool isc[8];
+      float xc[8];
       uint32_t n = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
         isc[e] = __uint_as_float(hi) >= th;  // -0 ties +0; NaN fails
+        xc[e] = isc[e] ? __uint_as_float(hi) : -__builtin_inff();
         words[e] = hi | (off + (uint32_t)e);
         n += isc[e];
       }
+      xcand = maximum3f(xcand, maximum3f(xc[0], xc[1], xc[2]), maximum3f(xc[3], xc[4], xc[5]));
+      xcand = maximum3f(xcand, xc[6], xc[7]);
       uint32_t total;
       uint32_t at = ncand + wave_excl_sum(n, total);
 #pragma unroll
@@ -608,53 +647,82 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       ncand += total;
     }
   }
-  // The stash slice of this wave is free now. It holds the wave's count per bin
-  // bi = key - theta_key (u16 pairs; later the exclusive prefix over earlier waves, the capture
-  // offsets) and each candidate's rank among the wave's earlier candidates of its bin.
-  uint32_t* bincnt = reinterpret_cast<uint32_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16);
-  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16 +
-                                                kDBins * 2);
-  for (uint32_t i = lane; i < (uint32_t)kDBins / 8; i += kWaveSize)
+  // The stash slices of this wave are free now: its count per bin and its candidates' ranks.
+  uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16);
+  uint64_t* binmask = reinterpret_cast<uint64_t*>(lds + kOffBinMask + wid * kStashPerWave * 16);
+  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + kOffRank) + wid * kCandPerWave;
+  for (uint32_t i = lane; i < (uint32_t)(kStashPerWave * 16) / 16; i += kWaveSize)
     reinterpret_cast<uint4*>(bincnt)[i] = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
   // Maximum: for top_p < 1 the largest candidate (the row maximum is >= theta, so it is one);
   // otherwise the running maximum of the stream (which also carries NaN).
-  float xm = NEED_P ? -__builtin_inff() : m_l;
+  const float wxc = wave_reduce(xcand, MaximumF32());
+  {
+    float wm = wxc;
+    if constexpr (!NEED_P) wm = wave_reduce(m_l, MaximumF32());
+    if (lane == 0) fs.wave_m[wid] = wm;
+  }
+  // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
+  // earlier chunks (this wave's own table, so plain reads and writes) plus the lanes of its bin
+  // below it in this chunk. Those lanes come from a 64-bit mask per bin that every lane ORs its
+  // bit into, or, when the wave's bins reach beyond the mask table, from ballots over the bits
+  // of the bin. The bin's first lane stores the new count and adds the chunk's count to the
+  // row histogram.
+  const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
+  const bool by_mask = bmax < (uint32_t)kMaskBins;
   for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
     const uint32_t i = base + lane;
     const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
-    if constexpr (NEED_P) xm = maximum2f(xm, __uint_as_float(wd & 0xFFFF0000u));
     const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
     const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
-    // Lanes of this chunk with my bin: intersect, over the 10 bits of bi, the ballot of lanes
-    // whose bit matches mine. The bin's first lane adds the bin's count once.
-    uint64_t same = __ballot(in);
+    uint64_t same;
+    if (by_mask) {
+      if (in) atomicOr(reinterpret_cast<unsigned long long*>(&binmask[bi]), 1ull << lane);
+      same = in ? binmask[bi] : 0ull;
+    } else {
+      same = __ballot(in);
 #pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
-      same &= ((bi >> bit) & 1u) ? ones : ~ones;
+      for (int bit = 0; bit < 10; ++bit) {
+        const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
+        same &= ((bi >> bit) & 1u) ? ones : ~ones;
+      }
     }
-    const uint32_t first = (uint32_t)__builtin_ctzll(same | (1ull << 63));
-    uint32_t before = 0;
-    if (in && lane == first) {
-      const uint32_t cnt = (uint32_t)__popcll(same);
-      atomicAdd(&hcnt[bi], cnt);
-      const uint32_t sh = (bi & 1u) * 16u;
-      before = (atomicAdd(&bincnt[bi >> 1], cnt << sh) >> sh) & 0xFFFFu;
+    if (in) {
+      const uint32_t c0 = bincnt[bi];
+      rankw[i] = (uint16_t)(c0 + mbcnt(same));
+      if (lane == (uint32_t)__builtin_ctzll(same)) {
+        const uint32_t cnt = (uint32_t)__popcll(same);
+        bincnt[bi] = (uint16_t)(c0 + cnt);
+        if (by_mask) binmask[bi] = 0ull;
+        atomicAdd(&hcnt[bi], cnt);
+      }
     }
-    before = (uint32_t)__shfl((int)before, (int)first, kWaveSize);
-    if (in) rankw[i] = (uint16_t)(before + mbcnt(same));
   }
-  {
-    const float wm = wave_reduce(xm, MaximumF32());
-    if (lane == 0) fs.wave_m[wid] = wm;
+  // Race noise of this wave's candidates, 64 at a time, until every wave's stream has ended
+  // (the waves among the last four to end leave all of it): the helper waves draw the rest
+  // during the bin scan.
+  uint32_t nz = 0;
+  if (order < (uint32_t)kWaves - 4) {
+    for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
+      if (uniform_u32(*reinterpret_cast<volatile uint32_t*>(&fs.ndone)) >= (uint32_t)kWaves) break;
+      const uint32_t i = base + lane;
+      if (i < nc_here) {
+        const uint32_t id = id0 + (cand[i] & 0x3FFFu);
+        noise[i] = race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
+      }
+      nz = base + kWaveSize < nc_here ? base + kWaveSize : nc_here;
+    }
   }
-  if (lane == 0) fs.wave_cand[wid] = ncand;
+  if (lane == 0) {
+    fs.wave_cand[wid] = ncand;
+    fs.noise_done[wid] = nz;
+  }
   lds_barrier();
 
   // ---- 4. Wave 0: status and the joint threshold. Waves 1-15: capture offsets, race noise -----
   const bool capture = slot >= 0;
   if (wid == 0) {
+    __builtin_amdgcn_s_setprio(3);
     const uint32_t w = lane & (kWaves - 1);
     const float m = row16_reduce(fs.wave_m[w], MaximumF32());
     const uint32_t ntot = row16_reduce(fs.wave_cand[w], SumU32());
@@ -690,28 +758,32 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
   } else {
+    __builtin_amdgcn_s_setprio(1);
     const uint32_t h = wid - 1;  // helper index 0..14
     if (capture) {
-      // Exclusive prefix of every bin's count over the waves (u16 pairs, added as u32: totals
-      // stay below 2^16): wave w's first capture offset in each tie group.
-      const uint32_t* cnt0 = reinterpret_cast<const uint32_t*>(lds + kOffBinCnt);
-      for (uint32_t j = tid - kWaveSize; j < (uint32_t)kDBins / 2; j += kThreads - kWaveSize) {
+      // Exclusive prefix of every bin's count over the waves: wave w's first capture offset in
+      // each tie group, relative to the group's base.
+      uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + kOffBinCnt);
+      constexpr int kStride = kStashPerWave * 16 / 2;  // u16 between two waves' tables
+      for (uint32_t j = tid - kWaveSize; j < (uint32_t)kDBins; j += kThreads - kWaveSize) {
         uint32_t v[kWaves];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * (kStashPerWave * 4) + j];
+        for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * kStride + j];
         uint32_t acc = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const_cast<uint32_t*>(cnt0)[w * (kStashPerWave * 4) + j] = acc;
+          cnt0[w * kStride + j] = (uint16_t)acc;
           acc += v[w];
         }
       }
     }
-    // Race noise of every candidate of every wave, 64 at a time, spread over the 15 helpers.
+    // Race noise of the candidates of the waves that left it, 64 at a time, spread over the 15
+    // helpers.
     const uint32_t l16 = lane & (kWaves - 1);
-    const uint32_t nw = fs.wave_cand[l16];
-    const uint32_t nchunks = ((nw < (uint32_t)kCandPerWave ? nw : (uint32_t)kCandPerWave) +
-                              kWaveSize - 1) / kWaveSize;
+    const uint32_t nw0 = fs.wave_cand[l16];
+    const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
+    const uint32_t first = fs.noise_done[l16];  // candidates done: a multiple of 64, or all
+    const uint32_t nchunks = (nw - first + kWaveSize - 1) / kWaveSize;
     const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? nchunks : 0u, SumU32(), 0u);
     const uint32_t jobs = read_lane(incl, kWaves - 1);
     const uint32_t cwv = cw;
@@ -719,7 +791,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
       const uint32_t c0 = read_lane(incl - nchunks, (int)ww);
       const uint32_t nww = read_lane(nw, (int)ww);
-      const uint32_t i = (q - c0) * kWaveSize + lane;
+      const uint32_t i = read_lane(first, (int)ww) + (q - c0) * kWaveSize + lane;
       if (i < nww && i < (uint32_t)kCandPerWave) {
         const uint32_t wd = reinterpret_cast<const uint32_t*>(lds + kOffCand)[ww * kCandPerWave + i];
         const uint32_t id = ww * cwv * 8u + (wd & 0x3FFFu);
@@ -729,6 +801,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
   }
   lds_barrier();
+  __builtin_amdgcn_s_setprio(2);
   const int32_t decision = fs.decision;
   if (decision == kNonfinite || decision == kNoSupport) {
     finish_empty_row(a, b, slot, decision == kNonfinite ? TSC_ROW_NONFINITE : TSC_ROW_NO_SUPPORT);
@@ -776,8 +849,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (capture) {
       const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
       const uint32_t g = group_of_bin[bi];
-      const uint32_t pre = (bincnt[bi >> 1] >> ((bi & 1u) * 16u)) & 0xFFFFu;
-      const uint32_t at = grp_base[g] + pre + rankw[i];
+      const uint32_t at = grp_base[g] + bincnt[bi] + rankw[i];
       if (at < W) {
         out_ids[at] = (int32_t)id;
         if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
