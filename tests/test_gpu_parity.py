@@ -258,8 +258,13 @@ def _fast_rows(rng, V):
     # over six binades above a dense filler): the capture tables are too small, general path.
     spread = rng.uniform(1.0, 1.9, V)
     spread[rng.choice(V, 900, replace=False)] = np.geomspace(2.0, 60.0, 900)
+    # A key span of several hundred bins between the cutoff and the maximum (spikes on a
+    # geometric ladder above a coarse-grid bulk) that still has few distinct values: the wide
+    # form of the bin scan, served by the single-read path.
+    wide = np.round(rng.standard_normal(V) * 4) / 4
+    wide[rng.choice(V, 40, replace=False)] = np.round(np.geomspace(8.0, 60.0, 40))
     return dict(grid=grid, gauss=gauss, neg=neg, nan=nan, pinf=pinf, allneg=allneg,
-                hidden=hidden, front=front, spread=spread)
+                hidden=hidden, front=front, spread=spread, wide=wide)
 
 
 FAST_PARAMS = [
@@ -280,6 +285,8 @@ FAST_PARAMS = [
     ("hidden_top", "hidden", 1.0, 1024, 0.95, 0.0),
     ("front_loaded", "front", 1.0, 1024, 1.0, 0.0),
     ("spread_keys", "spread", 5.0, 1000, 1.0, 0.0),
+    ("wide_span", "wide", 12.0, 1024, 0.97, 0.0),
+    ("wide_span_minp", "wide", 12.0, 1024, 1.0, 0.01),
     ("tiny_T", "gauss", 1e-3, 50, 0.9, 0.0),
     ("greedy", "grid", 0.0, 50, 0.9, 0.0),
 ]

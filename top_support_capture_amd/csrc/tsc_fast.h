@@ -4,9 +4,9 @@
 // all per-element work happens while the loads land. Wave w owns a contiguous segment of the row
 // (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
 //
-//   1. Stream. The lane maxima of the first load of every segment (a sample spread over the whole
-//      row) give a reference R for the mass and a cutoff theta that about twice top_k tokens of
-//      the row should exceed: an LDS histogram of their key distances to the sample's maximum,
+//   1. Stream. The lane maxima of the first loads of every segment (a sample spread over the
+//      whole row) give a reference R for the mass and a cutoff theta that about 1.6 top_k tokens
+//      of the row should exceed: an LDS histogram of their key distances to the sample's maximum,
 //      built over the first stream steps so that the loads keep flowing.
 //   2. As each load lands: running maximum (NaN-propagating, so it also detects NaN), for
 //      top_p < 1 the lane sum of exp2(x * log2(e) / T - R * log2(e) / T), and a ballot on "this
@@ -78,7 +78,8 @@ struct FastShared {
   uint32_t theta_hist[kThetaBins];
   uint32_t kmax0_w[kWaves];
   uint32_t ndone;              // waves whose stream has ended
-  uint32_t noise_done[kWaves];  // 1 if the wave drew its candidates' noise itself
+  uint32_t noise_done[kWaves];  // candidates whose noise the wave drew itself (from the first)
+  uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
   uint32_t theta_key;
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
@@ -239,8 +240,96 @@ __device__ inline T row16_reduce(T v, Op op) {
 // were counted by bi = key - theta_key = dspan - d. Lane l owns the nb consecutive bins from
 // l * nb. Publishes the threshold d*, the support size, and for capture rows the tie-group tables:
 // the group of each support bin, each group's base position and (x - m) / T, and ln Z_S.
-template <bool NEED_P>
+template <bool NEED_P, int NB>
 __device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
+                                      int32_t k, float p, float mp, double Z, bool capture,
+                                      const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
+  using E = Elem<TSC_DTYPE_BF16>;
+  const uint32_t lane = lane_id();
+  const uint32_t nb = (dspan + kWaveSize) / kWaveSize;  // 1..NB
+  const bool need_m = mp > 0.0f;
+  // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
+  const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
+  // Per bin (all loads first, so that their latencies overlap): value, count after min-p (a
+  // per-value predicate, monotone in d), and mass. The count is packed with the group
+  // indicator as count << 11 | present (at most 8192 candidates and 1024 bins), so that one
+  // integer scan gives both positions and group indices.
+  float xs[NB];
+  uint32_t pk[NB];
+  double bm[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const uint32_t d = lane * nb + (uint32_t)t;
+    pk[t] = 0u;
+    xs[t] = 0.0f;
+    if ((uint32_t)t < nb && d <= dspan) {
+      xs[t] = E::to_float(bits_of_key<E>(kmax - d));
+      pk[t] = hcnt[dspan - d];
+    }
+  }
+  uint32_t lp_ = 0;
+  double lmass = 0.0;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const uint32_t bc = (!need_m || ((double)xs[t] - (double)m) >= tln_mp) ? pk[t] : 0u;
+    pk[t] = (bc << 11) | (uint32_t)(bc > 0u);
+    bm[t] = (NEED_P || capture) ? (double)bc * (double)__builtin_amdgcn_exp2f((xs[t] - m) * c)
+                                : 0.0;
+    lp_ += pk[t];
+    lmass += bm[t];
+  }
+  uint32_t tp;
+  double tm;
+  uint32_t ep = wave_excl_scan(lp_, SumU32(), tp);
+  double em = wave_excl_scan(lmass, SumF64(), tm);
+  const double pz = (double)p * Z;
+  // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
+  // strictly above <= top_p * Z. Each predicate is monotone in d, so this is the last qualifying
+  // bin of the last lane that has one.
+  int32_t best = -1;
+  uint32_t bL = 0, bG = 0;
+  double bZ = 0.0;
+  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + kOffGroupOfBin);
+  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
+  double* grp_s = reinterpret_cast<double*>(lds + kOffGrpS);
+  const double invT = 1.0 / (double)T;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const uint32_t d = lane * nb + (uint32_t)t;
+    if (pk[t] & 1u) {
+      const uint32_t ec = ep >> 11, eg = ep & 0x7FFu;
+      const bool qual = ec < (uint32_t)k && (!NEED_P || em <= pz);
+      if (qual) {
+        best = (int32_t)d;
+        bL = ec + (pk[t] >> 11);
+        bG = eg + 1u;
+        bZ = em + bm[t];
+        if (capture && eg < (uint32_t)kMaxGroups) {
+          group_of_bin[dspan - d] = (uint16_t)eg;
+          grp_base[eg] = ec;
+          grp_s[eg] = ((double)xs[t] - (double)m) * invT;
+        }
+      }
+    }
+    ep += pk[t];
+    em += bm[t];
+  }
+  // d* >= 0 always: bin 0 holds the maximum, which passes every predicate.
+  const int32_t dstar = wave_reduce(best, MaxI32());
+  const int owner = (int)((uint32_t)dstar / nb);
+  const uint32_t L = read_lane(bL, owner), G = read_lane(bG, owner);
+  const double zs = read_lane(bZ, owner);
+  if (lane == 0) {
+    fs.decision = (capture && G > (uint32_t)kMaxGroups) ? kFallback : kProceed;
+    fs.dstar = dstar;
+    fs.L = L;
+    fs.lnzs = ln_fast(zs);  // logprob = (x - m) / T - ln Z_S
+  }
+}
+
+// The same for spans of 256 bins and more (bins re-read per pass instead of kept in registers).
+template <bool NEED_P>
+__device__ inline void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
                                       const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
@@ -358,13 +447,17 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   // Rank of theta among the 1024 lane maxima of the first loads: aim for about 2k + 64 tokens
   // above theta; a maximum of 8 values exceeds the quantile 1 - q with probability 1 - (1-q)^8.
+  // The sample is the lane maxima of the first two loads (2048 values, 16384 elements); the
+  // target of 1.6 k + 64 candidates keeps the k-th largest value above theta by about five
+  // standard deviations of the estimate.
+  constexpr int kSamples = 2 * kThreads;
   uint32_t theta_rank;
   {
-    const float q = fminf(1.0f, (2.0f * (float)k + 64.0f) / (float)V);
+    const float q = fminf(1.0f, (1.6f * (float)k + 64.0f) / (float)V);
     const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
     const float pr = 1.0f - t4 * t4;
-    const int rr = (int)ceilf(pr * (float)kThreads);
-    theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kThreads ? kThreads : rr));
+    const int rr = (int)ceilf(pr * (float)kSamples);
+    theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kSamples ? kSamples : rr));
   }
 
   // Wave priorities: streaming waves issue first (priority 3). A wave whose stream has ended
@@ -503,8 +596,13 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   add_mass(f);
   pin();
   {
-    const uint32_t dist = kmax0 - key0;  // keys below 0x80 are -inf or NaN: not counted
-    if (dist < (uint32_t)kThetaBins && (key0 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist], 1u);
+    // Distances below the first loads' maximum (the second load's maximum may lie above it: then
+    // distance 0); keys below 0x80 are -inf or NaN and are not counted.
+    const uint32_t key1 = key_of<E>(__float_as_uint(lm1) >> 16);
+    const uint32_t dist0 = kmax0 - key0;
+    const uint32_t dist1 = key1 >= kmax0 ? 0u : kmax0 - key1;
+    if (dist0 < (uint32_t)kThetaBins && (key0 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist0], 1u);
+    if (dist1 < (uint32_t)kThetaBins && (key1 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist1], 1u);
   }
   if (a.R <= kThreads) slot_step2(a, b, sscan, fs);
   lds_barrier();
@@ -716,6 +814,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   if (lane == 0) {
     fs.wave_cand[wid] = ncand;
     fs.noise_done[wid] = nz;
+    fs.bin_hi[wid] = wxc > -__builtin_inff() ? bmax + 1u : 0u;
   }
   lds_barrier();
 
@@ -752,9 +851,13 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       // theta is a lower bound of the k-th largest value iff at least k candidates exist.
       if (over || ntot < (uint32_t)k || kmax < theta_key || kmax - theta_key >= (uint32_t)kDBins)
         decision = kFallback;
-      if (decision == kProceed)
-        bin_scan_wave0<NEED_P>(kmax, kmax - theta_key, m, T, c, k, p, mp, Z, capture, hcnt, lds,
-                               fs);
+      if (decision == kProceed) {
+        const uint32_t dspan = kmax - theta_key;
+        if (dspan < 4u * kWaveSize)
+          bin_scan_wave0<NEED_P, 4>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+        else
+          bin_scan_wave0_wide<NEED_P>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+      }
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
   } else {
@@ -765,7 +868,11 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       // each tie group, relative to the group's base.
       uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + kOffBinCnt);
       constexpr int kStride = kStashPerWave * 16 / 2;  // u16 between two waves' tables
-      for (uint32_t j = tid - kWaveSize; j < (uint32_t)kDBins; j += kThreads - kWaveSize) {
+      uint32_t nbins = 0;  // bins any wave used
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) nbins = nbins > fs.bin_hi[w] ? nbins : fs.bin_hi[w];
+      nbins = uniform_u32(nbins < (uint32_t)kDBins ? nbins : (uint32_t)kDBins);
+      for (uint32_t j = tid - kWaveSize; j < nbins; j += kThreads - kWaveSize) {
         uint32_t v[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * kStride + j];
