@@ -241,7 +241,7 @@ __device__ inline T row16_reduce(T v, Op op) {
 // l * nb. Publishes the threshold d*, the support size, and for capture rows the tie-group tables:
 // the group of each support bin, each group's base position and (x - m) / T, and ln Z_S.
 template <bool NEED_P, int NB>
-__device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
+__device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
                                       const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
@@ -329,7 +329,7 @@ __device__ inline void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, fl
 
 // The same for spans of 256 bins and more (bins re-read per pass instead of kept in registers).
 template <bool NEED_P>
-__device__ inline void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, float m, float T, float c,
+__device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
                                       const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
