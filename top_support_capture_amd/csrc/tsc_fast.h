@@ -80,7 +80,6 @@ struct FastShared {
   uint32_t ndone;              // waves whose stream has ended
   uint32_t noise_done[kWaves];  // candidates whose noise the wave drew itself (from the first)
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
-  uint32_t theta_key;
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
   float wave_m[kWaves];
@@ -606,8 +605,9 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   if (a.R <= kThreads) slot_step2(a, b, sscan, fs);
   lds_barrier();
-  // Step 2, exchange 3: wave 0 finds the smallest distance whose cumulative count reaches the rank
-  // (when fewer maxima are within reach, the deepest reachable key).
+  // Step 2: every wave finds the smallest distance whose cumulative count reaches the rank (when
+  // fewer maxima are within reach, the deepest reachable key); the same scan in each wave saves
+  // an exchange.
   issue(kLoadsAhead + 2);
   mask_tail(2);
   unpack(r[2], f);
@@ -615,7 +615,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   m_l = maximum2f(m_l, lm2);
   add_mass(f);
   pin();
-  if (wid == 0) {
+  uint32_t theta_key;
+  {
     uint32_t hc[4];
     uint32_t lsum = 0;
 #pragma unroll
@@ -633,10 +634,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
     const uint32_t dmin = wave_reduce(found, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
     const uint32_t dsel = dmin != 0xFFFFFFFFu ? dmin : (uint32_t)kThetaBins - 1u;
-    if (lane == 0) fs.theta_key = kmax0 > dsel ? kmax0 - dsel : 0u;
+    theta_key = uniform_u32(kmax0 > dsel ? kmax0 - dsel : 0u);
   }
-  lds_barrier();
-  const uint32_t theta_key = uniform_u32(fs.theta_key);
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
   stash_load(0, r[0], lm0 >= theta);
@@ -862,7 +861,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (decision != kProceed && lane == 0) fs.decision = decision;
   } else {
     __builtin_amdgcn_s_setprio(1);
-    const uint32_t h = wid - 1;  // helper index 0..14
     if (capture) {
       // Exclusive prefix of every bin's count over the waves: wave w's first capture offset in
       // each tie group, relative to the group's base.
@@ -872,7 +870,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) nbins = nbins > fs.bin_hi[w] ? nbins : fs.bin_hi[w];
       nbins = uniform_u32(nbins < (uint32_t)kDBins ? nbins : (uint32_t)kDBins);
-      for (uint32_t j = tid - kWaveSize; j < nbins; j += kThreads - kWaveSize) {
+      // Waves 1-4 only: the other helpers start on the noise at once.
+      for (uint32_t j = tid - kWaveSize; wid <= 4u && j < nbins; j += 4u * kWaveSize) {
         uint32_t v[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * kStride + j];
@@ -884,27 +883,34 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         }
       }
     }
-    // Race noise of the candidates of the waves that left it, 64 at a time, spread over the 15
-    // helpers.
+    // Race noise of the candidates of the waves that left it, 128 at a time (two independent
+    // Philox chains per lane, whose latencies overlap), spread over the 15 helpers; waves 5-15
+    // take the first jobs.
+    constexpr uint32_t kJob = 2 * kWaveSize;
     const uint32_t l16 = lane & (kWaves - 1);
     const uint32_t nw0 = fs.wave_cand[l16];
     const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
     const uint32_t first = fs.noise_done[l16];  // candidates done: a multiple of 64, or all
-    const uint32_t nchunks = (nw - first + kWaveSize - 1) / kWaveSize;
-    const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? nchunks : 0u, SumU32(), 0u);
+    const uint32_t njobs = (nw - first + kJob - 1) / kJob;
+    const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
     const uint32_t jobs = read_lane(incl, kWaves - 1);
     const uint32_t cwv = cw;
-    for (uint32_t q = h; q < jobs; q += kWaves - 1) {
+    const uint32_t* cand_all = reinterpret_cast<const uint32_t*>(lds + kOffCand);
+    float* noise_all = reinterpret_cast<float*>(lds + kOffNoise);
+    const uint32_t hh = wid >= 5u ? wid - 5u : wid + (uint32_t)kWaves - 6u;  // 0..14
+    for (uint32_t q = hh; q < jobs; q += kWaves - 1) {
       const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
-      const uint32_t c0 = read_lane(incl - nchunks, (int)ww);
+      const uint32_t c0 = read_lane(incl - njobs, (int)ww);
       const uint32_t nww = read_lane(nw, (int)ww);
-      const uint32_t i = read_lane(first, (int)ww) + (q - c0) * kWaveSize + lane;
-      if (i < nww && i < (uint32_t)kCandPerWave) {
-        const uint32_t wd = reinterpret_cast<const uint32_t*>(lds + kOffCand)[ww * kCandPerWave + i];
-        const uint32_t id = ww * cwv * 8u + (wd & 0x3FFFu);
-        reinterpret_cast<float*>(lds + kOffNoise)[ww * kCandPerWave + i] =
-            race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
-      }
+      const uint32_t i0 = read_lane(first, (int)ww) + (q - c0) * kJob + lane;
+      const uint32_t i1 = i0 + kWaveSize;
+      const bool v0 = i0 < nww, v1 = i1 < nww;
+      const uint32_t wd0 = v0 ? cand_all[ww * kCandPerWave + i0] : 0u;
+      const uint32_t wd1 = v1 ? cand_all[ww * kCandPerWave + i1] : 0u;
+      const uint32_t r0 = race_word(ww * cwv * 8u + (wd0 & 0x3FFFu), seed, pos);
+      const uint32_t r1 = race_word(ww * cwv * 8u + (wd1 & 0x3FFFu), seed, pos);
+      if (v0) noise_all[ww * kCandPerWave + i0] = race_noise((float)(2u * (r0 >> 9) + 1u) * 0x1p-24f);
+      if (v1) noise_all[ww * kCandPerWave + i1] = race_noise((float)(2u * (r1 >> 9) + 1u) * 0x1p-24f);
     }
   }
   lds_barrier();
