@@ -13,14 +13,19 @@
 //      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash.
 //   3. Each wave, as soon as its segment is done: expands its stash into candidate words
 //      (bf16 bits << 16 | offset in the segment), still in id order, counts them into a
-//      histogram over key - key(theta), and draws their race noise (Philox4x32-10).
-//   4. One wave reads the per-wave results and scans the histogram bins from the maximum down:
-//      the joint threshold is the largest distance d from the maximum with fewer than k tokens
-//      strictly above and (top_p < 1) mass strictly above <= top_p * Z; min-p drops whole bins.
-//      theta was a true lower bound iff at least k candidates were found (checked here).
-//   5. Race over the survivors (float32 scores, float64 for the few within 1e-4 of the best),
-//      then, for opt-in rows, the ordered capture: the bin scan gives each tie group's base
-//      position and a ballot multisplit ranks the group's members by id.
+//      histogram over key - key(theta) and ranks each among its wave's earlier candidates of
+//      the same key.
+//   4. After one barrier, no more: wave 0 checks the row and scans the histogram bins from the
+//      maximum down: the joint threshold is the largest distance d from the maximum with fewer
+//      than k tokens strictly above and (top_p < 1) mass strictly above <= top_p * Z; min-p
+//      drops whole bins. theta was a true lower bound iff at least k candidates were found
+//      (checked here). Meanwhile the other waves draw every candidate's race uniform
+//      (Philox4x32-10, in jobs claimed from an LDS counter) and keep per bin the largest one
+//      (all candidates of a bin share their logit, so that one is the bin's best race score).
+//   5. The wave that completes the last draw picks the token over the support's bins (float32
+//      scores, float64 for the few within 1e-4 of the best); every wave writes the ordered
+//      capture of its own candidates: the bin scan gives each tie group's base position, the
+//      ranks and a prefix over the waves the rest. Waves wait on LDS flags, not barriers.
 // Any row this path cannot serve exactly (capacities, theta above the k-th value, overflow of
 // the mass, greedy rows, other dtypes or layouts) runs through general_row in the same workgroup.
 #pragma once
@@ -47,8 +52,9 @@ constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of
 constexpr int kOffStash = 0;                                          // uint4 [16][256]
 constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16][256]
 constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
-constexpr int kOffNoise = kOffCand + kWaves * kCandPerWave * 4;       // f32 [16][512] race noise
-constexpr int kOffCnt = kOffNoise + kWaves * kCandPerWave * 4;        // u32 [1024] by key - theta
+constexpr int kOffBinBest = kOffCand + kWaves * kCandPerWave * 4;     // u64 [1024] race per bin
+constexpr int kOffDummy = kOffBinBest + kDBins * 8;                   // u32 [64] scatter sink
+constexpr int kOffCnt = kOffDummy + kWaveSize * 4;                    // u32 [1024] by key - theta
 constexpr int kOffGroupOfBin = kOffCnt + kDBins * 4;                // u16 [1024] group by bin
 constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;              // u32 [256]
 constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;                // f64 [256] (x - m) / T
@@ -78,7 +84,10 @@ struct FastShared {
   uint32_t theta_hist[kThetaBins];
   uint32_t kmax0_w[kWaves];
   uint32_t ndone;              // waves whose stream has ended
-  uint32_t noise_done[kWaves];  // candidates whose noise the wave drew itself (from the first)
+  uint32_t scan_ready;          // set by wave 0 once the decision and the bin scan are published
+  uint32_t prefix_done;         // waves that finished their share of the capture offsets
+  uint32_t job_next;            // next race-draw job to claim
+  uint32_t job_done;            // race-draw jobs completed
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
@@ -90,12 +99,6 @@ struct FastShared {
   int32_t dstar;
   uint32_t L;
   double lnzs;
-  float race_b1[kWaves], race_b2[kWaves];
-  int32_t race_id[kWaves];
-  float race_x[kWaves];
-  double ref_top[kWaves];
-  int32_t ref_id[kWaves];
-  float ref_x[kWaves];
 };
 
 __device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -168,6 +171,27 @@ struct MaximumF32 {
 __device__ inline float race_noise(float u) {
   const float e = -__builtin_amdgcn_logf(u) * 0.6931471805599453f;
   return -__builtin_amdgcn_logf(e) * 0.6931471805599453f;
+}
+
+// Flags between the waves of one workgroup, in LDS. A publish orders every earlier LDS write of
+// the wave before the flag (release at workgroup scope); a wait spins with s_sleep until the flag
+// reaches a value, then orders the wave's later LDS reads after it. Every flag a wave waits on is
+// published unconditionally by waves that never wait on it, so every wait ends.
+__device__ inline void lds_publish(uint32_t* flag, uint32_t v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if (lane_id() == 0) __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Adds to a counter after every earlier LDS write of the wave; returns the previous value.
+__device__ inline uint32_t lds_publish_add(uint32_t* ctr, uint32_t v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  uint32_t old = 0u;
+  if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return read_lane(old, 0);
+}
+__device__ inline void lds_wait_at_least(const uint32_t* flag, uint32_t v) {
+  while (uniform_u32(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v)
+    __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -491,7 +515,14 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
   hcnt[tid] = 0u;  // published by the first exchange below
   if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
-  if (tid == 0) fs.ndone = 0u;
+  if (tid == 0) {
+    fs.ndone = 0u;
+    fs.scan_ready = 0u;
+    fs.prefix_done = 0u;
+    fs.job_next = 0u;
+    fs.job_done = 0u;
+  }
+  reinterpret_cast<uint64_t*>(lds + kOffBinBest)[tid] = 0ull;
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
   const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
@@ -670,7 +701,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     stash_load(j, r[j], flag);
   }
 
-  // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts, ranks --------
+  // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts ---------------
   uint32_t order;  // 0 for the first wave whose stream ended, 15 for the last
   {
     uint32_t o = 0;
@@ -690,16 +721,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
-  float* noise = reinterpret_cast<float*>(lds + kOffNoise) + wid * kCandPerWave;
+  uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + kOffBinBest);
   uint32_t ncand = 0;            // wave-uniform
   float xcand = -__builtin_inff();  // lane maximum of the candidates
   {
     const uint32_t nstash = wfill;  // never slots that were not written in this row
     // theta is finite whenever the row can be served here; clamping it keeps -inf out.
     const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
-    // Elements that are not candidates are written to a dummy slot of this lane (in the noise
-    // array, which is filled later), which keeps the scatter free of branches.
-    uint32_t* dummy = reinterpret_cast<uint32_t*>(noise) + lane;
+    // Elements that are not candidates are written to a dummy slot of this lane, which keeps
+    // the scatter free of branches.
+    uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + kOffDummy) + lane;
     // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
     constexpr int kChunks = kStashPerWave / kWaveSize;
     uint4 qs[kChunks];
@@ -744,7 +775,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       ncand += total;
     }
   }
-  // The stash slices of this wave are free now: its count per bin and its candidates' ranks.
+  // The stash slices of this wave are free now: its count per bin, the bin masks of the
+  // ranking, and its candidates' ranks.
   uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16);
   uint64_t* binmask = reinterpret_cast<uint64_t*>(lds + kOffBinMask + wid * kStashPerWave * 16);
   uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + kOffRank) + wid * kCandPerWave;
@@ -759,14 +791,14 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if constexpr (!NEED_P) wm = wave_reduce(m_l, MaximumF32());
     if (lane == 0) fs.wave_m[wid] = wm;
   }
+  const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
+  const bool by_mask = bmax < (uint32_t)kMaskBins;
   // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
   // earlier chunks (this wave's own table, so plain reads and writes) plus the lanes of its bin
   // below it in this chunk. Those lanes come from a 64-bit mask per bin that every lane ORs its
   // bit into, or, when the wave's bins reach beyond the mask table, from ballots over the bits
   // of the bin. The bin's first lane stores the new count and adds the chunk's count to the
   // row histogram.
-  const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
-  const bool by_mask = bmax < (uint32_t)kMaskBins;
   for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
     const uint32_t i = base + lane;
     const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
@@ -795,30 +827,26 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   }
-  // Race noise of this wave's candidates, 64 at a time, until every wave's stream has ended
-  // (the waves among the last four to end leave all of it): the helper waves draw the rest
-  // during the bin scan.
-  uint32_t nz = 0;
-  if (order < (uint32_t)kWaves - 4) {
-    for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
-      if (uniform_u32(*reinterpret_cast<volatile uint32_t*>(&fs.ndone)) >= (uint32_t)kWaves) break;
-      const uint32_t i = base + lane;
-      if (i < nc_here) {
-        const uint32_t id = id0 + (cand[i] & 0x3FFFu);
-        noise[i] = race_noise((float)(2u * (race_word(id, seed, pos) >> 9) + 1u) * 0x1p-24f);
-      }
-      nz = base + kWaveSize < nc_here ? base + kWaveSize : nc_here;
-    }
-  }
   if (lane == 0) {
     fs.wave_cand[wid] = ncand;
-    fs.noise_done[wid] = nz;
     fs.bin_hi[wid] = wxc > -__builtin_inff() ? bmax + 1u : 0u;
   }
   lds_barrier();
 
-  // ---- 4. Wave 0: status and the joint threshold. Waves 1-15: capture offsets, race noise -----
+  // ---- 4. Wave 0: status and the joint threshold. Waves 1-15: capture offsets, race draws ------
+  // No barrier follows: each wave waits on LDS flags for exactly what it needs next.
   const bool capture = slot >= 0;
+  // Race draws: jobs of 128 candidates of one wave (two independent Philox chains per lane,
+  // whose latencies overlap), claimed by the helper waves from an LDS counter. The wave that
+  // completes the last job picks the token (wave 0 when there is no job).
+  constexpr uint32_t kJob = 2 * kWaveSize;
+  const uint32_t l16 = lane & (kWaves - 1);
+  const uint32_t nw0 = fs.wave_cand[l16];
+  const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
+  const uint32_t njobs = (nw + kJob - 1) / kJob;
+  const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
+  const uint32_t jobs = read_lane(incl, kWaves - 1);
+  bool picker = wid == 0 && jobs == 0u;
   if (wid == 0) {
     __builtin_amdgcn_s_setprio(3);
     const uint32_t w = lane & (kWaves - 1);
@@ -859,19 +887,20 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
+    lds_publish(&fs.scan_ready, 1u);
   } else {
-    __builtin_amdgcn_s_setprio(1);
-    if (capture) {
+    __builtin_amdgcn_s_setprio(2);
+    if (capture && wid <= 4u) {
       // Exclusive prefix of every bin's count over the waves: wave w's first capture offset in
-      // each tie group, relative to the group's base.
+      // each tie group, relative to the group's base (waves 1-4; the other helpers start on the
+      // race draws at once).
       uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + kOffBinCnt);
       constexpr int kStride = kStashPerWave * 16 / 2;  // u16 between two waves' tables
       uint32_t nbins = 0;  // bins any wave used
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) nbins = nbins > fs.bin_hi[w] ? nbins : fs.bin_hi[w];
       nbins = uniform_u32(nbins < (uint32_t)kDBins ? nbins : (uint32_t)kDBins);
-      // Waves 1-4 only: the other helpers start on the noise at once.
-      for (uint32_t j = tid - kWaveSize; wid <= 4u && j < nbins; j += 4u * kWaveSize) {
+      for (uint32_t j = tid - kWaveSize; j < nbins; j += 4u * kWaveSize) {
         uint32_t v[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) v[w] = cnt0[w * kStride + j];
@@ -882,39 +911,38 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           acc += v[w];
         }
       }
+      lds_publish_add(&fs.prefix_done, 1u);
     }
-    // Race noise of the candidates of the waves that left it, 128 at a time (two independent
-    // Philox chains per lane, whose latencies overlap), spread over the 15 helpers; waves 5-15
-    // take the first jobs.
-    constexpr uint32_t kJob = 2 * kWaveSize;
-    const uint32_t l16 = lane & (kWaves - 1);
-    const uint32_t nw0 = fs.wave_cand[l16];
-    const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
-    const uint32_t first = fs.noise_done[l16];  // candidates done: a multiple of 64, or all
-    const uint32_t njobs = (nw - first + kJob - 1) / kJob;
-    const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
-    const uint32_t jobs = read_lane(incl, kWaves - 1);
     const uint32_t cwv = cw;
     const uint32_t* cand_all = reinterpret_cast<const uint32_t*>(lds + kOffCand);
-    float* noise_all = reinterpret_cast<float*>(lds + kOffNoise);
-    const uint32_t hh = wid >= 5u ? wid - 5u : wid + (uint32_t)kWaves - 6u;  // 0..14
-    for (uint32_t q = hh; q < jobs; q += kWaves - 1) {
+    for (;;) {
+      uint32_t q = 0u;
+      if (lane == 0) q = atomicAdd(&fs.job_next, 1u);
+      q = read_lane(q, 0);
+      if (q >= jobs) break;
       const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
       const uint32_t c0 = read_lane(incl - njobs, (int)ww);
       const uint32_t nww = read_lane(nw, (int)ww);
-      const uint32_t i0 = read_lane(first, (int)ww) + (q - c0) * kJob + lane;
+      const uint32_t i0 = (q - c0) * kJob + lane;
       const uint32_t i1 = i0 + kWaveSize;
       const bool v0 = i0 < nww, v1 = i1 < nww;
       const uint32_t wd0 = v0 ? cand_all[ww * kCandPerWave + i0] : 0u;
       const uint32_t wd1 = v1 ? cand_all[ww * kCandPerWave + i1] : 0u;
-      const uint32_t r0 = race_word(ww * cwv * 8u + (wd0 & 0x3FFFu), seed, pos);
-      const uint32_t r1 = race_word(ww * cwv * 8u + (wd1 & 0x3FFFu), seed, pos);
-      if (v0) noise_all[ww * kCandPerWave + i0] = race_noise((float)(2u * (r0 >> 9) + 1u) * 0x1p-24f);
-      if (v1) noise_all[ww * kCandPerWave + i1] = race_noise((float)(2u * (r1 >> 9) + 1u) * 0x1p-24f);
+      const uint32_t id0w = ww * cwv * 8u + (wd0 & 0x3FFFu);
+      const uint32_t id1w = ww * cwv * 8u + (wd1 & 0x3FFFu);
+      const uint32_t r0 = race_word(id0w, seed, pos);
+      const uint32_t r1 = race_word(id1w, seed, pos);
+      const uint32_t bi0 = key_of<E>(wd0 >> 16) - theta_key, bi1 = key_of<E>(wd1 >> 16) - theta_key;
+      if (v0 && bi0 < (uint32_t)kDBins)
+        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi0]),
+                  ((unsigned long long)(2u * (r0 >> 9) + 1u) << 32) | (unsigned long long)(~id0w));
+      if (v1 && bi1 < (uint32_t)kDBins)
+        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
+                  ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
+      if (lds_publish_add(&fs.job_done, 1u) == jobs - 1u) picker = true;
     }
   }
-  lds_barrier();
-  __builtin_amdgcn_s_setprio(2);
+  lds_wait_at_least(&fs.scan_ready, 1u);
   const int32_t decision = fs.decision;
   if (decision == kNonfinite || decision == kNoSupport) {
     finish_empty_row(a, b, slot, decision == kNonfinite ? TSC_ROW_NONFINITE : TSC_ROW_NO_SUPPORT);
@@ -925,125 +953,95 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
   const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
+  const uint32_t dspan = kmax - theta_key;
   const int32_t dstar = fs.dstar;
   const uint32_t L = fs.L;
   const double lnzs = fs.lnzs;
-  // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
-  // value >= x_cut (-0 and +0 compare equal, as their keys do).
-  const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
-
-  // ---- 5. Race over the survivors and, for opt-in rows, their ordered capture ----------------
-  // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
-  // members in earlier segments (smaller ids) + its rank among this wave's members.
   const uint16_t* group_of_bin = reinterpret_cast<const uint16_t*>(lds + kOffGroupOfBin);
   const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + kOffGrpBase);
   const double* grp_s = reinterpret_cast<const double*>(lds + kOffGrpS);
   const uint32_t W = (uint32_t)a.W;
-  int32_t* out_ids = capture ? a.packed_ids + slot * a.W : nullptr;
-  float* out_lp = (capture && a.logprobs) ? a.logprobs + slot * a.W : nullptr;
   const float invT = 1.0f / T;
-  float b1 = -__builtin_inff(), b2 = -__builtin_inff();  // lane's best two float32 scores
-  int32_t b1_id = 0x7FFFFFFF;
-  float b1_x = 0.0f;
-  for (uint32_t i = lane; i < ncand; i += kWaveSize) {
-    const uint32_t wd = cand[i];
-    const float x = __uint_as_float(wd & 0xFFFF0000u);
-    if (!(x >= x_cut)) continue;
-    const uint32_t id = id0 + (wd & 0x3FFFu);
-    const float sc = (x - m) * invT + noise[i];
-    if (sc > b1) {
-      b2 = b1;
-      b1 = sc;
-      b1_id = (int32_t)id;
-      b1_x = x;
-    } else if (sc > b2) {
-      b2 = sc;
+
+  // ---- 5. The pick (one wave) and, for opt-in rows, the ordered capture (every wave) ----------
+  if (picker) {
+    __builtin_amdgcn_s_setprio(3);
+    // The support is bins d = 0..d*; bin d holds key kmax - d at index dspan - d. Float32 scores
+    // first; bins within kRaceMargin of the best are rescored in float64, ties -> lowest id.
+    float b1 = -__builtin_inff(), b2 = -__builtin_inff();
+    uint32_t p1 = 0u, d1 = 0u;  // best bin's ~id and d
+    for (uint32_t d = lane; d <= (uint32_t)dstar; d += kWaveSize) {
+      const uint64_t pk = binbest[dspan - d];
+      if (pk == 0ull) continue;
+      const float x = E::to_float(bits_of_key<E>(kmax - d));
+      const float sc = (x - m) * invT + race_noise((float)(uint32_t)(pk >> 32) * 0x1p-24f);
+      if (sc > b1) {
+        b2 = b1;
+        b1 = sc;
+        p1 = (uint32_t)pk;
+        d1 = d;
+      } else if (sc > b2) {
+        b2 = sc;
+      }
     }
-    if (capture) {
+    const float t1 = wave_reduce(b1, [](float x, float y) { return x > y ? x : y; });
+    const uint32_t src = (uint32_t)__builtin_ctzll(__ballot(b1 == t1));
+    const float t2 = wave_reduce(lane == src ? b2 : b1, [](float x, float y) { return x > y ? x : y; });
+    int32_t token = (int32_t)~read_lane(p1, (int)src);
+    uint32_t td = read_lane(d1, (int)src);
+    if (!(t1 - t2 > kRaceMargin)) {
+      double bs = -__builtin_inf();
+      int32_t bid = 0x7FFFFFFF;
+      uint32_t bd = 0u;
+      for (uint32_t d = lane; d <= (uint32_t)dstar; d += kWaveSize) {
+        const uint64_t pk = binbest[dspan - d];
+        if (pk == 0ull) continue;
+        const float x = E::to_float(bits_of_key<E>(kmax - d));
+        const float u32f = (float)(uint32_t)(pk >> 32) * 0x1p-24f;
+        if ((x - m) * invT + race_noise(u32f) < t1 - kRaceMargin) continue;
+        const double sv = ((double)x - (double)m) / (double)T;
+        const double sc = sv - log(-log((double)(uint32_t)(pk >> 32) * 0x1p-24));
+        const int32_t id = (int32_t)~(uint32_t)pk;
+        if (sc > bs || (sc == bs && id < bid)) {
+          bs = sc;
+          bid = id;
+          bd = d;
+        }
+      }
+      const double wt = wave_reduce(bs, [](double x, double y) { return x > y ? x : y; });
+      token = wave_reduce(bs == wt ? bid : 0x7FFFFFFF, [](int32_t x, int32_t y) { return x < y ? x : y; });
+      td = wave_reduce(bs == wt && bid == token ? bd : 0u, MaxU32());
+    }
+    if (lane == 0) {
+      a.tokens[b] = token;
+      a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
+      if (capture) {
+        a.lengths[slot] = (int32_t)(L < W ? L : W);
+        a.selected_logprob[slot] = (float)(grp_s[group_of_bin[dspan - td]] - lnzs);
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(1);
+  if (capture) {
+    // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
+    // members in earlier segments (smaller ids) + its rank among this wave's members.
+    lds_wait_at_least(&fs.prefix_done, 4u);
+    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
+    // value >= x_cut (-0 and +0 compare equal, as their keys do).
+    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
+    int32_t* out_ids = a.packed_ids + slot * a.W;
+    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+    for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
+      const uint32_t wd = cand[i];
+      const float x = __uint_as_float(wd & 0xFFFF0000u);
+      if (!(x >= x_cut)) continue;
       const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
       const uint32_t g = group_of_bin[bi];
       const uint32_t at = grp_base[g] + bincnt[bi] + rankw[i];
       if (at < W) {
-        out_ids[at] = (int32_t)id;
+        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
         if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
       }
-    }
-  }
-  {
-    const float wb1 = wave_reduce(b1, [](float x, float y) { return x > y ? x : y; });
-    const uint64_t at_max = __ballot(b1 == wb1);
-    const uint32_t src = (uint32_t)__builtin_ctzll(at_max);
-    const float l2 = lane == src ? b2 : b1;  // the best lane's second, or other lanes' best
-    const float wb2 = wave_reduce(l2, [](float x, float y) { return x > y ? x : y; });
-    if (lane == src) {
-      fs.race_b1[wid] = wb1;
-      fs.race_b2[wid] = wb2;
-      fs.race_id[wid] = b1_id;
-      fs.race_x[wid] = b1_x;
-    }
-  }
-  lds_barrier();
-  // Winner over the waves, lane-parallel: lane l looks at wave l % 16.
-  int32_t token;
-  float token_x;
-  float t1, t2;
-  {
-    const uint32_t w = lane & (kWaves - 1);
-    const float x1 = fs.race_b1[w], x2 = fs.race_b2[w];
-    t1 = row16_reduce(x1, [](float x, float y) { return x > y ? x : y; });
-    const uint32_t win = (uint32_t)__builtin_ctzll(__ballot(x1 == t1));  // the first such wave
-    t2 = row16_reduce(w == win ? x2 : x1, [](float x, float y) { return x > y ? x : y; });
-    token = fs.race_id[win];
-    token_x = fs.race_x[win];
-  }
-  if (!(t1 - t2 > kRaceMargin)) {
-    // Near tie in float32: rescore every survivor within the margin in float64, ties -> lowest id.
-    double bs = -__builtin_inf();
-    int32_t bid = 0x7FFFFFFF;
-    float bx = 0.0f;
-    for (uint32_t i = lane; i < ncand; i += kWaveSize) {
-      const uint32_t wd = cand[i];
-      const float x = __uint_as_float(wd & 0xFFFF0000u);
-      if (!(x >= x_cut)) continue;
-      if ((x - m) * invT + noise[i] < t1 - kRaceMargin) continue;
-      const int32_t id = (int32_t)(id0 + (wd & 0x3FFFu));
-      const double sv = ((double)x - (double)m) / (double)T;
-      const double sc = sv - log(-log(race_uniform((uint32_t)id, seed, pos)));
-      if (sc > bs || (sc == bs && id < bid)) {
-        bs = sc;
-        bid = id;
-        bx = x;
-      }
-    }
-    const double wt = wave_reduce(bs, [](double x, double y) { return x > y ? x : y; });
-    const int32_t wi = wave_reduce(bs == wt ? bid : 0x7FFFFFFF,
-                                   [](int32_t x, int32_t y) { return x < y ? x : y; });
-    if (bs == wt && bid == wi) {  // one lane, or every lane when the wave has no candidate
-      fs.ref_top[wid] = wt;
-      fs.ref_id[wid] = wi;
-      fs.ref_x[wid] = bx;
-    }
-    lds_barrier();
-    double top = -__builtin_inf();
-    token = 0x7FFFFFFF;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const double t = fs.ref_top[w];
-      const int32_t i = fs.ref_id[w];
-      if (t > top || (t == top && i < token)) {
-        top = t;
-        token = i;
-        token_x = fs.ref_x[w];
-      }
-    }
-  }
-  if (tid == 0) {
-    a.tokens[b] = token;
-    a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
-    if (capture) {
-      a.lengths[slot] = (int32_t)(L < W ? L : W);
-      const uint32_t tbi = key_of<E>(__float_as_uint(token_x) >> 16) - theta_key;
-      a.selected_logprob[slot] = (float)(grp_s[group_of_bin[tbi]] - lnzs);
     }
   }
   return true;
