@@ -85,6 +85,7 @@ struct FastShared {
   uint32_t kmax0_w[kWaves];
   uint32_t ndone;              // waves whose stream has ended
   uint32_t scan_ready;          // set by wave 0 once the decision and the bin scan are published
+  // Counters in steps of 64 (one per wave):
   uint32_t prefix_done;         // waves that finished their share of the capture offsets
   uint32_t job_next;            // next race-draw job to claim
   uint32_t job_done;            // race-draw jobs completed
@@ -173,20 +174,29 @@ __device__ inline float race_noise(float u) {
   return -__builtin_amdgcn_logf(e) * 0.6931471805599453f;
 }
 
-// Flags between the waves of one workgroup, in LDS. A publish orders every earlier LDS write of
-// the wave before the flag (release at workgroup scope); a wait spins with s_sleep until the flag
-// reaches a value, then orders the wave's later LDS reads after it. Every flag a wave waits on is
-// published unconditionally by waves that never wait on it, so every wait ends.
+// Flags and counters between the waves of one workgroup, in LDS. A publish orders every earlier
+// LDS write of the wave before the flag (release at workgroup scope); a wait spins with s_sleep
+// until the flag reaches a value, then orders the wave's later LDS reads after it. Every flag a
+// wave waits on is published unconditionally by waves that never wait on it, so every wait ends.
+// Counters move in steps of 64: every lane of the wave (always fully active here) adds 1, so
+// that no branch on the lane surrounds the atomic (such a branch inside a claim loop has been
+// compiled into a loop exit that only lane 0 takes) and the compiler can fold the 64 adds into
+// one. Lane 0's previous value, divided by 64, is the number of earlier steps either way.
+constexpr uint32_t kStep = kWaveSize;
 __device__ inline void lds_publish(uint32_t* flag, uint32_t v) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  if (lane_id() == 0) __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Adds to a counter after every earlier LDS write of the wave; returns the previous value.
-__device__ inline uint32_t lds_publish_add(uint32_t* ctr, uint32_t v) {
+// One step on a counter after every earlier LDS write of the wave; returns the earlier steps.
+__device__ inline uint32_t lds_publish_step(uint32_t* ctr) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  uint32_t old = 0u;
-  if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return read_lane(old, 0);
+  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return read_lane(old, 0) / kStep;
+}
+// Claims the next index of a work counter for the whole wave.
+__device__ inline uint32_t lds_claim(uint32_t* ctr) {
+  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return read_lane(old, 0) / kStep;
 }
 __device__ inline void lds_wait_at_least(const uint32_t* flag, uint32_t v) {
   while (uniform_u32(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v)
@@ -911,14 +921,12 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           acc += v[w];
         }
       }
-      lds_publish_add(&fs.prefix_done, 1u);
+      lds_publish_step(&fs.prefix_done);
     }
     const uint32_t cwv = cw;
     const uint32_t* cand_all = reinterpret_cast<const uint32_t*>(lds + kOffCand);
     for (;;) {
-      uint32_t q = 0u;
-      if (lane == 0) q = atomicAdd(&fs.job_next, 1u);
-      q = read_lane(q, 0);
+      const uint32_t q = lds_claim(&fs.job_next);
       if (q >= jobs) break;
       const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
       const uint32_t c0 = read_lane(incl - njobs, (int)ww);
@@ -939,7 +947,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (v1 && bi1 < (uint32_t)kDBins)
         atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
                   ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
-      if (lds_publish_add(&fs.job_done, 1u) == jobs - 1u) picker = true;
+      if (lds_publish_step(&fs.job_done) == jobs - 1u) picker = true;
     }
   }
   lds_wait_at_least(&fs.scan_ready, 1u);
@@ -1025,7 +1033,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   if (capture) {
     // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
     // members in earlier segments (smaller ids) + its rank among this wave's members.
-    lds_wait_at_least(&fs.prefix_done, 4u);
+    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
     // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
     // value >= x_cut (-0 and +0 compare equal, as their keys do).
     const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
