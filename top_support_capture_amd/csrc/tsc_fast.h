@@ -22,10 +22,10 @@
 //      (checked here). Meanwhile the other waves draw every candidate's race uniform
 //      (Philox4x32-10, in jobs claimed from an LDS counter) and keep per bin the largest one
 //      (all candidates of a bin share their logit, so that one is the bin's best race score).
-//   5. The wave that completes the last draw picks the token over the support's bins (float32
-//      scores, float64 for the few within 1e-4 of the best); every wave writes the ordered
-//      capture of its own candidates: the bin scan gives each tie group's base position, the
-//      ranks and a prefix over the waves the rest. Waves wait on LDS flags, not barriers.
+//   5. Every wave writes the ordered capture of its own candidates: the bin scan gives each tie
+//      group's base position, the ranks and a prefix over the waves the rest. Once every draw
+//      is done, wave 0 picks the token over the support's bins (float32 scores, float64 for the
+//      few within 1e-4 of the best). Waves wait on LDS flags, not barriers.
 // Any row this path cannot serve exactly (capacities, theta above the k-th value, overflow of
 // the mass, greedy rows, other dtypes or layouts) runs through general_row in the same workgroup.
 #pragma once
@@ -856,7 +856,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t njobs = (nw + kJob - 1) / kJob;
   const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
   const uint32_t jobs = read_lane(incl, kWaves - 1);
-  bool picker = wid == 0 && jobs == 0u;
   if (wid == 0) {
     __builtin_amdgcn_s_setprio(3);
     const uint32_t w = lane & (kWaves - 1);
@@ -947,7 +946,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (v1 && bi1 < (uint32_t)kDBins)
         atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
                   ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
-      if (lds_publish_step(&fs.job_done) == jobs - 1u) picker = true;
+      lds_publish_step(&fs.job_done);
     }
   }
   lds_wait_at_least(&fs.scan_ready, 1u);
@@ -971,8 +970,33 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t W = (uint32_t)a.W;
   const float invT = 1.0f / T;
 
-  // ---- 5. The pick (one wave) and, for opt-in rows, the ordered capture (every wave) ----------
-  if (picker) {
+  // ---- 5. The ordered capture of each wave's own candidates (opt-in rows), then the pick ------
+  __builtin_amdgcn_s_setprio(1);
+  if (capture) {
+    // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
+    // members in earlier segments (smaller ids) + its rank among this wave's members.
+    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
+    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
+    // value >= x_cut (-0 and +0 compare equal, as their keys do).
+    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
+    int32_t* out_ids = a.packed_ids + slot * a.W;
+    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+    for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
+      const uint32_t wd = cand[i];
+      const float x = __uint_as_float(wd & 0xFFFF0000u);
+      if (!(x >= x_cut)) continue;
+      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+      const uint32_t g = group_of_bin[bi];
+      const uint32_t at = grp_base[g] + bincnt[bi] + rankw[i];
+      if (at < W) {
+        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
+        if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
+      }
+    }
+  }
+  // The pick: wave 0, once every race draw is done (it has the row's scalars at hand).
+  if (wid == 0) {
+    lds_wait_at_least(&fs.job_done, jobs * kStep);
     __builtin_amdgcn_s_setprio(3);
     // The support is bins d = 0..d*; bin d holds key kmax - d at index dspan - d. Float32 scores
     // first; bins within kRaceMargin of the best are rescored in float64, ties -> lowest id.
@@ -1026,29 +1050,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (capture) {
         a.lengths[slot] = (int32_t)(L < W ? L : W);
         a.selected_logprob[slot] = (float)(grp_s[group_of_bin[dspan - td]] - lnzs);
-      }
-    }
-  }
-  __builtin_amdgcn_s_setprio(1);
-  if (capture) {
-    // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
-    // members in earlier segments (smaller ids) + its rank among this wave's members.
-    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
-    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
-    // value >= x_cut (-0 and +0 compare equal, as their keys do).
-    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
-    int32_t* out_ids = a.packed_ids + slot * a.W;
-    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
-    for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
-      const uint32_t wd = cand[i];
-      const float x = __uint_as_float(wd & 0xFFFF0000u);
-      if (!(x >= x_cut)) continue;
-      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-      const uint32_t g = group_of_bin[bi];
-      const uint32_t at = grp_base[g] + bincnt[bi] + rankw[i];
-      if (at < W) {
-        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
-        if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
       }
     }
   }
