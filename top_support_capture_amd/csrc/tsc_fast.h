@@ -46,7 +46,11 @@ constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
 constexpr int32_t kFastMaxK = 1536;
 constexpr int kFixShift = 48;         // fixed-point weights: 2^48 * w, candidates <= 8192
-constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
+constexpr float kRaceMargin = 1e-4f;
+// Waves whose stream ends among the first kOwnDraws draw the race uniforms of their own
+// candidates before the exchange (while the last streams and their post-stream work finish).
+constexpr uint32_t kOwnDraws = 4;
+constexpr bool kOwnDrawsStop = false;  // stop once every stream has ended  // float32 race scores are within ~3e-6 of exact
 
 // LDS layout of the fast path (bytes from the dynamic buffer base).
 constexpr int kOffStash = 0;                                          // uint4 [16][256]
@@ -90,6 +94,7 @@ struct FastShared {
   uint32_t job_next;            // next race-draw job to claim
   uint32_t job_done;            // race-draw jobs completed
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
+  uint32_t noise_done[kWaves];  // candidates whose race draws the wave made itself (from the first)
   int32_t slot_wmax[kWaves];
   int32_t slot_hit[kWaves];
   float wave_m[kWaves];
@@ -837,8 +842,35 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   }
+  // Race draws of this wave's own candidates, 128 at a time (two Philox chains per lane); the
+  // helper waves draw the rest after the exchange. Each candidate's uniform is kept per bin as
+  // max(u numerator << 32 | ~id) (see the pick).
+  uint32_t nz = 0;
+  if (order < kOwnDraws) {
+    for (uint32_t base = 0; base < nc_here; base += 2u * kWaveSize) {
+      if (kOwnDrawsStop &&
+          uniform_u32(__hip_atomic_load(&fs.ndone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >=
+              (uint32_t)kWaves)
+        break;
+      const uint32_t i0 = base + lane, i1 = i0 + kWaveSize;
+      const bool v0 = i0 < nc_here, v1 = i1 < nc_here;
+      const uint32_t wd0 = v0 ? cand[i0] : 0u, wd1 = v1 ? cand[i1] : 0u;
+      const uint32_t id0w = id0 + (wd0 & 0x3FFFu), id1w = id0 + (wd1 & 0x3FFFu);
+      const uint32_t r0 = race_word(id0w, seed, pos);
+      const uint32_t r1 = race_word(id1w, seed, pos);
+      const uint32_t bi0 = key_of<E>(wd0 >> 16) - theta_key, bi1 = key_of<E>(wd1 >> 16) - theta_key;
+      if (v0 && bi0 < (uint32_t)kDBins)
+        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi0]),
+                  ((unsigned long long)(2u * (r0 >> 9) + 1u) << 32) | (unsigned long long)(~id0w));
+      if (v1 && bi1 < (uint32_t)kDBins)
+        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
+                  ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
+      nz = base + 2u * kWaveSize < nc_here ? base + 2u * kWaveSize : nc_here;
+    }
+  }
   if (lane == 0) {
     fs.wave_cand[wid] = ncand;
+    fs.noise_done[wid] = nz;
     fs.bin_hi[wid] = wxc > -__builtin_inff() ? bmax + 1u : 0u;
   }
   lds_barrier();
@@ -853,7 +885,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t l16 = lane & (kWaves - 1);
   const uint32_t nw0 = fs.wave_cand[l16];
   const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
-  const uint32_t njobs = (nw + kJob - 1) / kJob;
+  const uint32_t first = fs.noise_done[l16];  // drawn already: a multiple of 128, or all
+  const uint32_t njobs = (nw - first + kJob - 1) / kJob;
   const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
   const uint32_t jobs = read_lane(incl, kWaves - 1);
   if (wid == 0) {
@@ -930,7 +963,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       const uint32_t ww = (uint32_t)__popcll(__ballot(lane < (uint32_t)kWaves && incl <= q));
       const uint32_t c0 = read_lane(incl - njobs, (int)ww);
       const uint32_t nww = read_lane(nw, (int)ww);
-      const uint32_t i0 = (q - c0) * kJob + lane;
+      const uint32_t i0 = read_lane(first, (int)ww) + (q - c0) * kJob + lane;
       const uint32_t i1 = i0 + kWaveSize;
       const bool v0 = i0 < nww, v1 = i1 < nww;
       const uint32_t wd0 = v0 ? cand_all[ww * kCandPerWave + i0] : 0u;
@@ -971,7 +1004,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const float invT = 1.0f / T;
 
   // ---- 5. The ordered capture of each wave's own candidates (opt-in rows), then the pick ------
-  __builtin_amdgcn_s_setprio(1);
+  if (wid == 0) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(1);
   if (capture) {
     // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
     // members in earlier segments (smaller ids) + its rank among this wave's members.
