@@ -136,8 +136,10 @@ def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # About 45 ms of untimed calls: long enough for the GPU clocks to reach their sustained level
+    # (20 warmup calls leave the timed region ~6% slower than the steady state).
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
