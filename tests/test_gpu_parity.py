@@ -289,6 +289,16 @@ FAST_PARAMS = [
     ("wide_span_minp", "wide", 12.0, 1024, 1.0, 0.01),
     ("tiny_T", "gauss", 1e-3, 50, 0.9, 0.0),
     ("greedy", "grid", 0.0, 50, 0.9, 0.0),
+    # top_k above 1536: the compaction mode of the single-read path
+    ("compact_k4000_p9", "gauss", 1.0, 4000, 0.9, 0.0),
+    ("compact_k8192_p1", "gauss", 1.0, 8192, 1.0, 0.0),
+    ("compact_grid_k2000", "grid", 0.8, 2000, 0.95, 0.0),
+    ("compact_minp", "gauss", 1.0, 3000, 1.0, 0.05),
+    ("compact_minp_p", "wide", 12.0, 2500, 0.97, 0.01),
+    ("compact_nan", "nan", 1.0, 2000, 0.9, 0.0),
+    ("compact_pinf", "pinf", 1.0, 2000, 1.0, 0.0),
+    ("compact_neg_inf", "neg", 1.0, 3000, 0.9, 0.0),
+    ("compact_hidden_top", "hidden", 1.0, 4096, 0.95, 0.0),
 ]
 
 

@@ -37,47 +37,73 @@ namespace tsc {
 constexpr int kFastLoads = 20;        // 16-byte loads per lane (segment of at most 20 * 512 values)
 constexpr int kLoadsFirst = 2;        // loads issued before the first one is awaited
 constexpr int kLoadsAhead = 4;        // software pipeline depth afterwards (loads in flight per lane)
-constexpr int kStashPerWave = 256;    // stashed loads per wave
-constexpr int kCandPerWave = 512;     // candidate words per wave
+constexpr int kStashPerWave = 256;    // stashed loads per wave (stash mode)
 constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
 constexpr int kMaxGroups = 256;       // distinct keys in a captured support
 constexpr int kThetaBins = 256;       // key distances of the sampled maxima below their maximum
+constexpr int kMaskBins = 256;        // bins with a 64-bit lane mask in the ranking tables
 constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
-constexpr int32_t kFastMaxK = 1536;
-constexpr int kFixShift = 48;         // fixed-point weights: 2^48 * w, candidates <= 8192
-constexpr float kRaceMargin = 1e-4f;
+constexpr int32_t kFastMaxK = 1536;   // stash mode; compaction mode above it
+constexpr int32_t kCompactMaxK = 8192;
+constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
 // Waves whose stream ends among the first kOwnDraws draw the race uniforms of their own
 // candidates before the exchange (while the last streams and their post-stream work finish).
 constexpr uint32_t kOwnDraws = 4;
-constexpr bool kOwnDrawsStop = false;  // stop once every stream has ended  // float32 race scores are within ~3e-6 of exact
 
-// LDS layout of the fast path (bytes from the dynamic buffer base).
-constexpr int kOffStash = 0;                                          // uint4 [16][256]
-constexpr int kOffStashCh = kOffStash + kWaves * kStashPerWave * 16;  // u32 [16][256]
-constexpr int kOffCand = kOffStashCh + kWaves * kStashPerWave * 4;    // u32 [16][512]
-constexpr int kOffBinBest = kOffCand + kWaves * kCandPerWave * 4;     // u64 [1024] race per bin
-constexpr int kOffDummy = kOffBinBest + kDBins * 8;                   // u32 [64] scatter sink
-constexpr int kOffCnt = kOffDummy + kWaveSize * 4;                    // u32 [1024] by key - theta
-constexpr int kOffGroupOfBin = kOffCnt + kDBins * 4;                // u16 [1024] group by bin
-constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;              // u32 [256]
-constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;                // f64 [256] (x - m) / T
-constexpr int kFastLdsEnd = kOffGrpS + kMaxGroups * 8;
-// Reuse of a wave's stash slices once the wave has expanded them: its count per bin
-// bi = key - theta_key (u16; later the exclusive prefix over earlier waves), 64-bit lane masks
-// for the first 256 bins (the ranking of one chunk), and each of its candidates' rank among its
-// earlier candidates of the same bin (u16).
-constexpr int kMaskBins = 256;
-constexpr int kOffBinCnt = kOffStash;                                 // u16 [1024], 4 KB apart
-constexpr int kOffBinMask = kOffStash + kDBins * 2;                   // u64 [256], per wave
-constexpr int kOffRank = kOffStashCh;                                 // u16 [16][512]
-static_assert(kDBins * 2 + kMaskBins * 8 == kStashPerWave * 16, "counts and masks fill a slice");
-static_assert(kCandPerWave * 2 <= kStashPerWave * 4, "a wave's ranks fit its chunk slice");
+// Two modes share everything but the way candidates are gathered during the stream:
+//   stash mode (top_k <= 1536): a load that may hold a value >= theta is stashed whole in LDS
+//     (one ballot per load) and expanded into candidates once the wave's stream has ended;
+//   compaction mode (1536 < top_k <= 8192, where most loads hold candidates): the values >= theta
+//     of each load are appended to the wave's candidate list as the load lands.
+// Per-wave ranking tables: the count per bin bi = key - theta_key (u16; later the exclusive
+// prefix over earlier waves) and, in stash mode, 64-bit lane masks for the first 256 bins.
+constexpr int kTableMaskOff = kDBins * 2;
 
-constexpr size_t kFastDynLds =
-    (size_t)kGeneralDynLds + sizeof(GeneralShared) > (size_t)kFastLdsEnd
-        ? (size_t)kGeneralDynLds + sizeof(GeneralShared)
-        : (size_t)kFastLdsEnd;
+// LDS regions after the mode-specific ones (bytes from the dynamic buffer base).
+template <int kOffTail>
+struct TailLayout {
+  static constexpr int kOffBinBest = kOffTail;                            // u64 [1024] race per bin
+  static constexpr int kOffDummy = kOffBinBest + kDBins * 8;              // u32 [64] scatter sink
+  static constexpr int kOffCnt = kOffDummy + kWaveSize * 4;               // u32 [1024] by key - theta
+  static constexpr int kOffGroupOfBin = kOffCnt + kDBins * 4;             // u16 [1024] group by bin
+  static constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;         // u32 [256]
+  static constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;           // f64 [256] (x - m) / T
+  static constexpr int kEnd = kOffGrpS + kMaxGroups * 8;
+};
+// Stash mode: the stash, its chunk indices, the candidates. Once a wave has expanded its stash,
+// its stash slice holds its ranking tables and its chunk-index slice its candidates' ranks.
+constexpr int kStashBytes = kWaves * kStashPerWave * 16;
+constexpr int kStashChBytes = kWaves * kStashPerWave * 4;
+struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> {
+  static constexpr int kCandCap = 512;                      // candidate words per wave
+  static constexpr int kOffStash = 0;                       // uint4 [16][256]
+  static constexpr int kOffStashCh = kStashBytes;           // u32 [16][256]
+  static constexpr int kOffCand = kOffStashCh + kStashChBytes;  // u32 [16][512]
+  static constexpr bool kMasks = true;                      // lane masks in the tables
+  static constexpr int kTableBytes = kDBins * 2 + kMaskBins * 8;  // per wave
+  static constexpr int kOffTables = kOffStash;              // [16][4 KB]
+  static constexpr int kOffRank = kOffStashCh;              // u16 [16][512]
+};
+static_assert(LayoutStash::kTableBytes == kStashPerWave * 16, "a wave's tables fill its slice");
+static_assert(LayoutStash::kCandCap * 2 <= kStashPerWave * 4, "a wave's ranks fit its chunk slice");
+// Compaction mode: the candidates, the ranking tables (counts only: the many candidates of a bin
+// are ranked with ballots, without LDS atomics), the ranks.
+constexpr int kCompactCap = 1024;
+struct LayoutCompact
+    : TailLayout<kWaves * kCompactCap * 4 + kWaves * kDBins * 2 + kWaves * kCompactCap * 2> {
+  static constexpr int kCandCap = kCompactCap;              // candidate words per wave
+  static constexpr int kOffCand = 0;                        // u32 [16][1024]
+  static constexpr bool kMasks = false;
+  static constexpr int kTableBytes = kDBins * 2;            // per wave
+  static constexpr int kOffTables = kOffCand + kWaves * kCandCap * 4;        // [16][2 KB]
+  static constexpr int kOffRank = kOffTables + kWaves * kTableBytes;         // u16 [16][1024]
+};
+
+constexpr size_t kMaxSz(size_t x, size_t y) { return x > y ? x : y; }
+constexpr size_t kFastDynLds = kMaxSz(kMaxSz((size_t)kGeneralDynLds + sizeof(GeneralShared),
+                                             (size_t)LayoutStash::kEnd),
+                                      (size_t)LayoutCompact::kEnd);
 
 // Outcome of the status checks and the bin scan, published by wave 0.
 enum FastDecision : int32_t { kProceed = 0, kNonfinite = 1, kNoSupport = 2, kFallback = 3 };
@@ -92,7 +118,8 @@ struct FastShared {
   // Counters in steps of 64 (one per wave):
   uint32_t prefix_done;         // waves that finished their share of the capture offsets
   uint32_t job_next;            // next race-draw job to claim
-  uint32_t job_done;            // race-draw jobs completed
+  uint32_t ready;               // race-draw jobs completed
+  uint32_t cap_next;            // next wave's candidate list to capture
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
   uint32_t noise_done[kWaves];  // candidates whose race draws the wave made itself (from the first)
   int32_t slot_wmax[kWaves];
@@ -278,7 +305,7 @@ __device__ inline T row16_reduce(T v, Op op) {
 // were counted by bi = key - theta_key = dspan - d. Lane l owns the nb consecutive bins from
 // l * nb. Publishes the threshold d*, the support size, and for capture rows the tie-group tables:
 // the group of each support bin, each group's base position and (x - m) / T, and ln Z_S.
-template <bool NEED_P, int NB>
+template <bool NEED_P, int NB, class LY>
 __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
                                       const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
@@ -327,9 +354,9 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
   int32_t best = -1;
   uint32_t bL = 0, bG = 0;
   double bZ = 0.0;
-  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + kOffGroupOfBin);
-  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
-  double* grp_s = reinterpret_cast<double*>(lds + kOffGrpS);
+  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + LY::kOffGroupOfBin);
+  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + LY::kOffGrpBase);
+  double* grp_s = reinterpret_cast<double*>(lds + LY::kOffGrpS);
   const double invT = 1.0 / (double)T;
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
@@ -366,7 +393,7 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
 }
 
 // The same for spans of 256 bins and more (bins re-read per pass instead of kept in registers).
-template <bool NEED_P>
+template <bool NEED_P, class LY>
 __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
                                       const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
@@ -413,9 +440,9 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   int32_t best = -1;
   uint32_t bL = 0;
   double bZ = 0.0;
-  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + kOffGroupOfBin);
-  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + kOffGrpBase);
-  double* grp_s = reinterpret_cast<double*>(lds + kOffGrpS);
+  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + LY::kOffGroupOfBin);
+  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + LY::kOffGrpBase);
+  double* grp_s = reinterpret_cast<double*>(lds + LY::kOffGrpS);
   const double invT = 1.0 / (double)T;
   for (uint32_t t = 0; t < nb; ++t) {
     const uint32_t d = lane * nb + t;
@@ -466,12 +493,16 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 
 // Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
 // go through the general path instead; `slot` is then already set.
-template <bool NEED_P>
+template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
+template <> struct LayoutOf<true> { using type = LayoutCompact; };
+
+template <bool NEED_P, bool COMPACT>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
                                               float T, int32_t k, float p, float mp,
                                               uint64_t seed, uint64_t pos, unsigned char* lds,
                                               FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
+  using LY = typename LayoutOf<COMPACT>::type;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
   const uint16_t* row = reinterpret_cast<const uint16_t*>(a.logits) + b * a.ld;
   const uint4* rowv = reinterpret_cast<const uint4*>(row);
@@ -483,15 +514,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t nseg = seg1 - seg0;                      // chunks in this wave's segment
   const uint32_t id0 = seg0 * 8u;                         // first token id of the segment
 
-  // Rank of theta among the 1024 lane maxima of the first loads: aim for about 2k + 64 tokens
-  // above theta; a maximum of 8 values exceeds the quantile 1 - q with probability 1 - (1-q)^8.
-  // The sample is the lane maxima of the first two loads (2048 values, 16384 elements); the
-  // target of 1.6 k + 64 candidates keeps the k-th largest value above theta by about five
-  // standard deviations of the estimate.
+  // Rank of theta among the lane maxima of the first loads: a maximum of 8 values exceeds the
+  // quantile 1 - q with probability 1 - (1-q)^8. The sample is the lane maxima of the first two
+  // loads (2048 values, 16384 elements). A target of 1.6 k + 64 candidates (stash mode) or
+  // 1.2 k + 320 (compaction mode, larger k: a relatively tighter estimate) keeps the k-th
+  // largest value above theta by about five standard deviations of the estimate.
   constexpr int kSamples = 2 * kThreads;
   uint32_t theta_rank;
   {
-    const float q = fminf(1.0f, (1.6f * (float)k + 64.0f) / (float)V);
+    const float target = COMPACT ? 1.2f * (float)k + 320.0f : 1.6f * (float)k + 64.0f;
+    const float q = fminf(1.0f, target / (float)V);
     const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
     const float pr = 1.0f - t4 * t4;
     const int rr = (int)ceilf(pr * (float)kSamples);
@@ -527,7 +559,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + kOffCnt);
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + LY::kOffCnt);
   hcnt[tid] = 0u;  // published by the first exchange below
   if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
   if (tid == 0) {
@@ -535,9 +567,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     fs.scan_ready = 0u;
     fs.prefix_done = 0u;
     fs.job_next = 0u;
-    fs.job_done = 0u;
+    fs.ready = 0u;
+    fs.cap_next = 0u;
   }
-  reinterpret_cast<uint64_t*>(lds + kOffBinBest)[tid] = 0ull;
+  reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest)[tid] = 0ull;
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
   const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
@@ -575,11 +608,45 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   };
-  uint32_t wcnt = 0;   // wave's flagged loads (wave-uniform)
+  uint32_t wcnt = 0;   // wave's flagged loads, or its candidates (compaction; wave-uniform)
   uint32_t wfill = 0;  // stash slots written: wcnt until a load no longer fits
-  uint4* stash = reinterpret_cast<uint4*>(lds + kOffStash) + wid * kStashPerWave;
-  uint32_t* stash_ch = reinterpret_cast<uint32_t*>(lds + kOffStashCh) + wid * kStashPerWave;
+  uint4* stash = reinterpret_cast<uint4*>(lds + LayoutStash::kOffStash) + wid * kStashPerWave;
+  uint32_t* stash_ch =
+      reinterpret_cast<uint32_t*>(lds + LayoutStash::kOffStashCh) + wid * kStashPerWave;
   float theta = __builtin_inff();
+  // Compaction: the load's values >= theta are appended to the wave's list in id order (lane
+  // counts, one DPP scan for the slots); a wave-load without any is skipped. Candidates past
+  // the capacity are counted, not written, and the row falls back.
+  auto compact_load = [&](int j, const uint4& q) {
+    // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14). Elements
+    // that are not candidates go to a dummy slot of this lane (branch-free scatter).
+    uint32_t* cand = reinterpret_cast<uint32_t*>(lds + LY::kOffCand) + wid * LY::kCandCap;
+    uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + LY::kOffDummy) + lane;
+    // theta is finite whenever the row can be served here; clamping it keeps -inf out.
+    const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t off = ((uint32_t)j * kWaveSize + lane) * 8u;
+    uint32_t words[8];
+    bool isc[8];
+    uint32_t n = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+      isc[e] = __uint_as_float(hi) >= th;  // -0 ties +0; NaN fails
+      words[e] = hi | (off + (uint32_t)e);
+      n += isc[e];
+    }
+    if (__ballot(n != 0u) == 0ull) return;
+    uint32_t total;
+    uint32_t at = wcnt + wave_excl_sum(n, total);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t* dst = (isc[e] && at < (uint32_t)LY::kCandCap) ? cand + at : dummy;
+      *dst = words[e];
+      at += isc[e];
+    }
+    wcnt += total;
+  };
   auto stash_load = [&](int j, const uint4& q, bool flag) {
     const uint64_t mask = __ballot(flag);
     const uint32_t n = (uint32_t)__popcll(mask);
@@ -684,9 +751,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
-  stash_load(0, r[0], lm0 >= theta);
-  stash_load(1, r[1], lm1 >= theta);
-  stash_load(2, r[2], lm2 >= theta);
+  if constexpr (COMPACT) {
+    compact_load(0, r[0]);
+    compact_load(1, r[1]);
+    compact_load(2, r[2]);
+  } else {
+    stash_load(0, r[0], lm0 >= theta);
+    stash_load(1, r[1], lm1 >= theta);
+    stash_load(2, r[2], lm2 >= theta);
+  }
   // From here on, for top_p < 1, a load is stashed when the sum of its weights reaches the
   // weight of theta (any element >= theta implies it; the small slack covers exp2 rounding), so
   // the load's maximum is not needed: the row maximum is the largest candidate, and a NaN logit
@@ -707,13 +780,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       const float ls = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       if (j & 1) s_b += ls; else s_a += ls;
       flag = ls >= wth;
-    } else {
+    }
+    if constexpr (!NEED_P || COMPACT) {
       const float lm = load_max(f);
       m_l = maximum2f(m_l, lm);
-      flag = lm >= theta;
+      if constexpr (!NEED_P) flag = lm >= theta;
     }
     pin();
-    stash_load(j, r[j], flag);
+    if constexpr (COMPACT) compact_load(j, r[j]);
+    else stash_load(j, r[j], flag);
   }
 
   // ---- 3. Per wave, as soon as its segment is done: partials, expansion, counts ---------------
@@ -731,21 +806,23 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
     if (lane == 0) {
       fs.wave_z[wid] = wz;
-      fs.wave_stash[wid] = wcnt;
+      fs.wave_stash[wid] = COMPACT ? 0u : wcnt;
     }
   }
   // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
-  uint32_t* cand = reinterpret_cast<uint32_t*>(lds + kOffCand) + wid * kCandPerWave;
-  uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + kOffBinBest);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(lds + LY::kOffCand) + wid * LY::kCandCap;
+  uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest);
+  // theta is finite whenever the row can be served here; clamping it keeps -inf out.
+  const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
   uint32_t ncand = 0;            // wave-uniform
   float xcand = -__builtin_inff();  // lane maximum of the candidates
-  {
+  if constexpr (COMPACT) {
+    ncand = wcnt;
+    xcand = m_l >= th ? m_l : -__builtin_inff();  // the lane maximum is a candidate iff >= theta
+  } else {
+    // Stash expansion: candidate words of the stashed loads, in id order.
+    uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + LY::kOffDummy) + lane;
     const uint32_t nstash = wfill;  // never slots that were not written in this row
-    // theta is finite whenever the row can be served here; clamping it keeps -inf out.
-    const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
-    // Elements that are not candidates are written to a dummy slot of this lane, which keeps
-    // the scatter free of branches.
-    uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + kOffDummy) + lane;
     // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
     constexpr int kChunks = kStashPerWave / kWaveSize;
     uint4 qs[kChunks];
@@ -783,21 +860,21 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       uint32_t at = ncand + wave_excl_sum(n, total);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t* dst = (isc[e] && at < (uint32_t)kCandPerWave) ? cand + at : dummy;
+        uint32_t* dst = (isc[e] && at < (uint32_t)LY::kCandCap) ? cand + at : dummy;
         *dst = words[e];
         at += isc[e];
       }
       ncand += total;
     }
   }
-  // The stash slices of this wave are free now: its count per bin, the bin masks of the
-  // ranking, and its candidates' ranks.
-  uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + kOffBinCnt + wid * kStashPerWave * 16);
-  uint64_t* binmask = reinterpret_cast<uint64_t*>(lds + kOffBinMask + wid * kStashPerWave * 16);
-  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + kOffRank) + wid * kCandPerWave;
-  for (uint32_t i = lane; i < (uint32_t)(kStashPerWave * 16) / 16; i += kWaveSize)
+  // The wave's ranking tables (in stash mode its stash slice, free now) and its candidates' ranks.
+  uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + LY::kOffTables + wid * LY::kTableBytes);
+  uint64_t* binmask =
+      reinterpret_cast<uint64_t*>(lds + LY::kOffTables + wid * LY::kTableBytes + kTableMaskOff);
+  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + LY::kOffRank) + wid * LY::kCandCap;
+  for (uint32_t i = lane; i < (uint32_t)LY::kTableBytes / 16; i += kWaveSize)
     reinterpret_cast<uint4*>(bincnt)[i] = make_uint4(0u, 0u, 0u, 0u);
-  const uint32_t nc_here = ncand < (uint32_t)kCandPerWave ? ncand : (uint32_t)kCandPerWave;
+  const uint32_t nc_here = ncand < (uint32_t)LY::kCandCap ? ncand : (uint32_t)LY::kCandCap;
   // Maximum: for top_p < 1 the largest candidate (the row maximum is >= theta, so it is one);
   // otherwise the running maximum of the stream (which also carries NaN).
   const float wxc = wave_reduce(xcand, MaximumF32());
@@ -807,7 +884,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (lane == 0) fs.wave_m[wid] = wm;
   }
   const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
-  const bool by_mask = bmax < (uint32_t)kMaskBins;
+  const bool by_mask = LY::kMasks && bmax < (uint32_t)kMaskBins;
   // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
   // earlier chunks (this wave's own table, so plain reads and writes) plus the lanes of its bin
   // below it in this chunk. Those lanes come from a 64-bit mask per bin that every lane ORs its
@@ -848,10 +925,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   uint32_t nz = 0;
   if (order < kOwnDraws) {
     for (uint32_t base = 0; base < nc_here; base += 2u * kWaveSize) {
-      if (kOwnDrawsStop &&
-          uniform_u32(__hip_atomic_load(&fs.ndone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >=
-              (uint32_t)kWaves)
-        break;
       const uint32_t i0 = base + lane, i1 = i0 + kWaveSize;
       const bool v0 = i0 < nc_here, v1 = i1 < nc_here;
       const uint32_t wd0 = v0 ? cand[i0] : 0u, wd1 = v1 ? cand[i1] : 0u;
@@ -884,18 +957,19 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   constexpr uint32_t kJob = 2 * kWaveSize;
   const uint32_t l16 = lane & (kWaves - 1);
   const uint32_t nw0 = fs.wave_cand[l16];
-  const uint32_t nw = nw0 < (uint32_t)kCandPerWave ? nw0 : (uint32_t)kCandPerWave;
+  const uint32_t nw = nw0 < (uint32_t)LY::kCandCap ? nw0 : (uint32_t)LY::kCandCap;
   const uint32_t first = fs.noise_done[l16];  // drawn already: a multiple of 128, or all
   const uint32_t njobs = (nw - first + kJob - 1) / kJob;
   const uint32_t incl = wave_incl_scan(lane < (uint32_t)kWaves ? njobs : 0u, SumU32(), 0u);
   const uint32_t jobs = read_lane(incl, kWaves - 1);
+  bool picker = false;
   if (wid == 0) {
     __builtin_amdgcn_s_setprio(3);
     const uint32_t w = lane & (kWaves - 1);
     const float m = row16_reduce(fs.wave_m[w], MaximumF32());
     const uint32_t ntot = row16_reduce(fs.wave_cand[w], SumU32());
     const bool over = __ballot(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
-                               fs.wave_cand[w] > (uint32_t)kCandPerWave) != 0;
+                               fs.wave_cand[w] > (uint32_t)LY::kCandCap) != 0;
     // A NaN logit: in the running maximum when top_p = 1, in the mass when top_p < 1.
     double zr = 0.0;
     if constexpr (NEED_P) zr = row16_reduce(fs.wave_z[w], SumF64());
@@ -923,21 +997,24 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (decision == kProceed) {
         const uint32_t dspan = kmax - theta_key;
         if (dspan < 4u * kWaveSize)
-          bin_scan_wave0<NEED_P, 4>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+          bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         else
-          bin_scan_wave0_wide<NEED_P>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+          bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
       }
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
     lds_publish(&fs.scan_ready, 1u);
+    // Wave 0 picks the token once every race draw is done (it has the row's scalars at hand).
+    lds_wait_at_least(&fs.ready, jobs * kStep);
+    picker = true;
   } else {
     __builtin_amdgcn_s_setprio(2);
     if (capture && wid <= 4u) {
       // Exclusive prefix of every bin's count over the waves: wave w's first capture offset in
       // each tie group, relative to the group's base (waves 1-4; the other helpers start on the
       // race draws at once).
-      uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + kOffBinCnt);
-      constexpr int kStride = kStashPerWave * 16 / 2;  // u16 between two waves' tables
+      uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + LY::kOffTables);
+      constexpr int kStride = LY::kTableBytes / 2;  // u16 between two waves' tables
       uint32_t nbins = 0;  // bins any wave used
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) nbins = nbins > fs.bin_hi[w] ? nbins : fs.bin_hi[w];
@@ -956,7 +1033,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       lds_publish_step(&fs.prefix_done);
     }
     const uint32_t cwv = cw;
-    const uint32_t* cand_all = reinterpret_cast<const uint32_t*>(lds + kOffCand);
+    const uint32_t* cand_all = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand);
     for (;;) {
       const uint32_t q = lds_claim(&fs.job_next);
       if (q >= jobs) break;
@@ -966,8 +1043,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       const uint32_t i0 = read_lane(first, (int)ww) + (q - c0) * kJob + lane;
       const uint32_t i1 = i0 + kWaveSize;
       const bool v0 = i0 < nww, v1 = i1 < nww;
-      const uint32_t wd0 = v0 ? cand_all[ww * kCandPerWave + i0] : 0u;
-      const uint32_t wd1 = v1 ? cand_all[ww * kCandPerWave + i1] : 0u;
+      const uint32_t wd0 = v0 ? cand_all[ww * LY::kCandCap + i0] : 0u;
+      const uint32_t wd1 = v1 ? cand_all[ww * LY::kCandCap + i1] : 0u;
       const uint32_t id0w = ww * cwv * 8u + (wd0 & 0x3FFFu);
       const uint32_t id1w = ww * cwv * 8u + (wd1 & 0x3FFFu);
       const uint32_t r0 = race_word(id0w, seed, pos);
@@ -979,7 +1056,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (v1 && bi1 < (uint32_t)kDBins)
         atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
                   ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
-      lds_publish_step(&fs.job_done);
+      lds_publish_step(&fs.ready);
     }
   }
   lds_wait_at_least(&fs.scan_ready, 1u);
@@ -997,40 +1074,14 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const int32_t dstar = fs.dstar;
   const uint32_t L = fs.L;
   const double lnzs = fs.lnzs;
-  const uint16_t* group_of_bin = reinterpret_cast<const uint16_t*>(lds + kOffGroupOfBin);
-  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + kOffGrpBase);
-  const double* grp_s = reinterpret_cast<const double*>(lds + kOffGrpS);
+  const uint16_t* group_of_bin = reinterpret_cast<const uint16_t*>(lds + LY::kOffGroupOfBin);
+  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + LY::kOffGrpBase);
+  const double* grp_s = reinterpret_cast<const double*>(lds + LY::kOffGrpS);
   const uint32_t W = (uint32_t)a.W;
   const float invT = 1.0f / T;
 
-  // ---- 5. The ordered capture of each wave's own candidates (opt-in rows), then the pick ------
-  if (wid == 0) __builtin_amdgcn_s_setprio(2);
-  else __builtin_amdgcn_s_setprio(1);
-  if (capture) {
-    // Capture position of a survivor: its group's base (tokens with larger keys) + the group's
-    // members in earlier segments (smaller ids) + its rank among this wave's members.
-    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
-    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
-    // value >= x_cut (-0 and +0 compare equal, as their keys do).
-    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
-    int32_t* out_ids = a.packed_ids + slot * a.W;
-    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
-    for (uint32_t i = lane; i < nc_here; i += kWaveSize) {
-      const uint32_t wd = cand[i];
-      const float x = __uint_as_float(wd & 0xFFFF0000u);
-      if (!(x >= x_cut)) continue;
-      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-      const uint32_t g = group_of_bin[bi];
-      const uint32_t at = grp_base[g] + bincnt[bi] + rankw[i];
-      if (at < W) {
-        out_ids[at] = (int32_t)(id0 + (wd & 0x3FFFu));
-        if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
-      }
-    }
-  }
-  // The pick: wave 0, once every race draw is done (it has the row's scalars at hand).
-  if (wid == 0) {
-    lds_wait_at_least(&fs.job_done, jobs * kStep);
+  // ---- 5. The pick, then the ordered capture of the opt-in row -----------------------------
+  if (picker) {
     __builtin_amdgcn_s_setprio(3);
     // The support is bins d = 0..d*; bin d holds key kmax - d at index dspan - d. Float32 scores
     // first; bins within kRaceMargin of the best are rescored in float64, ties -> lowest id.
@@ -1087,6 +1138,41 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   }
+  // Capture: one job per wave's candidate list, claimed by whichever waves are free. Position of
+  // a survivor: its group's base (tokens with larger keys) + the group's members in earlier
+  // segments (smaller ids) + its rank among its wave's members.
+  __builtin_amdgcn_s_setprio(1);
+  if (capture) {
+    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
+    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
+    // value >= x_cut (-0 and +0 compare equal, as their keys do).
+    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
+    int32_t* out_ids = a.packed_ids + slot * a.W;
+    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+    for (;;) {
+      const uint32_t cj = lds_claim(&fs.cap_next);
+      if (cj >= (uint32_t)kWaves) break;
+      const uint32_t ncj0 = fs.wave_cand[cj];
+      const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
+      const uint32_t* cand_c = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap;
+      const uint16_t* bincnt_c =
+          reinterpret_cast<const uint16_t*>(lds + LY::kOffTables + cj * LY::kTableBytes);
+      const uint16_t* rank_c = reinterpret_cast<const uint16_t*>(lds + LY::kOffRank) + cj * LY::kCandCap;
+      const uint32_t id0c = cj * cw * 8u;
+      for (uint32_t i = lane; i < ncj; i += kWaveSize) {
+        const uint32_t wd = cand_c[i];
+        const float x = __uint_as_float(wd & 0xFFFF0000u);
+        if (!(x >= x_cut)) continue;
+        const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+        const uint32_t g = group_of_bin[bi];
+        const uint32_t at = grp_base[g] + bincnt_c[bi] + rank_c[i];
+        if (at < W) {
+          out_ids[at] = (int32_t)(id0c + (wd & 0x3FFFu));
+          if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
+        }
+      }
+    }
+  }
   return true;
 }
 
@@ -1104,13 +1190,18 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     const float p = a.top_p[b];
     const float mp = a.min_p[b];
     const uint64_t seed = a.seeds[b], pos = a.positions[b];
-    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f && k >= 1 && k <= kFastMaxK &&
-                          a.V >= kFastMinV && a.V <= kFastMaxV && (a.V & 7) == 0 &&
-                          (a.ld & 7) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
+    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f && k >= 1 &&
+                          k <= kCompactMaxK && a.V >= kFastMinV && a.V <= kFastMaxV &&
+                          (a.V & 7) == 0 && (a.ld & 7) == 0 &&
+                          (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
     if (eligible) {
-      const bool done =
-          p < 1.0f ? fast_row_bf16<true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                   : fast_row_bf16<false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+      bool done;
+      if (k <= kFastMaxK)
+        done = p < 1.0f ? fast_row_bf16<true, false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                        : fast_row_bf16<false, false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+      else
+        done = p < 1.0f ? fast_row_bf16<true, true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                        : fast_row_bf16<false, true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }
