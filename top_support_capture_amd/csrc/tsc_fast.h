@@ -39,9 +39,7 @@ constexpr int kLoadsFirst = 2;        // loads issued before the first one is aw
 constexpr int kLoadsAhead = 4;        // software pipeline depth afterwards (loads in flight per lane)
 constexpr int kStashPerWave = 256;    // stashed loads per wave (stash mode)
 constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
-constexpr int kMaxGroups = 256;       // distinct keys in a captured support
 constexpr int kThetaBins = 256;       // key distances of the sampled maxima below their maximum
-constexpr int kMaskBins = 256;        // bins with a 64-bit lane mask in the ranking tables
 constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
 constexpr int32_t kFastMaxK = 1536;   // stash mode; compaction mode above it
@@ -56,9 +54,15 @@ constexpr uint32_t kOwnDraws = 4;
 //     (one ballot per load) and expanded into candidates once the wave's stream has ended;
 //   compaction mode (1536 < top_k <= 8192, where most loads hold candidates): the values >= theta
 //     of each load are appended to the wave's candidate list as the load lands.
-// Per-wave ranking tables: the count per bin bi = key - theta_key (u16; later the exclusive
-// prefix over earlier waves) and, in stash mode, 64-bit lane masks for the first 256 bins.
-constexpr int kTableMaskOff = kDBins * 2;
+// Each wave counts its candidates per bin bi = key - theta_key in a table of its own (u16; later
+// the exclusive prefix over the earlier waves) and ranks each among its earlier candidates of the
+// same bin. Stash mode (small supports) ranks before the exchange and writes the capture
+// directly. Compaction mode (supports of thousands) only counts before the exchange, ranks while
+// the race draws run, and writes each survivor's packed word (id | bi << 18) at its position in
+// an LDS stage that is copied out with coalesced stores (positions past the stage are written
+// directly).
+constexpr int kTableBytes = kDBins * 2;
+constexpr int kMaskBins = 256;        // stash mode: bins with a 64-bit lane mask in the table
 
 // LDS regions after the mode-specific ones (bytes from the dynamic buffer base).
 template <int kOffTail>
@@ -66,13 +70,13 @@ struct TailLayout {
   static constexpr int kOffBinBest = kOffTail;                            // u64 [1024] race per bin
   static constexpr int kOffDummy = kOffBinBest + kDBins * 8;              // u32 [64] scatter sink
   static constexpr int kOffCnt = kOffDummy + kWaveSize * 4;               // u32 [1024] by key - theta
-  static constexpr int kOffGroupOfBin = kOffCnt + kDBins * 4;             // u16 [1024] group by bin
-  static constexpr int kOffGrpBase = kOffGroupOfBin + kDBins * 2;         // u32 [256]
-  static constexpr int kOffGrpS = kOffGrpBase + kMaxGroups * 4;           // f64 [256] (x - m) / T
-  static constexpr int kEnd = kOffGrpS + kMaxGroups * 8;
+  static constexpr int kOffBinBase = kOffCnt + kDBins * 4;                // u32 [1024] capture base
+  static constexpr int kOffBinS = kOffBinBase + kDBins * 4;               // f64 [1024] (x - m) / T
+  static constexpr int kEnd = kOffBinS + kDBins * 8;
 };
 // Stash mode: the stash, its chunk indices, the candidates. Once a wave has expanded its stash,
-// its stash slice holds its ranking tables and its chunk-index slice its candidates' ranks.
+// its stash slice holds its table (counts, then lane masks) and its chunk-index slice its
+// candidates' ranks.
 constexpr int kStashBytes = kWaves * kStashPerWave * 16;
 constexpr int kStashChBytes = kWaves * kStashPerWave * 4;
 struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> {
@@ -80,24 +84,22 @@ struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> 
   static constexpr int kOffStash = 0;                       // uint4 [16][256]
   static constexpr int kOffStashCh = kStashBytes;           // u32 [16][256]
   static constexpr int kOffCand = kOffStashCh + kStashChBytes;  // u32 [16][512]
-  static constexpr bool kMasks = true;                      // lane masks in the tables
-  static constexpr int kTableBytes = kDBins * 2 + kMaskBins * 8;  // per wave
-  static constexpr int kOffTables = kOffStash;              // [16][4 KB]
+  static constexpr int kOffTables = kOffStash;              // u16 [1024] + u64 [256] per wave
+  static constexpr int kTableStride = kStashPerWave * 16;
   static constexpr int kOffRank = kOffStashCh;              // u16 [16][512]
 };
-static_assert(LayoutStash::kTableBytes == kStashPerWave * 16, "a wave's tables fill its slice");
-static_assert(LayoutStash::kCandCap * 2 <= kStashPerWave * 4, "a wave's ranks fit its chunk slice");
-// Compaction mode: the candidates, the ranking tables (counts only: the many candidates of a bin
-// are ranked with ballots, without LDS atomics), the ranks.
+static_assert(kTableBytes + kMaskBins * 8 <= LayoutStash::kTableStride, "tables fit a slice");
+static_assert(LayoutStash::kCandCap * 2 <= kStashPerWave * 4, "ranks fit a chunk-index slice");
+// Compaction mode: the candidates, the tables, the stage.
 constexpr int kCompactCap = 1024;
 struct LayoutCompact
-    : TailLayout<kWaves * kCompactCap * 4 + kWaves * kDBins * 2 + kWaves * kCompactCap * 2> {
+    : TailLayout<kWaves * kCompactCap * 4 + kWaves * kTableBytes + 8192 * 4> {
   static constexpr int kCandCap = kCompactCap;              // candidate words per wave
   static constexpr int kOffCand = 0;                        // u32 [16][1024]
-  static constexpr bool kMasks = false;
-  static constexpr int kTableBytes = kDBins * 2;            // per wave
-  static constexpr int kOffTables = kOffCand + kWaves * kCandCap * 4;        // [16][2 KB]
-  static constexpr int kOffRank = kOffTables + kWaves * kTableBytes;         // u16 [16][1024]
+  static constexpr int kOffTables = kOffCand + kWaves * kCandCap * 4;        // u16 [16][1024]
+  static constexpr int kTableStride = kTableBytes;
+  static constexpr int kOffStage = kOffTables + kWaves * kTableBytes;        // u32 [8192]
+  static constexpr int kStageCap = 8192;
 };
 
 constexpr size_t kMaxSz(size_t x, size_t y) { return x > y ? x : y; }
@@ -120,6 +122,8 @@ struct FastShared {
   uint32_t job_next;            // next race-draw job to claim
   uint32_t ready;               // race-draw jobs completed
   uint32_t cap_next;            // next wave's candidate list to capture
+  uint32_t staged;              // candidate lists captured into the stage
+  uint32_t copy_next;           // next slice of the stage to copy out
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
   uint32_t noise_done[kWaves];  // candidates whose race draws the wave made itself (from the first)
   int32_t slot_wmax[kWaves];
@@ -303,8 +307,8 @@ __device__ inline T row16_reduce(T v, Op op) {
 
 // Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d; they
 // were counted by bi = key - theta_key = dspan - d. Lane l owns the nb consecutive bins from
-// l * nb. Publishes the threshold d*, the support size, and for capture rows the tie-group tables:
-// the group of each support bin, each group's base position and (x - m) / T, and ln Z_S.
+// l * nb. Publishes the threshold d*, the support size and ln Z_S, and for every support bin its
+// capture base (the tokens with larger keys) and (x - m) / T; a logprob is (x - m) / T - ln Z_S.
 template <bool NEED_P, int NB, class LY>
 __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
                                       int32_t k, float p, float mp, double Z, bool capture,
@@ -316,79 +320,72 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
   // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
   const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
   // Per bin (all loads first, so that their latencies overlap): value, count after min-p (a
-  // per-value predicate, monotone in d), and mass. The count is packed with the group
-  // indicator as count << 11 | present (at most 8192 candidates and 1024 bins), so that one
-  // integer scan gives both positions and group indices.
+  // per-value predicate, monotone in d), and mass.
   float xs[NB];
-  uint32_t pk[NB];
+  uint32_t cnt[NB];
   double bm[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const uint32_t d = lane * nb + (uint32_t)t;
-    pk[t] = 0u;
+    cnt[t] = 0u;
     xs[t] = 0.0f;
     if ((uint32_t)t < nb && d <= dspan) {
       xs[t] = E::to_float(bits_of_key<E>(kmax - d));
-      pk[t] = hcnt[dspan - d];
+      cnt[t] = hcnt[dspan - d];
     }
   }
-  uint32_t lp_ = 0;
+  uint32_t lc = 0;
   double lmass = 0.0;
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
-    const uint32_t bc = (!need_m || ((double)xs[t] - (double)m) >= tln_mp) ? pk[t] : 0u;
-    pk[t] = (bc << 11) | (uint32_t)(bc > 0u);
-    bm[t] = (NEED_P || capture) ? (double)bc * (double)__builtin_amdgcn_exp2f((xs[t] - m) * c)
+    if (need_m && !(((double)xs[t] - (double)m) >= tln_mp)) cnt[t] = 0u;
+    bm[t] = (NEED_P || capture) ? (double)cnt[t] * (double)__builtin_amdgcn_exp2f((xs[t] - m) * c)
                                 : 0.0;
-    lp_ += pk[t];
+    lc += cnt[t];
     lmass += bm[t];
   }
-  uint32_t tp;
+  uint32_t tc;
   double tm;
-  uint32_t ep = wave_excl_scan(lp_, SumU32(), tp);
+  uint32_t ec = wave_excl_scan(lc, SumU32(), tc);
   double em = wave_excl_scan(lmass, SumF64(), tm);
   const double pz = (double)p * Z;
   // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
   // strictly above <= top_p * Z. Each predicate is monotone in d, so this is the last qualifying
   // bin of the last lane that has one.
   int32_t best = -1;
-  uint32_t bL = 0, bG = 0;
+  uint32_t bL = 0;
   double bZ = 0.0;
-  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + LY::kOffGroupOfBin);
-  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + LY::kOffGrpBase);
-  double* grp_s = reinterpret_cast<double*>(lds + LY::kOffGrpS);
+  uint32_t* binbase = reinterpret_cast<uint32_t*>(lds + LY::kOffBinBase);
+  double* bins = reinterpret_cast<double*>(lds + LY::kOffBinS);
   const double invT = 1.0 / (double)T;
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const uint32_t d = lane * nb + (uint32_t)t;
-    if (pk[t] & 1u) {
-      const uint32_t ec = ep >> 11, eg = ep & 0x7FFu;
+    if (cnt[t] != 0u) {
       const bool qual = ec < (uint32_t)k && (!NEED_P || em <= pz);
       if (qual) {
         best = (int32_t)d;
-        bL = ec + (pk[t] >> 11);
-        bG = eg + 1u;
+        bL = ec + cnt[t];
         bZ = em + bm[t];
-        if (capture && eg < (uint32_t)kMaxGroups) {
-          group_of_bin[dspan - d] = (uint16_t)eg;
-          grp_base[eg] = ec;
-          grp_s[eg] = ((double)xs[t] - (double)m) * invT;
+        if (capture) {
+          binbase[dspan - d] = ec;
+          bins[dspan - d] = ((double)xs[t] - (double)m) * invT;
         }
       }
     }
-    ep += pk[t];
+    ec += cnt[t];
     em += bm[t];
   }
   // d* >= 0 always: bin 0 holds the maximum, which passes every predicate.
   const int32_t dstar = wave_reduce(best, MaxI32());
   const int owner = (int)((uint32_t)dstar / nb);
-  const uint32_t L = read_lane(bL, owner), G = read_lane(bG, owner);
-  const double zs = read_lane(bZ, owner);
+  const uint32_t L = read_lane(bL, owner);
+  const double lnzs = ln_fast(read_lane(bZ, owner));  // logprob = (x - m) / T - ln Z_S
   if (lane == 0) {
-    fs.decision = (capture && G > (uint32_t)kMaxGroups) ? kFallback : kProceed;
+    fs.decision = kProceed;
     fs.dstar = dstar;
     fs.L = L;
-    fs.lnzs = ln_fast(zs);  // logprob = (x - m) / T - ln Z_S
+    fs.lnzs = lnzs;
   }
 }
 
@@ -404,34 +401,30 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
   const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
   auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
-  // Count and mass of bin d after min-p (a per-value predicate, monotone in d). The count is
-  // packed with the group indicator as count << 11 | present (at most 8192 candidates and 1024
-  // bins), so that one integer scan gives both positions and group indices.
-  auto bin = [&](uint32_t d, uint32_t& packed, double& bm) {
-    packed = 0;
+  // Count and mass of bin d after min-p (a per-value predicate, monotone in d).
+  auto bin = [&](uint32_t d, uint32_t& bc, double& bm) {
+    bc = 0;
     bm = 0.0;
     if (d <= dspan) {
       const float x = value_of_d(d);
       if (!need_m || ((double)x - (double)m) >= tln_mp) {
-        const uint32_t bc = hcnt[dspan - d];
-        packed = (bc << 11) | (uint32_t)(bc > 0u);
-        if constexpr (NEED_P) bm = (double)bc * (double)__builtin_amdgcn_exp2f((x - m) * c);
-        else if (capture) bm = (double)bc * (double)__builtin_amdgcn_exp2f((x - m) * c);
+        bc = hcnt[dspan - d];
+        if (NEED_P || capture) bm = (double)bc * (double)__builtin_amdgcn_exp2f((x - m) * c);
       }
     }
   };
-  uint32_t lp_ = 0;
+  uint32_t lc = 0;
   double lmass = 0.0;
   for (uint32_t t = 0; t < nb; ++t) {
-    uint32_t pk;
+    uint32_t bc;
     double bm;
-    bin(lane * nb + t, pk, bm);
-    lp_ += pk;
+    bin(lane * nb + t, bc, bm);
+    lc += bc;
     lmass += bm;
   }
-  uint32_t tp;
+  uint32_t tc;
   double tm;
-  uint32_t ep = wave_excl_scan(lp_, SumU32(), tp);
+  uint32_t ec = wave_excl_scan(lc, SumU32(), tc);
   double em = wave_excl_scan(lmass, SumF64(), tm);
   const double pz = (double)p * Z;
   // The largest present d with fewer than k tokens strictly above and, for top_p < 1, mass
@@ -440,53 +433,39 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   int32_t best = -1;
   uint32_t bL = 0;
   double bZ = 0.0;
-  uint16_t* group_of_bin = reinterpret_cast<uint16_t*>(lds + LY::kOffGroupOfBin);
-  uint32_t* grp_base = reinterpret_cast<uint32_t*>(lds + LY::kOffGrpBase);
-  double* grp_s = reinterpret_cast<double*>(lds + LY::kOffGrpS);
+  uint32_t* binbase = reinterpret_cast<uint32_t*>(lds + LY::kOffBinBase);
+  double* bins = reinterpret_cast<double*>(lds + LY::kOffBinS);
   const double invT = 1.0 / (double)T;
   for (uint32_t t = 0; t < nb; ++t) {
     const uint32_t d = lane * nb + t;
-    uint32_t pk;
+    uint32_t bc;
     double bm;
-    bin(d, pk, bm);
-    if (pk & 1u) {
-      const uint32_t ec = ep >> 11, eg = ep & 0x7FFu;
+    bin(d, bc, bm);
+    if (bc != 0u) {
       const bool qual = ec < (uint32_t)k && (!NEED_P || em <= pz);
       if (qual) {
         best = (int32_t)d;
-        bL = ec + (pk >> 11);
+        bL = ec + bc;
         bZ = em + bm;
-        if (capture && eg < (uint32_t)kMaxGroups) {
-          group_of_bin[dspan - d] = (uint16_t)eg;
-          grp_base[eg] = ec;
-          grp_s[eg] = ((double)value_of_d(d) - (double)m) * invT;
+        if (capture) {
+          binbase[dspan - d] = ec;
+          bins[dspan - d] = ((double)value_of_d(d) - (double)m) * invT;
         }
       }
     }
-    ep += pk;
+    ec += bc;
     em += bm;
   }
   // d* >= 0 always: bin 0 holds the maximum, which passes every predicate.
   const int32_t dstar = wave_reduce(best, MaxI32());
   const int owner = (int)((uint32_t)dstar / nb);
   const uint32_t L = read_lane(bL, owner);
-  const double zs = read_lane(bZ, owner);
-  // Groups in the support: present bins up to d*.
-  const uint32_t G = wave_reduce(
-      [&] {
-        uint32_t g = 0;
-        for (uint32_t t = 0; t < nb; ++t) {
-          const uint32_t d = lane * nb + t;
-          g += (int32_t)d <= dstar && d <= dspan && hcnt[dspan - d] > 0u;
-        }
-        return g;
-      }(),
-      SumU32());
+  const double lnzs = ln_fast(read_lane(bZ, owner));  // logprob = (x - m) / T - ln Z_S
   if (lane == 0) {
-    fs.decision = (capture && G > (uint32_t)kMaxGroups) ? kFallback : kProceed;
+    fs.decision = kProceed;
     fs.dstar = dstar;
     fs.L = L;
-    fs.lnzs = ln_fast(zs);  // logprob = (x - m) / T - ln Z_S
+    fs.lnzs = lnzs;
   }
 }
 
@@ -569,6 +548,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     fs.job_next = 0u;
     fs.ready = 0u;
     fs.cap_next = 0u;
+    fs.staged = 0u;
+    fs.copy_next = 0u;
   }
   reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest)[tid] = 0ull;
 
@@ -867,12 +848,9 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       ncand += total;
     }
   }
-  // The wave's ranking tables (in stash mode its stash slice, free now) and its candidates' ranks.
-  uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + LY::kOffTables + wid * LY::kTableBytes);
-  uint64_t* binmask =
-      reinterpret_cast<uint64_t*>(lds + LY::kOffTables + wid * LY::kTableBytes + kTableMaskOff);
-  uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + LY::kOffRank) + wid * LY::kCandCap;
-  for (uint32_t i = lane; i < (uint32_t)LY::kTableBytes / 16; i += kWaveSize)
+  // The wave's count table (in stash mode its stash slice, free now).
+  uint16_t* bincnt = reinterpret_cast<uint16_t*>(lds + LY::kOffTables + wid * LY::kTableStride);
+  for (uint32_t i = lane; i < (uint32_t)kTableBytes / 16; i += kWaveSize)
     reinterpret_cast<uint4*>(bincnt)[i] = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t nc_here = ncand < (uint32_t)LY::kCandCap ? ncand : (uint32_t)LY::kCandCap;
   // Maximum: for top_p < 1 the largest candidate (the row maximum is >= theta, so it is one);
@@ -884,38 +862,57 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (lane == 0) fs.wave_m[wid] = wm;
   }
   const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
-  const bool by_mask = LY::kMasks && bmax < (uint32_t)kMaskBins;
-  // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
-  // earlier chunks (this wave's own table, so plain reads and writes) plus the lanes of its bin
-  // below it in this chunk. Those lanes come from a 64-bit mask per bin that every lane ORs its
-  // bit into, or, when the wave's bins reach beyond the mask table, from ballots over the bits
-  // of the bin. The bin's first lane stores the new count and adds the chunk's count to the
-  // row histogram.
-  for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
-    const uint32_t i = base + lane;
-    const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
-    const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-    const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
-    uint64_t same;
-    if (by_mask) {
-      if (in) atomicOr(reinterpret_cast<unsigned long long*>(&binmask[bi]), 1ull << lane);
-      same = in ? binmask[bi] : 0ull;
-    } else {
-      same = __ballot(in);
-#pragma unroll
-      for (int bit = 0; bit < 10; ++bit) {
-        const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
-        same &= ((bi >> bit) & 1u) ? ones : ~ones;
+  if constexpr (COMPACT) {
+    // Counts: the row histogram and this wave's table (two 16-bit counts per word), with LDS
+    // atomics whose results are not needed, so that no chunk waits for another. (The ranks the
+    // capture needs are taken after the exchange, where they overlap the race draws.)
+    uint32_t* bincnt32 = reinterpret_cast<uint32_t*>(bincnt);
+    for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
+      const uint32_t i = base + lane;
+      const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
+      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+      if (i < nc_here && bi < (uint32_t)kDBins) {  // wider spans fall back (span test)
+        atomicAdd(&hcnt[bi], 1u);
+        atomicAdd(&bincnt32[bi >> 1], 1u << ((bi & 1u) * 16u));
       }
     }
-    if (in) {
-      const uint32_t c0 = bincnt[bi];
-      rankw[i] = (uint16_t)(c0 + mbcnt(same));
-      if (lane == (uint32_t)__builtin_ctzll(same)) {
-        const uint32_t cnt = (uint32_t)__popcll(same);
-        bincnt[bi] = (uint16_t)(c0 + cnt);
-        if (by_mask) binmask[bi] = 0ull;
-        atomicAdd(&hcnt[bi], cnt);
+  } else {
+    // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
+    // earlier chunks (this wave's own table, so plain reads and writes) plus the lanes of its
+    // bin below it in this chunk. Those lanes come from a 64-bit mask per bin that every lane
+    // ORs its bit into, or, when the wave's bins reach beyond the mask table, from ballots over
+    // the bits of the bin. The bin's first lane stores the new count and adds the chunk's count
+    // to the row histogram.
+    uint64_t* binmask = reinterpret_cast<uint64_t*>(bincnt + kDBins);
+    uint16_t* rankw = reinterpret_cast<uint16_t*>(lds + LayoutStash::kOffRank) + wid * LY::kCandCap;
+    for (uint32_t i = lane; i < (uint32_t)kMaskBins; i += kWaveSize) binmask[i] = 0ull;
+    const bool by_mask = bmax < (uint32_t)kMaskBins;
+    for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
+      const uint32_t i = base + lane;
+      const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
+      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+      const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
+      uint64_t same;
+      if (by_mask) {
+        if (in) atomicOr(reinterpret_cast<unsigned long long*>(&binmask[bi]), 1ull << lane);
+        same = in ? binmask[bi] : 0ull;
+      } else {
+        same = __ballot(in);
+#pragma unroll
+        for (int bit = 0; bit < 10; ++bit) {
+          const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
+          same &= ((bi >> bit) & 1u) ? ones : ~ones;
+        }
+      }
+      if (in) {
+        const uint32_t c0 = bincnt[bi];
+        rankw[i] = (uint16_t)(c0 + mbcnt(same));
+        if (lane == (uint32_t)__builtin_ctzll(same)) {
+          const uint32_t cnt = (uint32_t)__popcll(same);
+          bincnt[bi] = (uint16_t)(c0 + cnt);
+          if (by_mask) binmask[bi] = 0ull;
+          atomicAdd(&hcnt[bi], cnt);
+        }
       }
     }
   }
@@ -1014,7 +1011,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       // each tie group, relative to the group's base (waves 1-4; the other helpers start on the
       // race draws at once).
       uint16_t* cnt0 = reinterpret_cast<uint16_t*>(lds + LY::kOffTables);
-      constexpr int kStride = LY::kTableBytes / 2;  // u16 between two waves' tables
+      constexpr int kStride = LY::kTableStride / 2;  // u16 between two waves' tables
       uint32_t nbins = 0;  // bins any wave used
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) nbins = nbins > fs.bin_hi[w] ? nbins : fs.bin_hi[w];
@@ -1074,9 +1071,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const int32_t dstar = fs.dstar;
   const uint32_t L = fs.L;
   const double lnzs = fs.lnzs;
-  const uint16_t* group_of_bin = reinterpret_cast<const uint16_t*>(lds + LY::kOffGroupOfBin);
-  const uint32_t* grp_base = reinterpret_cast<const uint32_t*>(lds + LY::kOffGrpBase);
-  const double* grp_s = reinterpret_cast<const double*>(lds + LY::kOffGrpS);
+  const uint32_t* binbase = reinterpret_cast<const uint32_t*>(lds + LY::kOffBinBase);
+  const double* bins = reinterpret_cast<const double*>(lds + LY::kOffBinS);
   const uint32_t W = (uint32_t)a.W;
   const float invT = 1.0f / T;
 
@@ -1134,13 +1130,81 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
       if (capture) {
         a.lengths[slot] = (int32_t)(L < W ? L : W);
-        a.selected_logprob[slot] = (float)(grp_s[group_of_bin[dspan - td]] - lnzs);
+        a.selected_logprob[slot] = (float)(bins[dspan - td] - lnzs);
       }
     }
   }
-  // Capture: one job per wave's candidate list, claimed by whichever waves are free. Position of
-  // a survivor: its group's base (tokens with larger keys) + the group's members in earlier
-  // segments (smaller ids) + its rank among its wave's members.
+  if constexpr (COMPACT) {
+  // Capture (compaction mode): one job per wave's candidate list, claimed by whichever waves are free. A survivor's
+  // position is its bin's base (tokens with larger keys) + the bin's members in earlier segments
+  // (smaller ids: the wave's table, now the prefix over the waves, kept running) + the bin's
+  // members before it in this chunk (ballots over the bits of the bin). Its packed word goes to
+  // the LDS stage; once every list is staged, the stage is copied out with coalesced stores.
+  __builtin_amdgcn_s_setprio(1);
+  if (capture) {
+    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
+    // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
+    // value >= x_cut (-0 and +0 compare equal, as their keys do).
+    const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
+    int32_t* out_ids = a.packed_ids + slot * a.W;
+    float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+    uint32_t* stage = reinterpret_cast<uint32_t*>(lds + LY::kOffStage);
+    // Bits of the bins of the support: bi <= dspan.
+    const uint32_t nbits = 32u - (uint32_t)__builtin_clz(dspan | 1u);
+    for (;;) {
+      const uint32_t cj = lds_claim(&fs.cap_next);
+      if (cj >= (uint32_t)kWaves) break;
+      const uint32_t ncj0 = fs.wave_cand[cj];
+      const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
+      const uint32_t* cand_c = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap;
+      uint16_t* run_c = reinterpret_cast<uint16_t*>(lds + LY::kOffTables + cj * LY::kTableStride);
+      const uint32_t id0c = cj * cw * 8u;
+      for (uint32_t base = 0; base < ncj; base += kWaveSize) {
+        const uint32_t i = base + lane;
+        const uint32_t wd = i < ncj ? cand_c[i] : 0xFF800000u;
+        const bool in = i < ncj && __uint_as_float(wd & 0xFFFF0000u) >= x_cut;
+        const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+        uint64_t same = __ballot(in);
+        for (uint32_t bit = 0; bit < nbits; ++bit) {
+          const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
+          same &= ((bi >> bit) & 1u) ? ones : ~ones;
+        }
+        if (in) {
+          const uint32_t c0 = run_c[bi];
+          const uint32_t at = binbase[bi] + c0 + mbcnt(same);
+          if (lane == (uint32_t)__builtin_ctzll(same)) run_c[bi] = (uint16_t)(c0 + (uint32_t)__popcll(same));
+          const uint32_t id = id0c + (wd & 0x3FFFu);
+          if (at < (uint32_t)LY::kStageCap) {
+            stage[at] = id | (bi << 18);
+          } else if (at < W) {
+            out_ids[at] = (int32_t)id;
+            if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
+          }
+        }
+      }
+      lds_publish_step(&fs.staged);
+    }
+    // Copy-out of the stage, in slices of 1024 positions.
+    const uint32_t nl = L < W ? L : W;
+    const uint32_t nout = nl < (uint32_t)LY::kStageCap ? nl : (uint32_t)LY::kStageCap;
+    if (nout > 0u) {
+      lds_wait_at_least(&fs.staged, (uint32_t)kWaves * kStep);
+      for (;;) {
+        const uint32_t sl = lds_claim(&fs.copy_next);
+        if (sl * 1024u >= nout) break;
+        const uint32_t end = (sl + 1u) * 1024u < nout ? (sl + 1u) * 1024u : nout;
+        for (uint32_t j = sl * 1024u + lane; j < end; j += kWaveSize) {
+          const uint32_t e = stage[j];
+          out_ids[j] = (int32_t)(e & 0x3FFFFu);
+          if (out_lp) out_lp[j] = (float)(bins[e >> 18] - lnzs);
+        }
+      }
+    }
+  }
+  } else {
+  // Capture (stash mode): one job per wave's candidate list, claimed by whichever waves are free.
+  // A survivor's position is its bin's base (tokens with larger keys) + the bin's members in
+  // earlier segments (smaller ids: the prefix over the waves) + its rank in its wave.
   __builtin_amdgcn_s_setprio(1);
   if (capture) {
     lds_wait_at_least(&fs.prefix_done, 4u * kStep);
@@ -1156,22 +1220,23 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
       const uint32_t* cand_c = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap;
       const uint16_t* bincnt_c =
-          reinterpret_cast<const uint16_t*>(lds + LY::kOffTables + cj * LY::kTableBytes);
-      const uint16_t* rank_c = reinterpret_cast<const uint16_t*>(lds + LY::kOffRank) + cj * LY::kCandCap;
+          reinterpret_cast<const uint16_t*>(lds + LY::kOffTables + cj * LY::kTableStride);
+      const uint16_t* rank_c =
+          reinterpret_cast<const uint16_t*>(lds + LayoutStash::kOffRank) + cj * LY::kCandCap;
       const uint32_t id0c = cj * cw * 8u;
       for (uint32_t i = lane; i < ncj; i += kWaveSize) {
         const uint32_t wd = cand_c[i];
         const float x = __uint_as_float(wd & 0xFFFF0000u);
         if (!(x >= x_cut)) continue;
         const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-        const uint32_t g = group_of_bin[bi];
-        const uint32_t at = grp_base[g] + bincnt_c[bi] + rank_c[i];
+        const uint32_t at = binbase[bi] + bincnt_c[bi] + rank_c[i];
         if (at < W) {
           out_ids[at] = (int32_t)(id0c + (wd & 0x3FFFu));
-          if (out_lp) out_lp[at] = (float)(grp_s[g] - lnzs);
+          if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
         }
       }
     }
+  }
   }
   return true;
 }
@@ -1179,7 +1244,9 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
 template <int DT>
 __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
-  extern __shared__ uint64_t dyn[];
+  // The dynamic buffer starts after the static LDS; 256-byte alignment keeps every 16-byte
+  // stash access aligned (and the bank mapping of the layout fixed) whatever FastShared's size.
+  extern __shared__ __attribute__((aligned(256))) uint64_t dyn[];
   __shared__ FastShared fs;
   unsigned char* lds = reinterpret_cast<unsigned char*>(dyn);
   const int64_t b = blockIdx.x;
