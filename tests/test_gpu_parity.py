@@ -302,7 +302,7 @@ FAST_PARAMS = [
 ]
 
 
-@pytest.mark.parametrize("V", [32768, 151936])
+@pytest.mark.parametrize("V", [32768, 151936, 262144])
 def test_single_read_path_rows(V):
     rng = np.random.default_rng(77)
     rows = _fast_rows(rng, V)

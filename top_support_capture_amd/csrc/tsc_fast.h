@@ -34,14 +34,20 @@
 
 namespace tsc {
 
-constexpr int kFastLoads = 20;        // 16-byte loads per lane (segment of at most 20 * 512 values)
+// 16-byte loads per lane: a segment of at most 20 * 512 values for rows up to 163840, 32 * 512
+// for rows up to 262144 (two instantiations, so that shorter rows keep the shorter stream code).
+constexpr int kShortLoads = 20;
+constexpr int kFastLoads = 32;
 constexpr int kLoadsFirst = 2;        // loads issued before the first one is awaited
 constexpr int kLoadsAhead = 4;        // software pipeline depth afterwards (loads in flight per lane)
 constexpr int kStashPerWave = 256;    // stashed loads per wave (stash mode)
 constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
-constexpr int kThetaBins = 256;       // key distances of the sampled maxima below their maximum
+// Key distances of the sampled maxima below their maximum: heavy-tailed rows (a Zipf-like head
+// over a wide vocabulary) need theta over 256 keys (two binades of bf16) below it.
+constexpr int kThetaBins = 512;
 constexpr int64_t kFastMinV = 16384;
-constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;  // 163840
+constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;     // 262144
+constexpr int64_t kShortMaxV = (int64_t)kWaves * kWaveSize * kShortLoads * 8;   // 163840
 constexpr int32_t kFastMaxK = 1536;   // stash mode; compaction mode above it
 constexpr int32_t kCompactMaxK = 8192;
 constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
@@ -88,6 +94,7 @@ struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> 
   static constexpr int kTableStride = kStashPerWave * 16;
   static constexpr int kOffRank = kOffStashCh;              // u16 [16][512]
 };
+static_assert(kThetaBins % kWaveSize == 0 && kThetaBins <= kThreads, "theta histogram scan");
 static_assert(kTableBytes + kMaskBins * 8 <= LayoutStash::kTableStride, "tables fit a slice");
 static_assert(LayoutStash::kCandCap * 2 <= kStashPerWave * 4, "ranks fit a chunk-index slice");
 // Compaction mode: the candidates, the tables, the stage.
@@ -475,7 +482,7 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
 template <> struct LayoutOf<true> { using type = LayoutCompact; };
 
-template <bool NEED_P, bool COMPACT>
+template <bool NEED_P, bool COMPACT, int LOADS>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
                                               float T, int32_t k, float p, float mp,
                                               uint64_t seed, uint64_t pos, unsigned char* lds,
@@ -521,7 +528,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const int32_t opt_e = (a.R <= kThreads && (int64_t)tid < a.R) ? a.optin_rows[tid] : INT32_MIN;
   // Buffer loads: the wave's segment is one scalar resource descriptor (loads past its end return
   // zero and are replaced below), one shared VGPR offset, and a scalar offset per load.
-  uint4 r[kFastLoads];
+  uint4 r[LOADS];
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint4*>(rowv + seg0), (short)0, (int)(nseg * 16u), 0x00020000);
   const int voff = (int)(lane * 16u);
@@ -555,6 +562,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
   const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
+  [[maybe_unused]] const uint32_t nloads = uniform_u32((nseg + kWaveSize - 1) / kWaveSize);
   auto mask_tail = [&](int j) {
     if ((uint32_t)j >= nfull) {  // wave-uniform: a scalar branch, no vector work on full loads
       if ((uint32_t)j * kWaveSize + lane >= nseg)
@@ -658,7 +666,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   asm volatile("" ::"v"(lm0));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int jj = kLoadsFirst; jj <= kLoadsAhead && jj < kFastLoads; ++jj) issue(jj);
+  for (int jj = kLoadsFirst; jj <= kLoadsAhead && jj < LOADS; ++jj) issue(jj);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t key0 = key_of<E>(__float_as_uint(lm0) >> 16);
@@ -711,20 +719,21 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   pin();
   uint32_t theta_key;
   {
-    uint32_t hc[4];
+    constexpr int kPer = kThetaBins / kWaveSize;
+    uint32_t hc[kPer];
     uint32_t lsum = 0;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      hc[q4] = fs.theta_hist[lane * 4 + q4];
+    for (int q4 = 0; q4 < kPer; ++q4) {
+      hc[q4] = fs.theta_hist[lane * kPer + q4];
       lsum += hc[q4];
     }
     uint32_t tot;
     uint32_t run = wave_excl_sum(lsum, tot);
     uint32_t found = 0xFFFFFFFFu;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q4 = 0; q4 < kPer; ++q4) {
       run += hc[q4];
-      if (found == 0xFFFFFFFFu && run >= theta_rank) found = lane * 4 + q4;
+      if (found == 0xFFFFFFFFu && run >= theta_rank) found = lane * kPer + q4;
     }
     const uint32_t dmin = wave_reduce(found, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
     const uint32_t dsel = dmin != 0xFFFFFFFFu ? dmin : (uint32_t)kThetaBins - 1u;
@@ -749,8 +758,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // back, which happens only for extreme spreads of the logits at low temperature.)
   const float wth = 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc));
 #pragma unroll
-  for (int j = 3; j < kFastLoads; ++j) {
-    if (j + kLoadsAhead < kFastLoads) issue(j + kLoadsAhead);
+  for (int j = 3; j < LOADS; ++j) {
+    // The long stream skips the steps a shorter row does not need (a wave-uniform test). The
+    // short one has no such test: conditional issues make the compiler's wait counts
+    // conservative, which serialises the load pipeline (loads past the segment read zeros).
+    if constexpr (LOADS > kShortLoads) {
+      if ((uint32_t)j >= nloads) continue;
+      if (j + kLoadsAhead < LOADS && (uint32_t)(j + kLoadsAhead) < nloads) issue(j + kLoadsAhead);
+    } else {
+      if (j + kLoadsAhead < LOADS) issue(j + kLoadsAhead);
+    }
     mask_tail(j);
     unpack(r[j], f);
     bool flag;
@@ -1242,6 +1259,18 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 }
 
 
+template <int LOADS>
+__device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b, int64_t& slot,
+                                                  float T, int32_t k, float p, float mp,
+                                                  uint64_t seed, uint64_t pos, unsigned char* lds,
+                                                  FastShared& fs) {
+  if (k <= kFastMaxK)
+    return p < 1.0f ? fast_row_bf16<true, false, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                    : fast_row_bf16<false, false, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+  return p < 1.0f ? fast_row_bf16<true, true, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                  : fast_row_bf16<false, true, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
   // The dynamic buffer starts after the static LDS; 256-byte alignment keeps every 16-byte
@@ -1262,13 +1291,10 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
                           (a.V & 7) == 0 && (a.ld & 7) == 0 &&
                           (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
     if (eligible) {
-      bool done;
-      if (k <= kFastMaxK)
-        done = p < 1.0f ? fast_row_bf16<true, false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                        : fast_row_bf16<false, false>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
-      else
-        done = p < 1.0f ? fast_row_bf16<true, true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                        : fast_row_bf16<false, true>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+      const bool done =
+          a.V <= kShortMaxV
+              ? fast_row_dispatch<kShortLoads>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+              : fast_row_dispatch<kFastLoads>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }
