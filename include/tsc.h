@@ -108,6 +108,38 @@ int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64
                              float* logprobs, int32_t* lengths, float* selected_logprob,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * tsc_sample_with_mask_bits -- tsc_sample_with_mask, plus the exact support of every OVERFLOW
+ * slot as a bitmask (vLLM "Sampling Mask / Distribution Replay" article, "How it works" step 2:
+ * beside the compact id buffer of bounded width, a bit-packed mask of ceil(V / 8) bytes per row
+ * encodes a wider support exactly).
+ *
+ * All other arguments and outputs are those of tsc_sample_with_mask.
+ * support_bits [R, bits_ld] uint8 out, or NULL (then this is tsc_sample_with_mask). Written only
+ *              for slots whose row status is TSC_ROW_OVERFLOW: bit i % 8 of byte i / 8 is set iff
+ *              token i is in the support S, for 0 <= i < V. The first tsc_support_bits_ld(V)
+ *              bytes of the row are written (bits past V are zero); the rest of the row and the
+ *              rows of other slots are left untouched. The number of set bits equals |S|.
+ * bits_ld      row stride in bytes: a multiple of 16 and >= tsc_support_bits_ld(V); the buffer
+ *              must be 16-byte aligned. Both are checked only when support_bits is not NULL and
+ *              R > 0 (TSC_ERR_INVALID_ARGUMENT otherwise).
+ * Costs nothing extra for rows that do not overflow; an overflowing row adds one write of its
+ * bitmask row and one atomic OR per support token.
+ */
+int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, int64_t V,
+                                  int64_t ld, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, const float* min_p,
+                                  const int32_t* optin_rows, int64_t R, const uint64_t* seeds,
+                                  const uint64_t* positions, int32_t W, int32_t* tokens,
+                                  int8_t* row_status, int32_t* packed_ids, float* logprobs,
+                                  int32_t* lengths, float* selected_logprob,
+                                  uint8_t* support_bits, int64_t bits_ld, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Bytes of a support bitmask row that tsc_sample_with_mask_bits writes: ceil(V / 8) rounded up
+ * to a multiple of 16 (the smallest valid bits_ld); 0 for V < 1. */
+int64_t tsc_support_bits_ld(int64_t V);
+
 /* Device scratch bytes tsc_sample_with_mask needs for these sizes (currently always 0). */
 size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dtype);
 

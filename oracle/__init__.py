@@ -7,5 +7,5 @@ from .philox import philox4, token_uniforms  # noqa: F401
 from .sampler import (  # noqa: F401
     ROW_OK, ROW_OVERFLOW, ROW_NO_SUPPORT, ROW_NONFINITE, ROW_INVALID_PARAM,
     RACE_TIE_EPS, TOP_P_EPS, MIN_P_EPS, RowResult, BatchResult,
-    decode_logits, params_valid, sample_row, sample_with_mask, slot_validity,
+    decode_logits, params_valid, sample_row, sample_with_mask, slot_validity, support_bitmask,
 )

@@ -41,7 +41,11 @@ Readings taken where the pages are silent or disagree (each is a documented choi
   R9 capture slot j is valid iff 0 <= optin_rows[j] < B and optin_rows[j] exceeds every earlier
      entry (so valid slots name distinct rows, in ascending order); invalid slots get length 0
      and a NaN selected logprob;
-  R10 logprobs are normalized over the full support even when the packed prefix is clamped.
+  R10 logprobs are normalized over the full support even when the packed prefix is clamped;
+  R11 the exact fallback for a support wider than the packed width is a bit-packed mask of
+     ceil(V / 8) bytes per row (vLLM article, "How it works" step 2); the page does not fix the
+     bit order: token i is bit i % 8 of byte i // 8 (least significant bit first), and the mask
+     is written for OVERFLOW slots only.
 """
 from __future__ import annotations
 
@@ -187,6 +191,18 @@ def sample_row(x: np.ndarray, T: float, top_k: int, top_p: float, min_p: float,
     return RowResult(ROW_OK, token, ids[:L].astype(np.int64), lp, race_gap, top_p_flag, min_p_flag)
 
 
+def support_bitmask(support: np.ndarray, V: int, nbytes: Optional[int] = None) -> np.ndarray:
+    """R11: the support as a bit-packed mask, token i at bit i % 8 of byte i // 8, zero-padded to
+    ``nbytes`` bytes (default ceil(V / 8))."""
+    keep = np.zeros(V, dtype=bool)
+    keep[np.asarray(support, dtype=np.int64)] = True
+    packed = np.packbits(keep, bitorder="little")
+    n = packed.size if nbytes is None else int(nbytes)
+    out = np.zeros(n, np.uint8)
+    out[:packed.size] = packed
+    return out
+
+
 @dataclasses.dataclass
 class BatchResult:
     tokens: np.ndarray            # int32 [B]
@@ -197,6 +213,7 @@ class BatchResult:
     selected_logprob: np.ndarray  # float32 [R]
     slot_valid: np.ndarray        # bool [R]
     rows: List[RowResult]
+    support_bits: Optional[np.ndarray] = None  # uint8 [R, bits_ld]; zero except OVERFLOW slots
 
 
 def slot_validity(optin_rows: np.ndarray, B: int) -> np.ndarray:
@@ -210,13 +227,15 @@ def slot_validity(optin_rows: np.ndarray, B: int) -> np.ndarray:
 
 def sample_with_mask(logits: np.ndarray, dtype: str, temperature, top_k, top_p, min_p,
                      optin_rows, seeds, positions, W: int,
-                     rows: Optional[np.ndarray] = None) -> BatchResult:
+                     rows: Optional[np.ndarray] = None,
+                     bits_ld: Optional[int] = None) -> BatchResult:
     """Oracle of the whole batched call.
 
     ``logits``: float32 [B, V] or uint16 [B, V] of bfloat16 bits. Returns every output of the
     library call plus the per-row diagnostics. With ``rows`` given, only those rows are sampled
     (the others keep token -1 / status -1 and empty captures): used for sampled checks at full
-    size."""
+    size. With ``bits_ld`` the support of every OVERFLOW slot is also returned as a bitmask row
+    of that many bytes (R11)."""
     B = logits.shape[0]
     R = len(optin_rows)
     tokens = np.full(B, -1, np.int32)
@@ -225,6 +244,8 @@ def sample_with_mask(logits: np.ndarray, dtype: str, temperature, top_k, top_p, 
     lps = np.full((R, W), np.nan, np.float32)
     lengths = np.zeros(R, np.int32)
     sel = np.full(R, np.nan, np.float32)
+    V = logits.shape[1]
+    bits = None if bits_ld is None else np.zeros((R, int(bits_ld)), np.uint8)
     valid = slot_validity(optin_rows, B)
     slot_of = {int(optin_rows[j]): j for j in range(R) if valid[j]}
     todo = range(B) if rows is None else [int(r) for r in rows]
@@ -245,5 +266,7 @@ def sample_with_mask(logits: np.ndarray, dtype: str, temperature, top_k, top_p, 
             sel[j] = res.logprobs[pos]
             if res.L > W:
                 st = ROW_OVERFLOW
+                if bits is not None:
+                    bits[j] = support_bitmask(res.support, V, bits_ld)
         status[r] = st
-    return BatchResult(tokens, status, packed, lps, lengths, sel, valid, results)
+    return BatchResult(tokens, status, packed, lps, lengths, sel, valid, results, bits)

@@ -42,11 +42,30 @@ def device_inputs(wl, device="cuda:0", pad: int = 0) -> dict:
     }
 
 
-def run_gpu(wl, W=None, return_logprobs=True, pad=0, inputs=None) -> dict:
+def run_gpu(wl, W=None, return_logprobs=True, pad=0, inputs=None, bits=False) -> dict:
+    """One library call; with ``bits`` the support bitmask buffer is passed too, pre-filled with
+    BITS_SENTINEL so that rows the call must not write can be checked."""
     import top_support_capture_amd as tsc
+    from tests.parity import BITS_SENTINEL
     d = inputs if inputs is not None else device_inputs(wl, pad=pad)
+    W = wl.W if W is None else W
+    out = None
+    if bits:
+        dev = d["logits"].device
+        B, V = d["logits"].shape
+        R, Wc = int(d["optin_rows"].numel()), max(int(W), 1)
+        out = tsc.SampleOutput(
+            tokens=torch.empty(B, dtype=torch.int32, device=dev),
+            packed_ids=torch.empty((R, Wc), dtype=torch.int32, device=dev),
+            lengths=torch.empty(R, dtype=torch.int32, device=dev),
+            logprobs=(torch.empty((R, Wc), dtype=torch.float32, device=dev)
+                      if return_logprobs else None),
+            selected_logprob=torch.empty(R, dtype=torch.float32, device=dev),
+            row_status=torch.empty(B, dtype=torch.int8, device=dev),
+            support_bits=torch.full((R, tsc.support_bits_ld(V)), BITS_SENTINEL,
+                                    dtype=torch.uint8, device=dev))
     out = tsc.sample_with_mask(d["logits"], d["temperature"], d["top_k"], d["top_p"], d["min_p"],
-                               d["optin_rows"], d["seeds"], d["positions"],
-                               wl.W if W is None else W, return_logprobs=return_logprobs)
+                               d["optin_rows"], d["seeds"], d["positions"], W,
+                               return_logprobs=return_logprobs, out=out)
     torch.cuda.synchronize()
     return to_numpy_outputs(out)

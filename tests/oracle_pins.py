@@ -189,3 +189,45 @@ def pin_race_distribution(sample_row, draws=6000):
         counts[sample_row(x, 1.0, -1, 1.0, 0.0, 10_000 + s, 17).token] += 1
     p = chisquare(counts, probs * draws).pvalue
     return [] if p > 1e-4 else [f"race frequencies {counts} reject w/Z (p={p:.2e})"]
+
+
+def _int_mask_bytes(ids, nbytes):
+    """Bytes of the integer sum(2^i for i in ids), least significant byte first: token i lands at
+    bit i % 8 of byte i // 8 by positional notation, with no bit-packing routine involved."""
+    v = 0
+    for i in ids:
+        v |= 1 << int(i)
+    return list(v.to_bytes(nbytes, "little"))
+
+
+def pin_support_bitmask(support_bitmask, sample_row, rng_seed=2, cases=300):
+    """The bitmask of a support (vLLM article, "How it works" step 2: a bit-packed mask of
+    ceil(V / 8) bytes per row). The pages' tie example keeps ids {0, 1, 2} of V = 5, so its mask
+    is the single byte 0b111 = 7; random tiny rows compare the mask of the oracle's support with
+    the integer image of the brute-force support, zero-padded."""
+    fails = []
+    g = json.load(open(os.path.join(GOLDEN, "tie_example.json")))
+    x = np.log(np.array(g["probs"], dtype=np.float32)).astype(np.float32).astype(np.float64)
+    r = sample_row(x, 1.0, g["top_k"], g["top_p"], 0.0, 0, 0)
+    got = support_bitmask(r.support, len(x)).tolist()
+    if got != [7]:
+        fails.append(f"tie example mask {got} != [7]")
+    rng = np.random.default_rng(rng_seed)
+    for _ in range(cases):
+        V = int(rng.integers(1, 40))
+        xs = [float(v) for v in rng.choice(LEVELS, V)]
+        if all(v == -math.inf for v in xs):
+            continue
+        k = int(rng.integers(0, V + 2))
+        p = float(rng.choice([0.0, 0.3, 0.7, 1.0]))
+        S, near = brute_force(xs, 1.0, k, p, 0.0)
+        if near:
+            continue
+        nbytes = (V + 7) // 8 + int(rng.integers(0, 3))
+        r = sample_row(np.array(xs), 1.0, k, p, 0.0, 0, 0)
+        got = support_bitmask(r.support, V, nbytes).tolist()
+        want = _int_mask_bytes(S, nbytes)
+        if got != want:
+            fails.append(f"mask {got} != {want} for x={xs} k={k} p={p}")
+            break
+    return fails

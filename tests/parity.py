@@ -21,7 +21,38 @@ def to_numpy_outputs(out) -> dict:
         "lengths": out.lengths.cpu().numpy(),
         "logprobs": None if out.logprobs is None else out.logprobs.cpu().numpy(),
         "selected_logprob": out.selected_logprob.cpu().numpy(),
+        "support_bits": None if out.support_bits is None else out.support_bits.cpu().numpy(),
     }
+
+
+BITS_SENTINEL = 0xA5  # what a bitmask row holds before the call; slots that do not overflow keep it
+
+
+def compare_bits(got: dict, ref, optin_rows, rows=None):
+    """Support bitmasks: bit-exact against the oracle on every OVERFLOW slot whose support is
+    decided away from a filter boundary; every other valid slot's row left untouched. Returns
+    (errors, number of bitmask rows checked)."""
+    errs, n = [], 0
+    bits = got["support_bits"]
+    todo = None if rows is None else set(int(r) for r in rows)
+    for j in range(len(optin_rows)):
+        if not ref.slot_valid[j]:
+            continue
+        r = int(optin_rows[j])
+        if todo is not None and r not in todo:
+            continue
+        res = ref.rows[r]
+        if ref.row_status[r] == 1:
+            if res.top_p_flag or res.min_p_flag:
+                continue
+            n += 1
+            if not np.array_equal(bits[j], ref.support_bits[j]):
+                diff = np.nonzero(np.unpackbits(bits[j] ^ ref.support_bits[j], bitorder="little"))[0]
+                errs.append(f"slot {j} row {r}: bitmask differs at ids {diff[:8].tolist()} "
+                            f"({diff.size} bits)")
+        elif int(got["row_status"][r]) != 1 and not np.all(bits[j] == BITS_SENTINEL):
+            errs.append(f"slot {j} row {r}: bitmask row written without OVERFLOW")
+    return errs, n
 
 
 def compare(got: dict, ref, optin_rows, rows=None):

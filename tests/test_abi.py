@@ -23,7 +23,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["tsc_sample_with_mask", "tsc_status_string", "tsc_version",
+    assert declared_functions() == ["tsc_sample_with_mask", "tsc_sample_with_mask_bits",
+                                    "tsc_status_string", "tsc_support_bits_ld", "tsc_version",
                                     "tsc_workspace_size"]
 
 
@@ -58,6 +59,32 @@ def _call(lib, **kw):
 def test_host_argument_checks(lib, kw, code):
     # Every case returns before any HIP call, so this runs without a GPU.
     assert _call(lib, **kw) == code
+
+
+def _call_bits(lib, **kw):
+    args = dict(logits=0x1000, dtype=1, B=4, V=100, ld=100, temperature=8, top_k=8, top_p=8,
+                min_p=8, optin_rows=8, R=2, seeds=8, positions=8, W=16, tokens=8, row_status=8,
+                packed_ids=8, logprobs=8, lengths=8, selected_logprob=8, support_bits=0x2000,
+                bits_ld=16, workspace=None, wsb=0, stream=None)
+    args.update(kw)
+    return lib.tsc_sample_with_mask_bits(*args.values())
+
+
+def test_support_bits_row_size(lib):
+    # ceil(V / 8) bytes rounded up to 16.
+    for V, ld in [(1, 16), (8, 16), (128, 16), (129, 32), (100, 16), (151936, 18992),
+                  (129280, 16160), (262144, 32768), (32000, 4000), (0, 0)]:
+        assert lib.tsc_support_bits_ld(V) == ld, V
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits_ld=15), 1), (dict(bits_ld=8), 1), (dict(bits_ld=24), 1),
+    (dict(support_bits=0x2008), 1), (dict(V=129, ld=129, bits_ld=16), 1),
+    (dict(dtype=7), 1), (dict(W=0), 1), (dict(B=0, R=0), 0),
+])
+def test_bits_argument_checks(lib, kw, code):
+    # Every case returns before any HIP call, so this runs without a GPU.
+    assert _call_bits(lib, **kw) == code
 
 
 def test_binding_rejects_bad_tensors():

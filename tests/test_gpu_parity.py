@@ -11,16 +11,24 @@ import pytest
 import oracle
 from tests.gpu_helpers import device_inputs, log, run_gpu
 from tests.invariants import check_invariants
-from tests.parity import compare
+from tests.parity import compare, compare_bits
 from workloads import Workload, f32_to_bf16_bits, make_workload
 
 pytestmark = pytest.mark.gpu
 
 
-def oracle_of(wl, W=None, rows=None):
+def oracle_of(wl, W=None, rows=None, bits=False):
+    bits_ld = (wl.V + 127) // 128 * 16 if bits else None
     return oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k, wl.top_p,
                                    wl.min_p, wl.optin_rows, wl.seeds, wl.positions,
-                                   wl.W if W is None else W, rows=rows)
+                                   wl.W if W is None else W, rows=rows, bits_ld=bits_ld)
+
+
+def check_bits(wl, got, ref, rows=None, min_rows=1):
+    errs, n = compare_bits(got, ref, wl.optin_rows, rows=rows)
+    log(f"  {wl.name}: {n} overflow bitmask rows checked")
+    assert errs == [], errs[:10]
+    assert n >= min_rows, n
 
 
 def check(wl, got, ref, W=None, rows=None, max_flagged_frac=0.05):
@@ -75,6 +83,18 @@ def test_workload_parity_full(index):
     log(f"case workload {index} {wl.name} B={wl.B} V={wl.V} W={wl.W}")
     got = run_gpu(wl)
     check(wl, got, oracle_of(wl))
+
+
+@pytest.mark.parametrize("index,W", [(2, 2), (3, 512), (4, 8192)])
+def test_overflow_support_bitmasks(index, W):
+    # Workload 2 (float32, general path) with W = 2, workload 3 (stash mode) with W = 512 and
+    # workload 4 (compaction mode) at its own W: most captured rows overflow.
+    wl = make_workload(index, W=W)
+    log(f"case support bitmasks workload {index} W={W}")
+    got = run_gpu(wl, bits=True)
+    ref = oracle_of(wl, bits=True)
+    check(wl, got, ref)
+    check_bits(wl, got, ref, min_rows=len(wl.optin_rows) // 2)
 
 
 def test_workload4_wide_packed_width():
@@ -313,8 +333,9 @@ def test_single_read_path_rows(V):
         wl = make(f"fast_V{V}_W{W}", x, "bf16", T=np.array(cols[0]), k=np.array(cols[1]),
                   p=np.array(cols[2]), mp=np.array(cols[3]), W=W)
         log(f"case single-read path V={V} W={W}: {names}")
-        got = run_gpu(wl)
-        ref = oracle_of(wl)
+        got = run_gpu(wl, bits=True)
+        ref = oracle_of(wl, bits=True)
         errs, stats = compare(got, ref, wl.optin_rows)
         assert errs == [], [(e, names[int(e.split()[1].rstrip(':'))]) if e.startswith("row") else e for e in errs]
         check(wl, got, ref, max_flagged_frac=0.2)
+        check_bits(wl, got, ref, min_rows=0 if W == 2048 else 10)

@@ -28,6 +28,21 @@ def test_library_special_cases():
     assert pins.pin_special_cases(oracle.sample_row) == []
 
 
+def test_support_bitmask():
+    assert pins.pin_support_bitmask(oracle.support_bitmask, oracle.sample_row) == []
+
+
+def test_support_bitmask_pin_catches_planted_mistakes():
+    src = inspect.getsource(osampler.support_bitmask)
+    for old, new in (('bitorder="little"', 'bitorder="big"'),
+                     ("keep[np.asarray(support, dtype=np.int64)] = True",
+                      "keep[np.asarray(support, dtype=np.int64)[:-1]] = True")):
+        assert src.count(old) == 1
+        ns = dict(vars(osampler))
+        exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+        assert pins.pin_support_bitmask(ns["support_bitmask"], oracle.sample_row), old
+
+
 def test_race_distribution():
     assert pins.pin_race_distribution(oracle.sample_row) == []
 
@@ -102,6 +117,13 @@ def test_overflow_and_status_rows():
     # OVERFLOW: the packed prefix is the first W of the full order; logprobs use the full support.
     full = res.rows[0]
     assert full.L == V and res.packed_ids[0].tolist() == full.support[:16].tolist()
+    # The bitmask is written for the OVERFLOW slot only; it holds every finite token of row 0.
+    res_b = oracle.sample_with_mask(x, "f32", T, k, p, mp, opt, np.arange(6, dtype=np.uint64),
+                                    np.zeros(6, np.uint64), 16, bits_ld=48)
+    assert res_b.support_bits.shape == (6, 48)
+    assert not res_b.support_bits[1:].any()
+    assert np.unpackbits(res_b.support_bits[0], bitorder="little")[:V].all()
+    assert not np.unpackbits(res_b.support_bits[0], bitorder="little")[V:].any()
     xr = lambda r: x[r].astype(np.float64)
     assert check_invariants(res.tokens, res.row_status, res.packed_ids, res.logprobs, res.lengths,
                             res.selected_logprob, opt, 16, xr, T) == []

@@ -7,7 +7,7 @@ import os
 import numpy as np
 
 import oracle
-from tests.parity import compare
+from tests.parity import BITS_SENTINEL, compare, compare_bits
 
 
 def _tie_batch():
@@ -77,3 +77,38 @@ def test_status_rows_compare_nan_selected_logprob_as_equal():
     assert compare(got, ref, np.arange(2))[0] == []
     got["selected_logprob"][1] = np.nan
     assert compare(got, ref, np.arange(2))[0]
+
+
+def _bits_batch():
+    # The tie example with W = 2: support {0, 1, 2} overflows, bitmask byte 0b111.
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tie_example.json")))
+    B = 4
+    x = np.tile(np.log(np.array(g["probs"], np.float32)), (B, 1)).astype(np.float32)
+    T = np.ones(B, np.float32)
+    T[3] = 0.0  # greedy: width 1, never overflows
+    k = np.full(B, g["top_k"], np.int32)
+    p = np.full(B, g["top_p"], np.float32)
+    opt = np.arange(B, dtype=np.int32)
+    ref = oracle.sample_with_mask(x, "f32", T, k, p, np.zeros(B, np.float32), opt,
+                                  np.arange(B, dtype=np.uint64), np.zeros(B, np.uint64), 2,
+                                  bits_ld=16)
+    bits = ref.support_bits.copy()
+    bits[3] = BITS_SENTINEL
+    got = {"row_status": ref.row_status.copy(), "support_bits": bits}
+    return got, ref, opt
+
+
+def test_bitmask_harness():
+    got, ref, opt = _bits_batch()
+    assert ref.support_bits[0, 0] == 7 and not ref.support_bits[0, 1:].any()
+    errs, n = compare_bits(got, ref, opt)
+    assert errs == [] and n == 3
+    bad = copy.deepcopy(got)
+    bad["support_bits"][1, 0] ^= 0x08  # an extra token
+    assert compare_bits(bad, ref, opt)[0]
+    bad = copy.deepcopy(got)
+    bad["support_bits"][2, 0] = 3  # a dropped tied token
+    assert compare_bits(bad, ref, opt)[0]
+    bad = copy.deepcopy(got)
+    bad["support_bits"][3, 5] = 0  # a row without OVERFLOW written
+    assert compare_bits(bad, ref, opt)[0]

@@ -15,6 +15,7 @@ from typing import NamedTuple, Optional
 import torch  # must come first: the library binds to the HIP runtime PyTorch has loaded
 
 __all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "workspace_size",
+           "support_bits_ld",
            "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
            "MAX_PACKED_WIDTH", "TscError"]
@@ -47,6 +48,11 @@ def library() -> ctypes.CDLL:
     lib.tsc_sample_with_mask.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P, I64, P, P, I32,
                                          P, P, P, P, P, P, P, SZ, P]
     lib.tsc_sample_with_mask.restype = I32
+    lib.tsc_sample_with_mask_bits.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P, I64, P, P,
+                                              I32, P, P, P, P, P, P, P, I64, P, SZ, P]
+    lib.tsc_sample_with_mask_bits.restype = I32
+    lib.tsc_support_bits_ld.argtypes = [I64]
+    lib.tsc_support_bits_ld.restype = I64
     lib.tsc_workspace_size.argtypes = [I64, I64, I64, I32, I32]
     lib.tsc_workspace_size.restype = SZ
     lib.tsc_status_string.argtypes = [I32]
@@ -64,11 +70,19 @@ class SampleOutput(NamedTuple):
     logprobs: Optional[torch.Tensor]  # float32 [R, W] (None in selected mode)
     selected_logprob: torch.Tensor  # float32 [R]
     row_status: torch.Tensor        # int8 [B]
+    # uint8 [R, bits_ld]: the support bitmask of each OVERFLOW slot (bit i % 8 of byte i / 8);
+    # rows of other slots are left as they were. None unless requested.
+    support_bits: Optional[torch.Tensor] = None
 
 
 def workspace_size(B: int, V: int, R: int, W: int, dtype: torch.dtype) -> int:
     dt = TSC_DTYPE_BF16 if dtype == torch.bfloat16 else TSC_DTYPE_F32
     return int(library().tsc_workspace_size(B, V, R, W, dt))
+
+
+def support_bits_ld(V: int) -> int:
+    """Smallest row stride in bytes of a support bitmask buffer for vocabulary size V."""
+    return int(library().tsc_support_bits_ld(V))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -104,7 +118,7 @@ class PreparedSample:
                  top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
                  seeds: torch.Tensor, positions: torch.Tensor, W: int,
                  return_logprobs: bool = True, out: Optional[SampleOutput] = None,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, return_bits: bool = False):
         self._lib = library()
         if logits.dim() != 2 or logits.stride(1) != 1:
             raise ValueError("logits must be [B, V] with unit column stride")
@@ -134,9 +148,17 @@ class PreparedSample:
                 logprobs=(torch.empty((R, Wc), dtype=torch.float32, device=dev)
                           if return_logprobs else None),
                 selected_logprob=torch.empty(R, dtype=torch.float32, device=dev),
-                row_status=torch.empty(B, dtype=torch.int8, device=dev))
+                row_status=torch.empty(B, dtype=torch.int8, device=dev),
+                support_bits=(torch.zeros((R, support_bits_ld(V)), dtype=torch.uint8, device=dev)
+                              if return_bits else None))
         else:
             _check_out(out, B, R, W, dev)
+            sb = out.support_bits
+            if sb is not None and (sb.device != dev or sb.dtype != torch.uint8 or sb.dim() != 2
+                                   or sb.shape[0] != R or sb.stride(1) != 1
+                                   or (R > 1 and sb.stride(0) != sb.shape[1])):
+                raise ValueError(f"out.support_bits must be a contiguous uint8 tensor [{R}, ld] "
+                                 f"on {dev}")
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         self.out = out
         self._shape = (tuple(logits.shape), tuple(logits.stride()), logits.dtype, dev)
@@ -149,13 +171,15 @@ class PreparedSample:
             _ptr(out.packed_ids) if R else None,
             _ptr(out.logprobs) if (R and out.logprobs is not None) else None,
             _ptr(out.lengths) if R else None, _ptr(out.selected_logprob) if R else None,
+            _ptr(out.support_bits) if (R and out.support_bits is not None) else None,
+            int(out.support_bits.shape[1]) if out.support_bits is not None else 0,
             None, 0, s.cuda_stream)
 
     def __call__(self, logits: torch.Tensor, check: bool = True) -> SampleOutput:
         if check and (tuple(logits.shape), tuple(logits.stride()), logits.dtype,
                       logits.device) != self._shape:
             raise ValueError("logits must match the prepared shape, strides, dtype and device")
-        code = self._lib.tsc_sample_with_mask(logits.data_ptr(), *self._tail)
+        code = self._lib.tsc_sample_with_mask_bits(logits.data_ptr(), *self._tail)
         if code != 0:
             raise TscError(code, self._lib.tsc_status_string(code).decode())
         return self.out
@@ -164,24 +188,26 @@ class PreparedSample:
 def prepare(logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
             top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
             seeds: torch.Tensor, positions: torch.Tensor, W: int, return_logprobs: bool = True,
-            out: Optional[SampleOutput] = None,
-            stream: Optional[torch.cuda.Stream] = None) -> PreparedSample:
+            out: Optional[SampleOutput] = None, stream: Optional[torch.cuda.Stream] = None,
+            return_bits: bool = False) -> PreparedSample:
     """Validate the arguments once; the returned object samples a logits tensor per call."""
     return PreparedSample(logits, temperature, top_k, top_p, min_p, optin_rows, seeds, positions,
-                          W, return_logprobs, out, stream)
+                          W, return_logprobs, out, stream, return_bits)
 
 
 def sample_with_mask(logits: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor,
                      top_p: torch.Tensor, min_p: torch.Tensor, optin_rows: torch.Tensor,
                      seeds: torch.Tensor, positions: torch.Tensor, W: int,
                      return_logprobs: bool = True, out: Optional[SampleOutput] = None,
-                     stream: Optional[torch.cuda.Stream] = None) -> SampleOutput:
+                     stream: Optional[torch.cuda.Stream] = None,
+                     return_bits: bool = False) -> SampleOutput:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16, unit column stride)
     and capture the support of the rows listed in ``optin_rows`` (int32, ascending).
 
     ``temperature``/``top_p``/``min_p`` are float32 [B], ``top_k`` int32 [B], ``seeds`` and
     ``positions`` int64 [B] holding the uint64 bit patterns. Outputs are allocated on the
     logits' device unless ``out`` supplies them. Runs asynchronously on ``stream`` (default: the
-    current stream)."""
+    current stream). With ``return_bits`` (or ``out.support_bits`` given) the support of every
+    OVERFLOW slot is also written as a bitmask."""
     return PreparedSample(logits, temperature, top_k, top_p, min_p, optin_rows, seeds, positions,
-                          W, return_logprobs, out, stream)(logits, check=False)
+                          W, return_logprobs, out, stream, return_bits)(logits, check=False)

@@ -50,13 +50,15 @@ size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dt
   return 0;
 }
 
-int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64_t V, int64_t ld,
-                             const float* temperature, const int32_t* top_k, const float* top_p,
-                             const float* min_p, const int32_t* optin_rows, int64_t R,
-                             const uint64_t* seeds, const uint64_t* positions, int32_t W,
-                             int32_t* tokens, int8_t* row_status, int32_t* packed_ids,
-                             float* logprobs, int32_t* lengths, float* selected_logprob,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, int64_t V,
+                                  int64_t ld, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, const float* min_p,
+                                  const int32_t* optin_rows, int64_t R, const uint64_t* seeds,
+                                  const uint64_t* positions, int32_t W, int32_t* tokens,
+                                  int8_t* row_status, int32_t* packed_ids, float* logprobs,
+                                  int32_t* lengths, float* selected_logprob,
+                                  uint8_t* support_bits, int64_t bits_ld, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   (void)workspace;
   if (dtype != TSC_DTYPE_F32 && dtype != TSC_DTYPE_BF16) return TSC_ERR_INVALID_ARGUMENT;
   if (B < 0 || V < 1 || V > INT32_MAX - 16 || ld < V || R < 0 || R > B)
@@ -72,17 +74,37 @@ int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64
     if (!optin_rows || !packed_ids || !lengths || !selected_logprob) return TSC_ERR_INVALID_ARGUMENT;
     if (W < 1) return TSC_ERR_INVALID_ARGUMENT;
     if (W > TSC_MAX_PACKED_WIDTH) return TSC_ERR_UNSUPPORTED;
+    if (support_bits != nullptr &&
+        (bits_ld < tsc_support_bits_ld(V) || bits_ld % 16 != 0 ||
+         (reinterpret_cast<uintptr_t>(support_bits) & 15u) != 0))
+      return TSC_ERR_INVALID_ARGUMENT;
   }
   if (workspace_bytes < tsc_workspace_size(B, V, R, W, dtype)) return TSC_ERR_WORKSPACE;
 
   tsc::SampleArgs a{logits, B, V, ld, temperature, top_k, top_p, min_p, optin_rows, R,
                     seeds, positions, R > 0 ? W : 1, tokens, row_status, packed_ids,
-                    logprobs, lengths, selected_logprob};
+                    logprobs, lengths, selected_logprob,
+                    R > 0 ? reinterpret_cast<uint32_t*>(support_bits) : nullptr, bits_ld / 4};
   (void)hipGetLastError();  // start from a clean error state so a launch error is ours
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t err = dtype == TSC_DTYPE_F32 ? launch_sampler<TSC_DTYPE_F32>(a, s)
                                                 : launch_sampler<TSC_DTYPE_BF16>(a, s);
   return err == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
+
+int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64_t V, int64_t ld,
+                             const float* temperature, const int32_t* top_k, const float* top_p,
+                             const float* min_p, const int32_t* optin_rows, int64_t R,
+                             const uint64_t* seeds, const uint64_t* positions, int32_t W,
+                             int32_t* tokens, int8_t* row_status, int32_t* packed_ids,
+                             float* logprobs, int32_t* lengths, float* selected_logprob,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return tsc_sample_with_mask_bits(logits, dtype, B, V, ld, temperature, top_k, top_p, min_p,
+                                   optin_rows, R, seeds, positions, W, tokens, row_status,
+                                   packed_ids, logprobs, lengths, selected_logprob, nullptr, 0,
+                                   workspace, workspace_bytes, stream);
+}
+
+int64_t tsc_support_bits_ld(int64_t V) { return V < 1 ? 0 : tsc::bitmask_words(V) * 4; }
 
 }  // extern "C"

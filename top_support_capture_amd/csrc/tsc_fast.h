@@ -479,6 +479,17 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 
 // Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
 // go through the general path instead; `slot` is then already set.
+// Sets the bitmask bit of every survivor (value >= x_cut) of one wave's candidate list.
+__device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, float x_cut,
+                                            uint32_t id0, uint32_t* brow) {
+  for (uint32_t i = lane_id(); i < n; i += kWaveSize) {
+    const uint32_t wd = cand[i];
+    if (!(__uint_as_float(wd & 0xFFFF0000u) >= x_cut)) continue;
+    const uint32_t id = id0 + (wd & 0x3FFFu);
+    atomicOr(brow + (id >> 5), 1u << (id & 31u));
+  }
+}
+
 template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
 template <> struct LayoutOf<true> { using type = LayoutCompact; };
 
@@ -1014,6 +1025,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         else
           bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+        if (a.bits != nullptr && capture && fs.L > (uint32_t)a.W) {
+          // A support wider than W is also written as a bitmask: cleared here, and its bits set
+          // by the capture with atomic ORs. The device-scope release waits until the clearing
+          // stores have reached L2, before any wave can see scan_ready and start its ORs.
+          uint4* z = reinterpret_cast<uint4*>(a.bits + slot * a.bits_ld);
+          const uint32_t n16 = (uint32_t)(bitmask_words(a.V) / 4);
+          for (uint32_t i = lane; i < n16; i += kWaveSize) z[i] = make_uint4(0u, 0u, 0u, 0u);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        }
       }
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
@@ -1166,6 +1186,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     int32_t* out_ids = a.packed_ids + slot * a.W;
     float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
     uint32_t* stage = reinterpret_cast<uint32_t*>(lds + LY::kOffStage);
+    uint32_t* const brow = (a.bits != nullptr && L > W) ? a.bits + slot * a.bits_ld : nullptr;
+    if (brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // Bits of the bins of the support: bi <= dspan.
     const uint32_t nbits = 32u - (uint32_t)__builtin_clz(dspan | 1u);
     for (;;) {
@@ -1199,6 +1221,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           }
         }
       }
+      if (brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
       lds_publish_step(&fs.staged);
     }
     // Copy-out of the stage, in slices of 1024 positions.
@@ -1230,6 +1253,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
     int32_t* out_ids = a.packed_ids + slot * a.W;
     float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+    uint32_t* const brow = (a.bits != nullptr && L > W) ? a.bits + slot * a.bits_ld : nullptr;
+    if (brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     for (;;) {
       const uint32_t cj = lds_claim(&fs.cap_next);
       if (cj >= (uint32_t)kWaves) break;
@@ -1252,6 +1277,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
         }
       }
+      if (brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
     }
   }
   }

@@ -35,7 +35,14 @@ struct SampleArgs {
   float* logprobs;
   int32_t* lengths;
   float* selected_logprob;
+  uint32_t* bits;   // [R, bits_ld] support bitmasks of OVERFLOW slots, or null
+  int64_t bits_ld;  // row stride of `bits` in 32-bit words (a multiple of 4)
 };
+
+// Words of a support bitmask row that a kernel writes: the bits of ids 0..V-1 (bit i in word
+// i / 32 at position i % 32, the little-endian bit order of a byte array), zero-padded to a whole
+// number of 16-byte units.
+__host__ __device__ inline int64_t bitmask_words(int64_t V) { return (V + 127) / 128 * 4; }
 
 constexpr int kSortCap = TSC_MAX_PACKED_WIDTH;                 // u64 entries in the LDS buffer
 constexpr size_t kGeneralDynLds = (size_t)kSortCap * sizeof(uint64_t);
@@ -372,6 +379,19 @@ __device__ __forceinline__ void general_row(const SampleArgs& a, int64_t b, int6
 
   // ---- 5. Ordered capture ---------------------------------------------------------------------
   const uint32_t W = (uint32_t)a.W;
+  if (a.bits != nullptr && L > W) {
+    // The exact support of a row wider than W, as a bitmask: each thread builds whole words.
+    uint32_t* brow = a.bits + slot * a.bits_ld;
+    const int64_t nw = bitmask_words(V);
+    for (int64_t j = tid; j < nw; j += kThreads) {
+      uint32_t word = 0;
+      const int64_t i0 = j * 32;
+      const int n = i0 >= V ? 0 : (V - i0 < 32 ? (int)(V - i0) : 32);
+      for (int e = 0; e < n; ++e)
+        word |= (uint32_t)surv((int32_t)(i0 + e), (uint32_t)row[i0 + e]) << e;
+      brow[j] = word;
+    }
+  }
   const uint32_t len = L < W ? L : W;
   // Gather predicate: everything when the support fits the LDS buffer, else the first W in
   // order: keys above the W-th key, plus the lowest ids of its tie group.
