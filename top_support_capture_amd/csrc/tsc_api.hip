@@ -13,17 +13,17 @@ constexpr int32_t kVersion = 100;  // 0.1.0
 
 // One workgroup per row. Rows the single-read path serves run there; every other row runs the
 // general multi-pass algorithm inside the same launch.
-template <int DT>
+template <int DT, bool BITS>
 hipError_t launch_sampler(const tsc::SampleArgs& a, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_fast_kernel<DT>),
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_fast_kernel<DT, BITS>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)tsc::kFastDynLds);
   });
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(tsc::sample_fast_kernel<DT>, dim3((unsigned)a.B), dim3(tsc::kThreads),
+  hipLaunchKernelGGL((tsc::sample_fast_kernel<DT, BITS>), dim3((unsigned)a.B), dim3(tsc::kThreads),
                      tsc::kFastDynLds, stream, a);
   return hipGetLastError();
 }
@@ -87,8 +87,11 @@ int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, 
                     R > 0 ? reinterpret_cast<uint32_t*>(support_bits) : nullptr, bits_ld / 4};
   (void)hipGetLastError();  // start from a clean error state so a launch error is ours
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t err = dtype == TSC_DTYPE_F32 ? launch_sampler<TSC_DTYPE_F32>(a, s)
-                                                : launch_sampler<TSC_DTYPE_BF16>(a, s);
+  const bool bits = a.bits != nullptr;
+  const hipError_t err =
+      dtype == TSC_DTYPE_F32
+          ? (bits ? launch_sampler<TSC_DTYPE_F32, true>(a, s) : launch_sampler<TSC_DTYPE_F32, false>(a, s))
+          : (bits ? launch_sampler<TSC_DTYPE_BF16, true>(a, s) : launch_sampler<TSC_DTYPE_BF16, false>(a, s));
   return err == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
 

@@ -94,7 +94,7 @@ struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> 
   static constexpr int kTableStride = kStashPerWave * 16;
   static constexpr int kOffRank = kOffStashCh;              // u16 [16][512]
 };
-static_assert(kThetaBins % kWaveSize == 0 && kThetaBins <= kThreads, "theta histogram scan");
+static_assert(kThetaBins % (2 * kWaveSize) == 0 && kThetaBins / 2 <= kThreads, "theta histogram");
 static_assert(kTableBytes + kMaskBins * 8 <= LayoutStash::kTableStride, "tables fit a slice");
 static_assert(LayoutStash::kCandCap * 2 <= kStashPerWave * 4, "ranks fit a chunk-index slice");
 // Compaction mode: the candidates, the tables, the stage.
@@ -120,7 +120,7 @@ enum FastDecision : int32_t { kProceed = 0, kNonfinite = 1, kNoSupport = 2, kFal
 // Per-wave partial results exchanged through LDS (one barrier per exchange).
 struct FastShared {
   uint64_t red[kWaves];
-  uint32_t theta_hist[kThetaBins];
+  uint32_t theta_hist[kThetaBins / 2];  // two u16 counts per word: distance 2j low, 2j+1 high
   uint32_t kmax0_w[kWaves];
   uint32_t ndone;              // waves whose stream has ended
   uint32_t scan_ready;          // set by wave 0 once the decision and the bin scan are published
@@ -493,7 +493,7 @@ __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, fl
 template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
 template <> struct LayoutOf<true> { using type = LayoutCompact; };
 
-template <bool NEED_P, bool COMPACT, int LOADS>
+template <bool NEED_P, bool COMPACT, int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
                                               float T, int32_t k, float p, float mp,
                                               uint64_t seed, uint64_t pos, unsigned char* lds,
@@ -558,7 +558,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(lds + LY::kOffCnt);
   hcnt[tid] = 0u;  // published by the first exchange below
-  if (tid < (uint32_t)kThetaBins) fs.theta_hist[tid] = 0u;
+  if (tid < (uint32_t)kThetaBins / 2) fs.theta_hist[tid] = 0u;
   if (tid == 0) {
     fs.ndone = 0u;
     fs.scan_ready = 0u;
@@ -713,8 +713,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const uint32_t key1 = key_of<E>(__float_as_uint(lm1) >> 16);
     const uint32_t dist0 = kmax0 - key0;
     const uint32_t dist1 = key1 >= kmax0 ? 0u : kmax0 - key1;
-    if (dist0 < (uint32_t)kThetaBins && (key0 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist0], 1u);
-    if (dist1 < (uint32_t)kThetaBins && (key1 >> 7) != 0u) atomicAdd(&fs.theta_hist[dist1], 1u);
+    if (dist0 < (uint32_t)kThetaBins && (key0 >> 7) != 0u)
+      atomicAdd(&fs.theta_hist[dist0 >> 1], 1u << (16u * (dist0 & 1u)));
+    if (dist1 < (uint32_t)kThetaBins && (key1 >> 7) != 0u)
+      atomicAdd(&fs.theta_hist[dist1 >> 1], 1u << (16u * (dist1 & 1u)));
   }
   if (a.R <= kThreads) slot_step2(a, b, sscan, fs);
   lds_barrier();
@@ -730,13 +732,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   pin();
   uint32_t theta_key;
   {
+    // At most 2048 samples, so a u16 count never carries into its neighbour.
     constexpr int kPer = kThetaBins / kWaveSize;
     uint32_t hc[kPer];
     uint32_t lsum = 0;
 #pragma unroll
-    for (int q4 = 0; q4 < kPer; ++q4) {
-      hc[q4] = fs.theta_hist[lane * kPer + q4];
-      lsum += hc[q4];
+    for (int q2 = 0; q2 < kPer / 2; ++q2) {
+      const uint32_t two = fs.theta_hist[lane * (kPer / 2) + q2];
+      hc[2 * q2] = two & 0xFFFFu;
+      hc[2 * q2 + 1] = two >> 16;
+      lsum += hc[2 * q2] + hc[2 * q2 + 1];
     }
     uint32_t tot;
     uint32_t run = wave_excl_sum(lsum, tot);
@@ -1025,7 +1030,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         else
           bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
-        if (a.bits != nullptr && capture && fs.L > (uint32_t)a.W) {
+        if (BITS && capture && fs.L > (uint32_t)a.W) {
           // A support wider than W is also written as a bitmask: cleared here, and its bits set
           // by the capture with atomic ORs. The device-scope release waits until the clearing
           // stores have reached L2, before any wave can see scan_ready and start its ORs.
@@ -1186,8 +1191,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     int32_t* out_ids = a.packed_ids + slot * a.W;
     float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
     uint32_t* stage = reinterpret_cast<uint32_t*>(lds + LY::kOffStage);
-    uint32_t* const brow = (a.bits != nullptr && L > W) ? a.bits + slot * a.bits_ld : nullptr;
-    if (brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint32_t* const brow = (BITS && L > W) ? a.bits + slot * a.bits_ld : nullptr;
+    if (BITS && brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // Bits of the bins of the support: bi <= dspan.
     const uint32_t nbits = 32u - (uint32_t)__builtin_clz(dspan | 1u);
     for (;;) {
@@ -1221,7 +1226,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           }
         }
       }
-      if (brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
+      if (BITS && brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
       lds_publish_step(&fs.staged);
     }
     // Copy-out of the stage, in slices of 1024 positions.
@@ -1253,8 +1258,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
     int32_t* out_ids = a.packed_ids + slot * a.W;
     float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
-    uint32_t* const brow = (a.bits != nullptr && L > W) ? a.bits + slot * a.bits_ld : nullptr;
-    if (brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint32_t* const brow = (BITS && L > W) ? a.bits + slot * a.bits_ld : nullptr;
+    if (BITS && brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     for (;;) {
       const uint32_t cj = lds_claim(&fs.cap_next);
       if (cj >= (uint32_t)kWaves) break;
@@ -1277,7 +1282,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
         }
       }
-      if (brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
+      if (BITS && brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
     }
   }
   }
@@ -1285,19 +1290,21 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 }
 
 
-template <int LOADS>
+template <int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b, int64_t& slot,
                                                   float T, int32_t k, float p, float mp,
                                                   uint64_t seed, uint64_t pos, unsigned char* lds,
                                                   FastShared& fs) {
   if (k <= kFastMaxK)
-    return p < 1.0f ? fast_row_bf16<true, false, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                    : fast_row_bf16<false, false, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
-  return p < 1.0f ? fast_row_bf16<true, true, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                  : fast_row_bf16<false, true, LOADS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+    return p < 1.0f ? fast_row_bf16<true, false, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                    : fast_row_bf16<false, false, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+  return p < 1.0f ? fast_row_bf16<true, true, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+                  : fast_row_bf16<false, true, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
 }
 
-template <int DT>
+// BITS: the call passed a support bitmask buffer (a separate instantiation, so that calls without
+// one run no bitmask code at all).
+template <int DT, bool BITS>
 __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
   // The dynamic buffer starts after the static LDS; 256-byte alignment keeps every 16-byte
   // stash access aligned (and the bank mapping of the layout fixed) whatever FastShared's size.
@@ -1319,15 +1326,15 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     if (eligible) {
       const bool done =
           a.V <= kShortMaxV
-              ? fast_row_dispatch<kShortLoads>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-              : fast_row_dispatch<kFastLoads>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+              ? fast_row_dispatch<kShortLoads, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
+              : fast_row_dispatch<kFastLoads, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }
   }
   if (slot == -2) slot = find_capture_slot(a, b, fs.red);
   GeneralShared* sh = reinterpret_cast<GeneralShared*>(lds + kGeneralDynLds);
-  general_row<DT>(a, b, slot, dyn, *sh);
+  general_row<DT, BITS>(a, b, slot, dyn, *sh);
 }
 
 }  // namespace tsc

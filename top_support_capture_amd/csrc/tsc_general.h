@@ -245,7 +245,7 @@ __device__ inline bool row_params_valid(float T, float p, float mp) {
 
 // The whole sampling of row b by the general multi-pass algorithm. `sortbuf` holds kSortCap
 // u64 entries of LDS. Every thread of the workgroup calls it; it returns with the row done.
-template <int DT>
+template <int DT, bool BITS>
 __device__ __forceinline__ void general_row(const SampleArgs& a, int64_t b, int64_t slot, uint64_t* sortbuf,
                             GeneralShared& sh) {
   using E = Elem<DT>;
@@ -379,7 +379,7 @@ __device__ __forceinline__ void general_row(const SampleArgs& a, int64_t b, int6
 
   // ---- 5. Ordered capture ---------------------------------------------------------------------
   const uint32_t W = (uint32_t)a.W;
-  if (a.bits != nullptr && L > W) {
+  if (BITS && a.bits != nullptr && L > W) {
     // The exact support of a row wider than W, as a bitmask: each thread builds whole words.
     uint32_t* brow = a.bits + slot * a.bits_ld;
     const int64_t nw = bitmask_words(V);
@@ -471,7 +471,7 @@ __global__ void __launch_bounds__(kThreads) sample_general_kernel(SampleArgs a) 
   __shared__ GeneralShared sh;
   const int64_t b = blockIdx.x;
   const int64_t slot = find_capture_slot(a, b, sh.red);
-  general_row<DT>(a, b, slot, sortbuf, sh);
+  general_row<DT, true>(a, b, slot, sortbuf, sh);
 }
 
 }  // namespace tsc
