@@ -9,3 +9,4 @@ from .sampler import (  # noqa: F401
     RACE_TIE_EPS, TOP_P_EPS, MIN_P_EPS, RowResult, BatchResult,
     decode_logits, params_valid, sample_row, sample_with_mask, slot_validity, support_bitmask,
 )
+from .replay import ReplayRow, replay, replay_row  # noqa: F401

@@ -231,3 +231,55 @@ def pin_support_bitmask(support_bitmask, sample_row, rng_seed=2, cases=300):
             fails.append(f"mask {got} != {want} for x={xs} k={k} p={p}")
             break
     return fails
+
+
+def pin_replay(replay_row, sample_row, rng_seed=4, cases=200):
+    """The replay of a support under new logits (vLLM article, section "RL training side:
+    computing pi_theta with the mask": the training logits masked to the support, then the
+    log-softmax at the sampled token).
+    - The pages' tie example replayed on its own logits gives the closed forms ln 1/2, ln 1/4,
+      ln 1/4, and -inf for a token outside the support.
+    - Random rows against the page's recipe run with a library routine: scipy's log_softmax of
+      the logits divided by T with every token outside the support set to -inf.
+    - Replaying the oracle sampler's own support on the same logits reproduces its logprobs.
+    - Adding a constant to every logit changes nothing."""
+    from scipy.special import log_softmax
+    fails = []
+    g = json.load(open(os.path.join(GOLDEN, "tie_example.json")))
+    x = np.log(np.array(g["probs"], dtype=np.float32)).astype(np.float32).astype(np.float64)
+    S = np.array(g["expected_support_ids"])
+    want = {0: math.log(0.5), 1: math.log(0.25), 2: math.log(0.25), 3: -math.inf}
+    for tok, w in want.items():
+        r = replay_row(x, 1.0, S, tok)
+        if not (r.selected_logprob == w or abs(r.selected_logprob - w) < 1e-7):
+            fails.append(f"tie example replay token {tok}: {r.selected_logprob} != {w}")
+    rng = np.random.default_rng(rng_seed)
+    for _ in range(cases):
+        V = int(rng.integers(2, 60))
+        xs = np.round(rng.standard_normal(V) * 3, 2)
+        T = float(np.float32(rng.choice([0.5, 1.0, 1.7])))
+        n = int(rng.integers(1, V + 1))
+        S = rng.choice(V, n, replace=False)
+        tok = int(rng.integers(0, V))
+        keep = np.zeros(V, bool)
+        keep[S] = True
+        ref = log_softmax(np.where(keep, xs / T, -np.inf))
+        r = replay_row(xs, T, S, tok)
+        if not np.allclose(r.logprobs, ref[S], rtol=0, atol=1e-12):
+            fails.append(f"replay logprobs differ from log_softmax for x={xs.tolist()} S={S} T={T}")
+            break
+        if not (r.selected_logprob == ref[tok] or abs(r.selected_logprob - ref[tok]) < 1e-12):
+            fails.append(f"replay token {tok}: {r.selected_logprob} != {ref[tok]}")
+            break
+        shifted = replay_row(xs + 7.25, T, S, tok)
+        if not np.allclose(shifted.logprobs, r.logprobs, rtol=0, atol=1e-9):
+            fails.append("replay is not shift invariant")
+            break
+        k = int(rng.integers(1, V + 1))
+        sr = sample_row(xs, T, k, float(rng.choice([0.6, 1.0])), 0.0, 1, 0)
+        rr = replay_row(xs, T, sr.support, sr.token)
+        if (not np.allclose(rr.logprobs, sr.logprobs.astype(np.float64), rtol=0, atol=2e-6)
+                or abs(rr.selected_logprob - float(sr.logprobs[list(sr.support).index(sr.token)])) > 2e-6):
+            fails.append(f"replay of the sampler's own support differs for x={xs.tolist()}")
+            break
+    return fails

@@ -43,6 +43,46 @@ def test_support_bitmask_pin_catches_planted_mistakes():
         assert pins.pin_support_bitmask(ns["support_bitmask"], oracle.sample_row), old
 
 
+def test_replay():
+    assert pins.pin_replay(oracle.replay_row, oracle.sample_row) == []
+
+
+@pytest.mark.parametrize("old,new", [
+    ("z = (xs - m) / T", "z = (xs - m)"),
+    ("lse = np.log(np.sum(np.exp(z)))", "lse = np.log(np.sum(np.exp((x[np.isfinite(x)] - m) / T)))"),
+    ("sel = (x[token] - m) / T - lse", "sel = (x[token] - m) / T + lse"),
+    ("sel = -np.inf", "sel = (x[token] - m) / T - lse"),
+])
+def test_replay_pin_catches_planted_mistakes(old, new):
+    import importlib
+    oreplay = importlib.import_module("oracle.replay")
+    src = inspect.getsource(oreplay.replay_row)
+    assert src.count(old) == 1
+    ns = dict(vars(oreplay))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    assert pins.pin_replay(ns["replay_row"], oracle.sample_row, cases=60), old
+
+
+def test_replay_batch_statuses():
+    # Packed rows, an OVERFLOW row read from its bitmask, and the status rows.
+    x = np.log(np.array([[0.4, 0.2, 0.2, 0.1, 0.1]] * 6, np.float32))
+    x[3, 1] = np.nan
+    ids = np.array([[0, 1, 2, 0], [0, 1, 2, 0], [0, 1, 0, 0], [0, 1, 2, 0], [0, 1, 2, 0],
+                    [0, 1, 2, 0]], np.int32)
+    lengths = np.array([3, 3, 2, 3, 0, 3], np.int32)
+    cs = np.array([0, 0, 1, 0, 0, 3], np.int8)
+    bits = np.zeros((6, 16), np.uint8)
+    bits[2, 0] = 0b00111  # the full support {0, 1, 2} of the overflowing row
+    T = np.array([1, 1, 1, 1, 1, 1], np.float32)
+    tokens = np.array([0, 4, 1, 0, 0, 0], np.int32)
+    sel, lps, st = oracle.replay(x, "f32", T, ids, lengths, tokens, cs, bits)
+    assert st.tolist() == [0, 0, 0, 3, 4, 3]
+    assert abs(sel[0] - math.log(0.5)) < 1e-6 and sel[1] == -np.inf
+    assert abs(sel[2] - math.log(0.25)) < 1e-6
+    assert np.allclose(lps[2, :2], [math.log(0.5), math.log(0.25)], atol=1e-6)
+    assert np.isnan(sel[3:]).all()
+
+
 def test_race_distribution():
     assert pins.pin_race_distribution(oracle.sample_row) == []
 
