@@ -140,6 +140,45 @@ int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, 
  * to a multiple of 16 (the smallest valid bits_ld); 0 for V < 1. */
 int64_t tsc_support_bits_ld(int64_t V);
 
+/*
+ * tsc_replay_logprob -- the log-probability of each row's sampled token under new logits,
+ * normalized over the support captured for that row (vLLM "Sampling Mask / Distribution Replay"
+ * article, section "RL training side: computing pi_theta with the mask": the training logits
+ * are masked to the returned support, every other token at -inf, and the log-softmax is taken
+ * at the sampled token). With z_i = x_i / T:
+ *     selected_logprob[j] = z_a - ln sum_{i in S_j} exp(z_i)      (a = tokens[j])
+ * T = 1 is the article's recipe; passing the sampling temperature puts the result on the scale of
+ * the sampler's own logprobs. A token outside S_j gets -inf.
+ *
+ * logits       [N, V] row-major, row stride ld >= V elements, float32 or bfloat16 (dtype): row j
+ *              holds the new logits of the position captured in slot j. Read only.
+ * temperature  [N] float32: a normal positive finite value (else INVALID_PARAM).
+ * packed_ids, lengths  [N, W] int32 and [N] int32, as tsc_sample_with_mask writes them: the
+ *              support of row j is its first lengths[j] ids (1 <= lengths[j] <= W, ids in
+ *              [0, V), distinct), unless its capture overflowed.
+ * capture_status [N] int8 or NULL (all TSC_ROW_OK): the capture's row status. For
+ *              TSC_ROW_OVERFLOW the support is read from support_bits; for a status >= 2 the row
+ *              gets that status and a NaN logprob.
+ * support_bits [N, bits_ld] uint8 or NULL: bitmasks as tsc_sample_with_mask_bits writes them
+ *              (bit i % 8 of byte i / 8; bits past V ignored); bits_ld >= ceil(V / 8) bytes.
+ * tokens       [N] int32: the sampled token of each row, in [0, V).
+ * selected_logprob [N] float32 out; NaN unless row_status is TSC_ROW_OK.
+ * logprobs     [N, W] float32 out or NULL: the logprob of each of the first lengths[j] packed ids
+ *              (for an overflowing row, of its packed prefix), normalized over the full support.
+ * row_status   [N] int8 out: TSC_ROW_OK; TSC_ROW_INVALID_PARAM (temperature, token, length, an
+ *              id out of range, an empty support, OVERFLOW without support_bits);
+ *              TSC_ROW_NONFINITE (a support logit is NaN or +inf); TSC_ROW_NO_SUPPORT (every
+ *              support logit is -inf); or the capture status >= 2 it was given.
+ * Asynchronous on `stream`; allocates nothing. Returns TSC_OK or TSC_ERR_* (host checks: sizes,
+ * dtype, null pointers, alignment of logits, bits_ld).
+ */
+int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld,
+                           const float* temperature, const int32_t* packed_ids,
+                           const int32_t* lengths, int32_t W, const int8_t* capture_status,
+                           const uint8_t* support_bits, int64_t bits_ld, const int32_t* tokens,
+                           float* selected_logprob, float* logprobs, int8_t* row_status,
+                           void* stream);
+
 /* Device scratch bytes tsc_sample_with_mask needs for these sizes (currently always 0). */
 size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dtype);
 

@@ -23,9 +23,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["tsc_sample_with_mask", "tsc_sample_with_mask_bits",
-                                    "tsc_status_string", "tsc_support_bits_ld", "tsc_version",
-                                    "tsc_workspace_size"]
+    assert declared_functions() == ["tsc_replay_logprob", "tsc_sample_with_mask",
+                                    "tsc_sample_with_mask_bits", "tsc_status_string",
+                                    "tsc_support_bits_ld", "tsc_version", "tsc_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -85,6 +85,26 @@ def test_support_bits_row_size(lib):
 def test_bits_argument_checks(lib, kw, code):
     # Every case returns before any HIP call, so this runs without a GPU.
     assert _call_bits(lib, **kw) == code
+
+
+def _call_replay(lib, **kw):
+    args = dict(logits=0x1000, dtype=1, N=4, V=100, ld=100, temperature=8, packed_ids=8,
+                lengths=8, W=16, capture_status=None, support_bits=None, bits_ld=0, tokens=8,
+                selected_logprob=8, logprobs=None, row_status=8, stream=None)
+    args.update(kw)
+    return lib.tsc_replay_logprob(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 1), (dict(N=-1), 1), (dict(V=0), 1), (dict(ld=50), 1), (dict(W=0), 1),
+    (dict(W=16385), 2), (dict(logits=0x1001), 1), (dict(logits=None), 1),
+    (dict(temperature=None), 1), (dict(packed_ids=None), 1), (dict(lengths=None), 1),
+    (dict(tokens=None), 1), (dict(selected_logprob=None), 1), (dict(row_status=None), 1),
+    (dict(support_bits=0x2000, bits_ld=12), 1), (dict(N=0), 0),
+])
+def test_replay_argument_checks(lib, kw, code):
+    # Every case returns before any HIP call, so this runs without a GPU.
+    assert _call_replay(lib, **kw) == code
 
 
 def test_binding_rejects_bad_tensors():

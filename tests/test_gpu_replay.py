@@ -1,0 +1,183 @@
+"""Parity of the replay kernel (tsc_replay_logprob) with the CPU oracle (needs an MI355X).
+
+Supports and tokens always come from the CPU oracle's sampler, never from the library; both
+sides then replay them on the same new logits. Every case prints its name before touching the
+GPU."""
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import log, logits_tensor
+from workloads import make_workload, perturbed_logits
+
+pytestmark = pytest.mark.gpu
+
+LP_TOL = 1e-5
+
+
+def run_replay(logits, dtype, T, ids, lengths, tokens, cs=None, bits=None, return_logprobs=True):
+    import top_support_capture_amd as tsc
+    dev = "cuda:0"
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+    out = tsc.replay_logprob(logits_tensor(logits, dtype), t(T, torch.float32),
+                             t(ids, torch.int32), t(lengths, torch.int32), t(tokens, torch.int32),
+                             None if cs is None else t(cs, torch.int8),
+                             None if bits is None else t(bits, torch.uint8),
+                             return_logprobs=return_logprobs)
+    torch.cuda.synchronize()
+    return (out.selected_logprob.cpu().numpy(),
+            None if out.logprobs is None else out.logprobs.cpu().numpy(),
+            out.row_status.cpu().numpy())
+
+
+def compare_replay(got, ref, lengths, rows=None):
+    gs, gl, gst = got
+    rs, rl, rst = ref
+    todo = range(len(rs)) if rows is None else rows
+    errs, worst, n = [], 0.0, 0
+    for j in todo:
+        if gst[j] != rst[j]:
+            errs.append(f"row {j}: status {gst[j]} != {rst[j]}")
+            continue
+        if rst[j] != 0:
+            if not np.isnan(gs[j]):
+                errs.append(f"row {j}: logprob {gs[j]} on status {rst[j]}")
+            continue
+        if np.isinf(rs[j]) or np.isinf(gs[j]):
+            if gs[j] != rs[j]:
+                errs.append(f"row {j}: logprob {gs[j]} != {rs[j]}")
+            n += 1
+            continue
+        worst = max(worst, abs(float(gs[j]) - float(rs[j])))
+        if abs(float(gs[j]) - float(rs[j])) > LP_TOL:
+            errs.append(f"row {j}: logprob {gs[j]} != {rs[j]}")
+        m = int(lengths[j])
+        if gl is not None and 1 <= m <= gl.shape[1]:
+            a, b = gl[j, :m].astype(np.float64), rl[j, :m].astype(np.float64)
+            fin = np.isfinite(b)
+            if not np.array_equal(np.isfinite(a), fin) or np.any(np.abs(a[fin] - b[fin]) > LP_TOL):
+                errs.append(f"row {j}: support logprobs differ (max {np.max(np.abs(a[fin] - b[fin]))})")
+            if fin.any():
+                worst = max(worst, float(np.max(np.abs(a[fin] - b[fin]))))
+        n += 1
+    return errs, n, worst
+
+
+@functools.lru_cache(maxsize=None)
+def captured(index, W):
+    """The oracle sampler's capture of workload ``index``, one replay row per capture slot: the
+    slot's sampling logits and temperature, packed ids, length, row status, token, and the
+    bitmask of an overflowing slot."""
+    wl = make_workload(index, W=W)
+    bits_ld = (wl.V + 127) // 128 * 16
+    ref = oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k, wl.top_p,
+                                  wl.min_p, wl.optin_rows, wl.seeds, wl.positions, W,
+                                  bits_ld=bits_ld)
+    rows = wl.optin_rows.astype(np.int64)
+    ids = np.where(ref.packed_ids < 0, 0, ref.packed_ids).astype(np.int32)
+    return (np.ascontiguousarray(wl.logits[rows]), wl.dtype, wl.temperature[rows].copy(), ids,
+            ref.lengths.copy(), ref.row_status[rows].copy(), ref.tokens[rows].copy(),
+            ref.support_bits, ref.selected_logprob.copy(), ref.logprobs.copy())
+
+
+def test_tie_example_replay():
+    log("case replay tie example")
+    x = np.tile(np.log(np.array([0.4, 0.2, 0.2, 0.1, 0.1], np.float32)), (5, 1))
+    ids = np.tile(np.array([0, 1, 2, 0], np.int32), (5, 1))
+    lengths = np.full(5, 3, np.int32)
+    tokens = np.arange(5, dtype=np.int32)
+    T = np.ones(5, np.float32)
+    for dtype in ("f32", "bf16"):
+        xx = x if dtype == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+        got = run_replay(xx, dtype, T, ids, lengths, tokens)
+        ref = oracle.replay(xx, dtype, T, ids, lengths, tokens)
+        errs, n, _ = compare_replay(got, ref, lengths)
+        assert errs == [] and n == 5, errs
+    sel = got[0]
+    assert abs(sel[0] - math.log(0.5)) < 2e-2 and sel[3] == -np.inf and sel[4] == -np.inf
+
+
+@pytest.mark.parametrize("index,W", [(3, 2048), (4, 8192), (2, 2)])
+def test_replay_of_captured_workloads(index, W):
+    # Workload 3: packed supports of ~1000; workload 4 at W = 8192: most rows overflowed, their
+    # supports come from the bitmasks; workload 2 (float32) with W = 2: a mix of both.
+    x, dtype, T, ids, lengths, status, tokens, bits, _, _ = captured(index, W)
+    log(f"case replay workload {index} W={W}: {int((status == 1).sum())} overflowed rows")
+    x_new = perturbed_logits(x, dtype, seed=100 + index)
+    T = T.copy()
+    T[T == 0] = 1.0  # greedy rows replay their width-1 support at T = 1
+    got = run_replay(x_new, dtype, T, ids, lengths, tokens, status, bits)
+    ref = oracle.replay(x_new, dtype, T, ids, lengths, tokens, status, bits)
+    errs, n, worst = compare_replay(got, ref, lengths)
+    log(f"  {n} rows compared, max |logprob error| {worst:.2e}")
+    assert errs == [], errs[:10]
+    assert n >= len(tokens) // 2
+
+
+def test_replay_on_the_sampling_logits_reproduces_the_capture():
+    # Replaying the oracle's capture on the very logits it was sampled from gives back the
+    # oracle's own logprobs (the importance ratio of an unchanged policy is 1).
+    x, dtype, T, ids, lengths, status, tokens, bits, sel, lps = captured(3, 2048)
+    log("case replay on unchanged logits, workload 3")
+    got = run_replay(x, dtype, T, ids, lengths, tokens, status, bits)
+    ok = status == 0
+    assert ok.sum() > 200
+    assert np.all(got[2][ok] == 0)
+    assert np.max(np.abs(got[0][ok] - sel[ok])) <= LP_TOL
+    for j in np.nonzero(ok)[0]:
+        m = lengths[j]
+        assert np.max(np.abs(got[1][j, :m] - lps[j, :m])) <= LP_TOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_edge_cases(dtype):
+    rng = np.random.default_rng(9)
+    V, W = 1029, 8  # ragged: V % 8 = 5, so the last mask byte has bits past V
+    N = 14
+    x = rng.standard_normal((N, V)).astype(np.float32)
+    ids = np.tile(np.array([5, 9, 1028, 0, 700, 3, 2, 1], np.int32), (N, 1))
+    lengths = np.full(N, 5, np.int32)
+    tokens = np.full(N, 9, np.int32)
+    T = np.full(N, 0.8, np.float32)
+    cs = np.zeros(N, np.int8)
+    bits = np.zeros((N, (V + 7) // 8 + 3), np.uint8)
+    T[1] = 0.0                      # invalid temperature
+    T[2] = np.nan
+    tokens[3] = V                   # token out of range
+    tokens[4] = 4                   # token outside the support: -inf
+    lengths[5] = 0                  # empty packed support
+    lengths[6] = W + 1
+    ids[7, 2] = V                   # an id out of range
+    x[8, 700] = np.nan              # a non-finite support logit
+    x[9, [5, 9, 1028, 0, 700]] = -np.inf  # every support logit -inf
+    cs[10] = 3                      # capture status passed through
+    cs[11] = 1                      # overflowed: support from the bitmask, junk past V ignored
+    keep = np.zeros(V, bool)
+    keep[[9, 17, 64, 65, 1000, 1027, 1028]] = True
+    bits[11, :(V + 7) // 8] = np.packbits(keep, bitorder="little")
+    bits[11, -4] |= 0xE0            # bits 1029..1031 of the last byte: past V
+    bits[11, -3:] = 0xFF            # bytes past ceil(V / 8)
+    cs[12] = 1                      # overflowed with an empty bitmask
+    x[13, 9] = -np.inf              # the token's own logit is -inf: logprob -inf
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        xx = f32_to_bf16_bits(np.nan_to_num(x, nan=0.0, neginf=0.0))
+        xx[np.isnan(x)] = 0x7FC0
+        xx[np.isneginf(x)] = 0xFF80
+    else:
+        xx = x
+    log(f"case replay edge cases {dtype}")
+    got = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits)
+    ref = oracle.replay(xx, dtype, T, ids, lengths, tokens, cs, bits)
+    errs, n, _ = compare_replay(got, ref, lengths)
+    assert errs == [], errs
+    assert got[2].tolist() == [0, 4, 4, 4, 0, 4, 4, 4, 3, 2, 3, 0, 4, 0]
+    assert got[0][4] == -np.inf and got[0][13] == -np.inf and np.isfinite(got[0][11])
+    # Without logprobs requested, the selected logprobs are the same.
+    got2 = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits, return_logprobs=False)
+    assert np.array_equal(got2[2], got[2])
+    assert np.array_equal(np.nan_to_num(got2[0], nan=7.0), np.nan_to_num(got[0], nan=7.0))

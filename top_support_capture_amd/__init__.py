@@ -15,7 +15,7 @@ from typing import NamedTuple, Optional
 import torch  # must come first: the library binds to the HIP runtime PyTorch has loaded
 
 __all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "workspace_size",
-           "support_bits_ld",
+           "support_bits_ld", "replay_logprob", "ReplayOutput",
            "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
            "MAX_PACKED_WIDTH", "TscError"]
@@ -51,6 +51,9 @@ def library() -> ctypes.CDLL:
     lib.tsc_sample_with_mask_bits.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P, I64, P, P,
                                               I32, P, P, P, P, P, P, P, I64, P, SZ, P]
     lib.tsc_sample_with_mask_bits.restype = I32
+    lib.tsc_replay_logprob.argtypes = [P, I32, I64, I64, I64, P, P, P, I32, P, P, I64, P, P, P,
+                                       P, P]
+    lib.tsc_replay_logprob.restype = I32
     lib.tsc_support_bits_ld.argtypes = [I64]
     lib.tsc_support_bits_ld.restype = I64
     lib.tsc_workspace_size.argtypes = [I64, I64, I64, I32, I32]
@@ -211,3 +214,58 @@ def sample_with_mask(logits: torch.Tensor, temperature: torch.Tensor, top_k: tor
     OVERFLOW slot is also written as a bitmask."""
     return PreparedSample(logits, temperature, top_k, top_p, min_p, optin_rows, seeds, positions,
                           W, return_logprobs, out, stream, return_bits)(logits, check=False)
+
+
+class ReplayOutput(NamedTuple):
+    selected_logprob: torch.Tensor     # float32 [N]
+    logprobs: Optional[torch.Tensor]   # float32 [N, W] (None unless requested)
+    row_status: torch.Tensor           # int8 [N]
+
+
+def replay_logprob(logits: torch.Tensor, temperature: torch.Tensor, packed_ids: torch.Tensor,
+                   lengths: torch.Tensor, tokens: torch.Tensor,
+                   capture_status: Optional[torch.Tensor] = None,
+                   support_bits: Optional[torch.Tensor] = None, return_logprobs: bool = False,
+                   stream: Optional[torch.cuda.Stream] = None) -> ReplayOutput:
+    """Log-probability of ``tokens`` under ``logits`` [N, V] normalized over each row's captured
+    support: ``packed_ids`` [N, W] / ``lengths`` [N] (int32, as the sampler writes them), or,
+    where ``capture_status`` (int8 [N]) is OVERFLOW, the row of ``support_bits`` (uint8 [N, ld]).
+    ``temperature`` float32 [N] divides the logits first (1 = the plain masked log-softmax)."""
+    lib = library()
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [N, V] with unit column stride")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    dt = TSC_DTYPE_BF16 if logits.dtype == torch.bfloat16 else TSC_DTYPE_F32
+    dev = logits.device
+    N, V = logits.shape
+    ld = logits.stride(0) if N > 1 else V
+    _check(temperature, "temperature", torch.float32, N, dev)
+    _check(lengths, "lengths", torch.int32, N, dev)
+    _check(tokens, "tokens", torch.int32, N, dev)
+    if (packed_ids.device != dev or packed_ids.dtype != torch.int32 or packed_ids.dim() != 2
+            or packed_ids.shape[0] != N or not packed_ids.is_contiguous()):
+        raise ValueError(f"packed_ids must be a contiguous int32 tensor [{N}, W] on {dev}")
+    W = int(packed_ids.shape[1])
+    if capture_status is not None:
+        _check(capture_status, "capture_status", torch.int8, N, dev)
+    bits_ld = 0
+    if support_bits is not None:
+        if (support_bits.device != dev or support_bits.dtype != torch.uint8
+                or support_bits.dim() != 2 or support_bits.shape[0] != N
+                or not support_bits.is_contiguous()):
+            raise ValueError(f"support_bits must be a contiguous uint8 tensor [{N}, ld] on {dev}")
+        bits_ld = int(support_bits.shape[1])
+    out = ReplayOutput(torch.empty(N, dtype=torch.float32, device=dev),
+                       torch.empty((N, W), dtype=torch.float32, device=dev)
+                       if return_logprobs else None,
+                       torch.empty(N, dtype=torch.int8, device=dev))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    code = lib.tsc_replay_logprob(logits.data_ptr(), dt, N, V, ld, temperature.data_ptr(),
+                                  packed_ids.data_ptr(), lengths.data_ptr(), W,
+                                  _ptr(capture_status), _ptr(support_bits), bits_ld,
+                                  tokens.data_ptr(), out.selected_logprob.data_ptr(),
+                                  _ptr(out.logprobs), out.row_status.data_ptr(), s.cuda_stream)
+    if code != 0:
+        raise TscError(code, lib.tsc_status_string(code).decode())
+    return out

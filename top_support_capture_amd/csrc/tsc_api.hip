@@ -6,6 +6,7 @@
 
 #include "tsc.h"
 #include "tsc_fast.h"
+#include "tsc_replay.h"
 
 namespace {
 
@@ -109,5 +110,34 @@ int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64
 }
 
 int64_t tsc_support_bits_ld(int64_t V) { return V < 1 ? 0 : tsc::bitmask_words(V) * 4; }
+
+int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld,
+                           const float* temperature, const int32_t* packed_ids,
+                           const int32_t* lengths, int32_t W, const int8_t* capture_status,
+                           const uint8_t* support_bits, int64_t bits_ld, const int32_t* tokens,
+                           float* selected_logprob, float* logprobs, int8_t* row_status,
+                           void* stream) {
+  if (dtype != TSC_DTYPE_F32 && dtype != TSC_DTYPE_BF16) return TSC_ERR_INVALID_ARGUMENT;
+  if (N < 0 || V < 1 || V > INT32_MAX - 16 || ld < V) return TSC_ERR_INVALID_ARGUMENT;
+  if (N > 0x7FFFFFFF) return TSC_ERR_UNSUPPORTED;
+  if (N == 0) return TSC_OK;
+  if (W < 1) return TSC_ERR_INVALID_ARGUMENT;
+  if (W > TSC_MAX_PACKED_WIDTH) return TSC_ERR_UNSUPPORTED;
+  const size_t esize = dtype == TSC_DTYPE_F32 ? 4 : 2;
+  if (!logits || (reinterpret_cast<uintptr_t>(logits) % esize) != 0)
+    return TSC_ERR_INVALID_ARGUMENT;
+  if (!temperature || !packed_ids || !lengths || !tokens || !selected_logprob || !row_status)
+    return TSC_ERR_INVALID_ARGUMENT;
+  if (support_bits != nullptr && bits_ld < (V + 7) / 8) return TSC_ERR_INVALID_ARGUMENT;
+  tsc::ReplayArgs a{logits, N, V, ld, temperature, packed_ids, lengths, W, capture_status,
+                    support_bits, bits_ld, tokens, selected_logprob, logprobs, row_status};
+  (void)hipGetLastError();
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == TSC_DTYPE_F32)
+    hipLaunchKernelGGL(tsc::replay_kernel<TSC_DTYPE_F32>, dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(tsc::replay_kernel<TSC_DTYPE_BF16>, dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? TSC_OK : TSC_ERR_HIP;
+}
 
 }  // extern "C"

@@ -100,6 +100,23 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def perturbed_logits(logits: np.ndarray, dtype: str, seed: int, sigma: float = 0.25) -> np.ndarray:
+    """New logits for a replay: the given [B, V] logits (float32, or uint16 bfloat16 bits) plus
+    seeded N(0, sigma^2) noise, rounded back to the same dtype; -inf entries stay -inf. Stands
+    in for a training model's logits at the captured positions, a small step away from the
+    sampling model's."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits_to_f32(logits) if dtype == "bf16" else np.asarray(logits, np.float32)
+    noise = (rng.standard_normal(x.shape) * sigma).astype(np.float32)
+    finite = np.isfinite(x)
+    y = np.where(finite, x + noise, x).astype(np.float32)
+    if dtype != "bf16":
+        return y
+    out = f32_to_bf16_bits(np.where(finite, y, 0.0))
+    out[~finite] = np.asarray(logits)[~finite]
+    return out
+
+
 def _zipf_bonus(rng: np.random.Generator, V: int, s: float, a: float) -> np.ndarray:
     rank = rng.permutation(V).astype(np.float64) + 1.0
     H = np.sum(np.arange(1, V + 1, dtype=np.float64) ** (-s))
