@@ -13,6 +13,10 @@ call: B*V*2 (one read of the logits) + sum over opt-in rows of min(L, W)*8 (ids 
 R*8 (length + selected logprob) + B*5 (token + status), divided by the kernel's average launch
 duration: HIP events on the launch stream around the K timed calls, over K.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+
+``--kernel replay`` times ``tsc_replay_logprob`` instead: the supports and tokens a sampler call
+captured on the workload, replayed on new logits (the workload's logits plus seeded N(0, 0.25^2)
+noise, cast back to the same dtype); one step = one replay call over all captured rows.
 """
 from __future__ import annotations
 
@@ -133,6 +137,121 @@ def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) 
             "kernel_source_hash": kernel_source_hash()}
 
 
+def param_summary(v):
+    """A per-row parameter for the config record: its value when every row shares it, else its
+    range."""
+    import numpy as np
+    v = np.asarray(v)
+    if np.all(v == v[0]):
+        return v[0].item()
+    return f"per row, {v.min().item():.4g}..{v.max().item():.4g}"
+
+
+def replay_cpu_baseline(x_new, dtype, T, ids, lengths, tokens, budget_s: float = 10.0) -> dict:
+    """The replay oracle (as it stands) on a bounded sample: rows in order, cycling."""
+    import oracle
+    decoded = {}
+    rows, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        j = rows % len(tokens)
+        if j not in decoded:
+            decoded[j] = oracle.decode_logits(x_new[j], dtype)
+        oracle.replay_row(decoded[j], T[j], ids[j, :lengths[j]], int(tokens[j]))
+        rows += 1
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} rows (the captured rows of the batch, cycled) through "
+                      f"oracle.replay_row in one process and one thread, {dt:.1f} s; decoding "
+                      f"done once per row outside the clock"}
+
+
+def bench_replay(args, wl) -> int:
+    """Replay of the workload's captured supports on new logits (see the module docstring)."""
+    import numpy as np
+    import torch
+    import top_support_capture_amd as tsc
+    from tests.gpu_helpers import device_inputs, logits_tensor
+    from workloads import perturbed_logits
+    dev = torch.device("cuda:0")
+    d = device_inputs(wl)
+    cap = tsc.sample_with_mask(d["logits"], d["temperature"], d["top_k"], d["top_p"], d["min_p"],
+                               d["optin_rows"], d["seeds"], d["positions"], wl.W,
+                               return_logprobs=False, return_bits=True)
+    torch.cuda.synchronize()
+    rows = d["optin_rows"].long()
+    N = rows.numel()
+    x_new_host = perturbed_logits(wl.logits[wl.optin_rows], wl.dtype, seed=12345)
+    esize = 2 if wl.dtype == "bf16" else 4
+    in_bytes = N * wl.V * esize
+    ncopies = max(1, -(-512 * 2**20 // in_bytes) + 1)
+    x0 = logits_tensor(x_new_host, wl.dtype)
+    copies = [x0] + [x0.clone() for _ in range(ncopies - 1)]
+    T = d["temperature"][rows].contiguous()
+    T = torch.where(T > 0, T, torch.ones_like(T))
+    tokens = cap.tokens[rows].contiguous()
+    status = cap.row_status[rows].contiguous()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, lp=False):
+        return tsc.replay_logprob(copies[i % ncopies], T, cap.packed_ids, cap.lengths, tokens,
+                                  status, cap.support_bits, return_logprobs=lp, stream=stream)
+
+    def timed(lp):
+        for i in range(args.warmup):
+            step(i, lp)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            out = step(i, lp)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1) / args.steps, out
+
+    wall, avg_ms, out = timed(False)
+    wall_lp, avg_ms_lp, _ = timed(True)
+    lengths = cap.lengths.cpu().numpy().astype(np.int64)
+    st = status.cpu().numpy()
+    packed = lengths[st == 0]
+    nbits = int((st == 1).sum())
+    members = cap.support_bits.cpu().numpy() if nbits else None
+    bit_members = 0 if not nbits else int(sum(
+        np.unpackbits(members[j], bitorder="little")[:wl.V].sum() for j in np.nonzero(st == 1)[0]))
+    # Algorithmic bytes: packed rows read their ids and gather their logits; bitmask rows read
+    # ceil(V / 8) mask bytes and gather their members; every row reads length, token and
+    # temperature and writes its logprob and status.
+    alg = int(packed.sum()) * (4 + esize) + nbits * ((wl.V + 7) // 8) + bit_members * esize + N * 17
+    alg_lp = alg + int(lengths[st <= 1].sum()) * 4
+    achieved = alg / (avg_ms * 1e-3) / 1e9
+    rs = out.row_status.cpu().numpy()
+    line = {
+        "metric": "replayed rows/s and achieved GB/s (% of HBM peak), replay of captured supports",
+        "value": N * args.steps / wall, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (the workload's captures replayed on its logits plus seeded noise)",
+        "config": {"workload": f"replay of {wl.name}", "N": N, "V": wl.V, "W": wl.W,
+                   "rows_from_bitmask": nbits, "mean_support": float(lengths.mean()),
+                   "outputs": "selected logprob"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+        "kernel_ms": {"mean": avg_ms, "with_support_logprobs": avg_ms_lp},
+        "algorithmic_bytes_per_launch": alg,
+        "algorithmic_bytes_with_support_logprobs": alg_lp,
+        "rows_not_ok": int(np.count_nonzero(rs != 0)),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        ids = cap.packed_ids.cpu().numpy()
+        ok = np.nonzero(st == 0)[0]
+        line["cpu_baseline"] = replay_cpu_baseline(
+            x_new_host[ok], wl.dtype, T.cpu().numpy()[ok], ids[ok], lengths[ok],
+            tokens.cpu().numpy()[ok])
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +261,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", choices=["sample", "replay"], default="sample",
+                    help="time the sampler (default) or the replay of its captures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the known-size copy kernel that scales the HBM counters")
     ap.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LINE"),
@@ -161,6 +282,8 @@ def main() -> int:
         from tests.gpu_helpers import device_inputs
 
     wl = make_workload(args.workload)
+    if args.kernel == "replay":
+        return bench_replay(args, wl)
     in_bytes = wl.B * wl.V * (2 if wl.dtype == "bf16" else 4)
     if args.ingest_pmc:
         with open(args.ingest_pmc[2]) as f:  # the last JSON line (a profiler may print after it)
@@ -233,10 +356,13 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded Gaussian logits on a 0.125 grid, cast to bfloat16)",
-        "config": {"workload": wl.name, "B": wl.B, "V": wl.V, "logits": wl.dtype, "top_k": 1024,
-                   "top_p": 0.95, "temperature": "U[0.6,1.2] per row", "R": wl.R, "W": wl.W,
+        "dtype": wl.dtype,
+        "data": ("synthetic (seeded Gaussian logits on a 0.125 grid, cast to bfloat16)"
+                 if args.workload == 3 else f"synthetic (seeded workload {wl.name})"),
+        "config": {"workload": wl.name, "B": wl.B, "V": wl.V, "logits": wl.dtype,
+                   "top_k": param_summary(wl.top_k), "top_p": param_summary(wl.top_p),
+                   "min_p": param_summary(wl.min_p),
+                   "temperature": param_summary(wl.temperature), "R": wl.R, "W": wl.W,
                    "input_copies_rotated": ncopies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},

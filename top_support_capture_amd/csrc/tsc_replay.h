@@ -5,9 +5,9 @@
 //
 // One workgroup per row. The support is either the row's packed ids (a gather of at most W
 // logits) or, for a row whose capture overflowed, its bitmask (a pass over ceil(V / 8) mask
-// bytes that loads only the logits of set bits). Each thread keeps an online maximum and sum of
-// exp((x - max) / T) over its share; one block reduction of the maxima, one of the rescaled
-// sums, then the token's logprob in float64.
+// bytes that loads only the chunks of 8 logits holding set bits). Each thread keeps an online
+// maximum and sum of exp((x - max) / T) over its share; one block-wide merge of those states,
+// then the token's logprob in float64.
 #pragma once
 
 #include "tsc_device.h"
@@ -31,7 +31,9 @@ struct ReplayArgs {
 };
 
 struct ReplayShared {
-  uint64_t red[kWaves];
+  float m[kWaves];
+  float s[kWaves];
+  uint32_t f[kWaves];
 };
 
 // Online log-sum-exp state of one thread: m the largest finite logit seen, s = sum of
@@ -39,12 +41,11 @@ struct ReplayShared {
 struct OnlineLse {
   float m = -__builtin_inff();
   float s = 0.0f;
-  uint32_t bad = 0;  // a NaN or +inf logit
-  uint32_t n = 0;    // support entries seen
+  uint32_t flags = 0;  // kBad: a NaN or +inf logit; kSeen: an entry of the support
   __device__ inline void add(float x, float c) {
-    ++n;
+    flags |= kSeen;
     if (x != x || x == __builtin_inff()) {
-      bad = 1;
+      flags |= kBad;
     } else if (x > m) {
       s = s * __builtin_amdgcn_exp2f((m - x) * c) + 1.0f;  // m = -inf: s is 0, 0 * 0 + 1
       m = x;
@@ -52,7 +53,66 @@ struct OnlineLse {
       s += __builtin_amdgcn_exp2f((x - m) * c);
     }
   }
+  static constexpr uint32_t kBad = 1, kBadId = 2, kFound = 4, kSeen = 8;
 };
+
+// (m, s) of two partial states over one scale: the larger maximum, the sums rescaled to it.
+__device__ inline void lse_merge(float& m, float& s, float m2, float s2, float c) {
+  const float M = m > m2 ? m : m2;
+  float r = 0.0f;
+  if (m != -__builtin_inff()) r += s * __builtin_amdgcn_exp2f((m - M) * c);
+  if (m2 != -__builtin_inff()) r += s2 * __builtin_amdgcn_exp2f((m2 - M) * c);
+  m = M;
+  s = r;
+}
+
+// One workgroup-wide combination of the threads' states (a single barrier): each wave merges
+// its lanes with DPP moves, lane 0 stores the wave's state, and every thread merges the 16
+// wave states in the same fixed order.
+__device__ inline void lse_block(OnlineLse& st, float c, ReplayShared& sh) {
+  float m = st.m, s = st.s;
+  uint32_t f = st.flags;
+  auto step = [&](auto mv) {
+    const float m2 = mv(m), s2 = mv(s);
+    lse_merge(m, s, m2, s2, c);
+    f |= mv(f);
+  };
+  step([](auto v) { return dpp_mov<dpp::kQuadSwap1>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kQuadSwap2>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kRowRor4>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kRowRor8>(v, v); });
+  {
+    // Every lane of a row of 16 now holds that row's state: merge the four rows.
+    float rm[4], rs[4];
+    uint32_t rf[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rm[r] = read_lane(m, 16 * r);
+      rs[r] = read_lane(s, 16 * r);
+      rf[r] = read_lane(f, 16 * r);
+    }
+    m = rm[0], s = rs[0], f = rf[0];
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      lse_merge(m, s, rm[r], rs[r], c);
+      f |= rf[r];
+    }
+  }
+  const uint32_t w = threadIdx.x / kWaveSize;
+  if ((threadIdx.x & (kWaveSize - 1)) == 0) {
+    sh.m[w] = m;
+    sh.s[w] = s;
+    sh.f[w] = f;
+  }
+  lds_barrier();
+  m = sh.m[0], s = sh.s[0], f = sh.f[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) {
+    lse_merge(m, s, sh.m[i], sh.s[i], c);
+    f |= sh.f[i];
+  }
+  st.m = m, st.s = s, st.flags = f;
+}
 
 template <int DT>
 __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
@@ -76,8 +136,8 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   const int32_t tok = a.tokens[j];
   const bool from_bits = cs == TSC_ROW_OVERFLOW;
   const bool n_ok = n >= 1 && n <= a.W;
-  bool ok = __builtin_isfinite(T) && T >= 1.1754943508222875e-38f && tok >= 0 && tok < V &&
-            (from_bits ? a.bits != nullptr : n_ok);
+  const bool ok = __builtin_isfinite(T) && T >= 1.1754943508222875e-38f && tok >= 0 && tok < V &&
+                  (from_bits ? a.bits != nullptr : n_ok);
   if (!ok) {
     if (tid == 0) {
       a.row_status[j] = TSC_ROW_INVALID_PARAM;
@@ -85,63 +145,90 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
     }
     return;
   }
+  // The token's own logit, loaded now so that its latency overlaps the support's.
+  const float xt = tid == 0 ? E::to_float((uint32_t)row[tok]) : 0.0f;
   const float c = 1.4426950408889634f / T;
   OnlineLse acc;
-  uint32_t bad_id = 0, found = 0;
   const int32_t* ids = a.packed_ids + j * a.W;
+  const uint8_t* brow = from_bits ? a.bits + j * a.bits_ld : nullptr;
   if (!from_bits) {
     for (int32_t i = (int32_t)tid; i < n; i += kThreads) {
       const int32_t id = ids[i];
       if (id < 0 || id >= V) {
-        bad_id = 1;
+        acc.flags |= OnlineLse::kBadId;
         continue;
       }
-      found |= id == tok;
+      if (id == tok) acc.flags |= OnlineLse::kFound;
       acc.add(E::to_float((uint32_t)row[id]), c);
     }
   } else {
-    // Chunks of 8 ids, one mask byte each; neighbouring lanes take neighbouring chunks.
-    const uint8_t* brow = a.bits + j * a.bits_ld;
+    // Chunks of 8 ids, one mask byte each; a chunk with members is loaded whole (16 bytes of
+    // bfloat16, 32 of float32) when the row allows aligned vector loads; each thread takes four
+    // consecutive chunks per step, so that their loads are in flight together.
     const int64_t nchunks = (V + 7) / 8;
-    for (int64_t ch = tid; ch < nchunks; ch += kThreads) {
-      uint32_t byte = brow[ch];
-      if (ch == nchunks - 1 && (V & 7)) byte &= (1u << (V & 7)) - 1u;  // bits past V
-      if (byte == 0u) continue;
-      float x[8];
+    const int64_t nfull = V / 8;  // chunks wholly inside the row
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    constexpr int kQ = 4;
+    for (int64_t q0 = (int64_t)tid * kQ; q0 < nchunks; q0 += (int64_t)kThreads * kQ) {
+      uint32_t bytes[kQ];
+      float x[kQ][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = (byte >> e) & 1u ? E::to_float((uint32_t)row[ch * 8 + e]) : -__builtin_inff();
+      for (int u = 0; u < kQ; ++u) {
+        const int64_t ch = q0 + u;
+        uint32_t byte = ch < nchunks ? brow[ch] : 0u;
+        if (ch == nchunks - 1 && (V & 7)) byte &= (1u << (V & 7)) - 1u;  // bits past V
+        bytes[u] = byte;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((byte >> e) & 1u) acc.add(x[e], c);
-      if ((int64_t)tok >> 3 == ch) found |= (byte >> (tok & 7)) & 1u;
+      for (int u = 0; u < kQ; ++u) {
+        const int64_t ch = q0 + u;
+        if (vec && ch < nfull && bytes[u] != 0u) {
+          if constexpr (sizeof(typename E::Bits) == 2) {
+            const uint4 v = *reinterpret_cast<const uint4*>(row + ch * 8);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[u][e] = E::to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          } else {
+            const uint4 v0 = *reinterpret_cast<const uint4*>(row + ch * 8);
+            const uint4 v1 = *reinterpret_cast<const uint4*>(row + ch * 8 + 4);
+            const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[u][e] = E::to_float(w8[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[u][e] = (bytes[u] >> e) & 1u ? E::to_float((uint32_t)row[ch * 8 + e]) : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((bytes[u] >> e) & 1u) acc.add(x[u][e], c);
+        if ((int64_t)tok >> 3 == q0 + u && ((bytes[u] >> (tok & 7)) & 1u)) acc.flags |= OnlineLse::kFound;
+      }
     }
   }
-  // Block reductions: the maximum, then the sums rescaled to it, and the flags.
-  const float M = block_reduce(acc.m, MaxOp(), sh.red);
-  const float sr = acc.m == -__builtin_inff() ? 0.0f : acc.s * __builtin_amdgcn_exp2f((acc.m - M) * c);
-  const float S = block_reduce(sr, SumOp(), sh.red);
-  const uint32_t flags = block_reduce((acc.bad ? 1u : 0u) | (bad_id ? 2u : 0u) | (found ? 4u : 0u) |
-                                          (acc.n ? 8u : 0u),
-                                      [](uint32_t x, uint32_t y) { return x | y; }, sh.red);
+  lse_block(acc, c, sh);
+  const float M = acc.m;
+  const uint32_t flags = acc.flags;
   int8_t status = TSC_ROW_OK;
-  if ((flags & 2u) || !(flags & 8u)) status = TSC_ROW_INVALID_PARAM;  // bad id, empty support
-  else if (flags & 1u) status = TSC_ROW_NONFINITE;
+  if ((flags & OnlineLse::kBadId) || !(flags & OnlineLse::kSeen)) status = TSC_ROW_INVALID_PARAM;
+  else if (flags & OnlineLse::kBad) status = TSC_ROW_NONFINITE;
   else if (M == -__builtin_inff()) status = TSC_ROW_NO_SUPPORT;
-  const double lnS = log((double)S);
+  const double lnS = log((double)acc.s);
   if (tid == 0) {
     a.row_status[j] = status;
     float sel = __builtin_nanf("");
-    if (status == TSC_ROW_OK) {
-      const float xt = E::to_float((uint32_t)row[tok]);
-      sel = (flags & 4u) ? (float)(((double)xt - (double)M) / (double)T - lnS) : -__builtin_inff();
-    }
+    if (status == TSC_ROW_OK)
+      sel = (flags & OnlineLse::kFound) ? (float)(((double)xt - (double)M) / (double)T - lnS)
+                                        : -__builtin_inff();
     a.selected_logprob[j] = sel;
   }
   // The logprob of every packed entry (for an overflowing row, of its packed prefix).
   if (a.logprobs != nullptr && status == TSC_ROW_OK && n_ok) {
     float* out = a.logprobs + j * a.W;
-    const uint8_t* brow = from_bits ? a.bits + j * a.bits_ld : nullptr;
     for (int32_t i = (int32_t)tid; i < n; i += kThreads) {
       const int32_t id = ids[i];
       // Masked log-softmax: an id outside the support (possible only in a bitmask row) is -inf.
