@@ -10,3 +10,4 @@ from .sampler import (  # noqa: F401
     decode_logits, params_valid, sample_row, sample_with_mask, slot_validity, support_bitmask,
 )
 from .replay import ReplayRow, replay, replay_row  # noqa: F401
+from .csr import support_csr  # noqa: F401

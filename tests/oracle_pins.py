@@ -283,3 +283,39 @@ def pin_replay(replay_row, sample_row, rng_seed=4, cases=200):
             fails.append(f"replay of the sampler's own support differs for x={xs.tolist()}")
             break
     return fails
+
+
+def pin_support_csr(support_csr, rng_seed=6, cases=100):
+    """The CSR layout of packed supports (sglang PR #40986, "Limitations": a transfer sized by
+    the realized support instead of the packed capacity). Checked by properties that hold for any
+    layout of this kind: offsets start at 0 and step by each row's length (clamped to [0, W]),
+    the payload has offsets[R] entries, and cutting the payload at the offsets gives back every
+    row's packed prefix, ids and logprobs alike; a hand-made three-row case is written out."""
+    fails = []
+    ids = np.array([[7, 3, 9, 0], [1, 2, 0, 0], [5, 6, 8, 4]], np.int32)
+    lps = np.array([[-0.5, -1, -2, 0], [-0.1, -3, 0, 0], [-1, -1, -1, -1]], np.float32)
+    off, cid, clp = support_csr(np.array([3, 0, 4], np.int32), ids, lps)
+    if off.tolist() != [0, 3, 3, 7] or cid.tolist() != [7, 3, 9, 5, 6, 8, 4]:
+        fails.append(f"three-row CSR {off.tolist()} {cid.tolist()}")
+    if clp is None or clp.tolist() != [-0.5, -1, -2, -1, -1, -1, -1]:
+        fails.append(f"three-row CSR logprobs {clp}")
+    rng = np.random.default_rng(rng_seed)
+    for _ in range(cases):
+        R, W = int(rng.integers(0, 9)), int(rng.integers(1, 12))
+        lengths = rng.integers(-2, W + 3, R).astype(np.int32)
+        packed = rng.integers(0, 1000, (R, W)).astype(np.int32)
+        lp = rng.standard_normal((R, W)).astype(np.float32)
+        off, cid, clp = support_csr(lengths, packed, lp)
+        n = [min(max(int(x), 0), W) for x in lengths]
+        if off[0] != 0 or any(off[j + 1] - off[j] != n[j] for j in range(R)):
+            fails.append(f"offsets {off.tolist()} for lengths {lengths.tolist()} W={W}")
+            break
+        if cid.size != off[-1] or clp.size != off[-1]:
+            fails.append("payload size differs from offsets[R]")
+            break
+        for j in range(R):
+            if (cid[off[j]:off[j + 1]].tolist() != packed[j, :n[j]].tolist()
+                    or clp[off[j]:off[j + 1]].tolist() != lp[j, :n[j]].tolist()):
+                fails.append(f"row {j} of the payload differs")
+                break
+    return fails

@@ -83,6 +83,29 @@ def test_replay_batch_statuses():
     assert np.isnan(sel[3:]).all()
 
 
+def test_support_csr():
+    assert pins.pin_support_csr(oracle.support_csr) == []
+
+
+@pytest.mark.parametrize("old,new", [
+    ("offsets[1:] = np.cumsum(n)", "offsets[1:] = np.cumsum(n) - n"),
+    ("n = np.clip(np.asarray(lengths, dtype=np.int64), 0, W)", "n = np.asarray(lengths, dtype=np.int64)"),
+    ("packed_ids[j, :n[j]] for j in range(R)", "packed_ids[j, 1:n[j] + 1] for j in range(R)"),
+])
+def test_support_csr_pin_catches_planted_mistakes(old, new):
+    import importlib
+    ocsr = importlib.import_module("oracle.csr")
+    src = inspect.getsource(ocsr.support_csr)
+    assert src.count(old) == 1
+    ns = dict(vars(ocsr))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    try:
+        fails = pins.pin_support_csr(ns["support_csr"])
+    except Exception as e:  # a broken layout may also raise
+        fails = [repr(e)]
+    assert fails, old
+
+
 def test_race_distribution():
     assert pins.pin_race_distribution(oracle.sample_row) == []
 
