@@ -179,6 +179,26 @@ int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t
                            float* selected_logprob, float* logprobs, int8_t* row_status,
                            void* stream);
 
+/*
+ * tsc_support_csr -- the captured supports back to back (CSR), so that a copy to the host can be
+ * sized by the realized support rather than by the packed capacity R * W (sglang PR #40986,
+ * "Limitations": the packed [B, max tokens] buffer crosses every step whole).
+ *
+ * lengths, packed_ids, logprobs  [R], [R, W], [R, W] as tsc_sample_with_mask writes them;
+ *              logprobs may be NULL (then csr_logprobs is not written). A length outside
+ *              [0, W] counts as clamped into it. Read only.
+ * offsets      [R + 1] int64 out: offsets[0] = 0, offsets[j + 1] = offsets[j] + lengths[j].
+ * csr_ids      [cap] int32 out: slot j's ids at offsets[j] .. offsets[j + 1] - 1.
+ * csr_logprobs [cap] float32 out or NULL, aligned with csr_ids.
+ * cap          capacity of the payload buffers in entries: entries at positions >= cap are not
+ *              written (offsets[R] is always the full total; R * W never overflows).
+ * Two kernels on `stream`, asynchronous, no allocation: the caller reads offsets[R] and copies
+ * that many entries. Returns TSC_OK or TSC_ERR_INVALID_ARGUMENT / UNSUPPORTED / HIP.
+ */
+int32_t tsc_support_csr(const int32_t* lengths, const int32_t* packed_ids, const float* logprobs,
+                        int64_t R, int32_t W, int64_t* offsets, int32_t* csr_ids,
+                        float* csr_logprobs, int64_t cap, void* stream);
+
 /* Device scratch bytes tsc_sample_with_mask needs for these sizes (currently always 0). */
 size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dtype);
 

@@ -25,7 +25,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["tsc_replay_logprob", "tsc_sample_with_mask",
                                     "tsc_sample_with_mask_bits", "tsc_status_string",
-                                    "tsc_support_bits_ld", "tsc_version", "tsc_workspace_size"]
+                                    "tsc_support_bits_ld", "tsc_support_csr", "tsc_version",
+                                    "tsc_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -105,6 +106,19 @@ def _call_replay(lib, **kw):
 def test_replay_argument_checks(lib, kw, code):
     # Every case returns before any HIP call, so this runs without a GPU.
     assert _call_replay(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=-1), 1), (dict(W=0), 1), (dict(W=16385), 2), (dict(cap=-1), 1),
+    (dict(offsets=None), 1), (dict(lengths=None), 1), (dict(packed_ids=None), 1),
+    (dict(csr_ids=None), 1),
+])
+def test_csr_argument_checks(lib, kw, code):
+    # Every case returns before any HIP call, so this runs without a GPU.
+    args = dict(lengths=8, packed_ids=8, logprobs=None, R=4, W=16, offsets=8, csr_ids=8,
+                csr_logprobs=None, cap=64, stream=None)
+    args.update(kw)
+    assert lib.tsc_support_csr(*args.values()) == code
 
 
 def test_binding_rejects_bad_tensors():

@@ -15,7 +15,8 @@ from typing import NamedTuple, Optional
 import torch  # must come first: the library binds to the HIP runtime PyTorch has loaded
 
 __all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "workspace_size",
-           "support_bits_ld", "replay_logprob", "ReplayOutput",
+           "support_bits_ld", "replay_logprob", "ReplayOutput", "support_csr", "SupportCsr",
+           "csr_to_host",
            "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
            "MAX_PACKED_WIDTH", "TscError"]
@@ -54,6 +55,8 @@ def library() -> ctypes.CDLL:
     lib.tsc_replay_logprob.argtypes = [P, I32, I64, I64, I64, P, P, P, I32, P, P, I64, P, P, P,
                                        P, P]
     lib.tsc_replay_logprob.restype = I32
+    lib.tsc_support_csr.argtypes = [P, P, P, I64, I32, P, P, P, I64, P]
+    lib.tsc_support_csr.restype = I32
     lib.tsc_support_bits_ld.argtypes = [I64]
     lib.tsc_support_bits_ld.restype = I64
     lib.tsc_workspace_size.argtypes = [I64, I64, I64, I32, I32]
@@ -269,3 +272,41 @@ def replay_logprob(logits: torch.Tensor, temperature: torch.Tensor, packed_ids: 
     if code != 0:
         raise TscError(code, lib.tsc_status_string(code).decode())
     return out
+
+
+class SupportCsr(NamedTuple):
+    offsets: torch.Tensor              # int64 [R + 1]
+    ids: torch.Tensor                  # int32 [cap]; the first offsets[R] entries are valid
+    logprobs: Optional[torch.Tensor]   # float32 [cap] or None
+
+
+def support_csr(out: SampleOutput, cap: Optional[int] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> SupportCsr:
+    """The captured supports of ``out`` back to back on the device (asynchronous): slot j's ids
+    (and logprobs) at offsets[j] .. offsets[j + 1]. ``cap`` (default R * W) bounds the payload."""
+    lib = library()
+    R, W = out.packed_ids.shape
+    dev = out.packed_ids.device
+    cap = R * W if cap is None else int(cap)
+    csr = SupportCsr(torch.empty(R + 1, dtype=torch.int64, device=dev),
+                     torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                     torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+                     if out.logprobs is not None else None)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    code = lib.tsc_support_csr(_ptr(out.lengths), _ptr(out.packed_ids), _ptr(out.logprobs), R, W,
+                               csr.offsets.data_ptr(), csr.ids.data_ptr(), _ptr(csr.logprobs),
+                               cap, s.cuda_stream)
+    if code != 0:
+        raise TscError(code, lib.tsc_status_string(code).decode())
+    return csr
+
+
+def csr_to_host(csr: SupportCsr, stream: Optional[torch.cuda.Stream] = None):
+    """Copy a support CSR to host memory sized by the realized support: the offsets first (one
+    synchronization), then exactly offsets[R] ids and logprobs. Returns numpy arrays
+    (offsets, ids, logprobs or None)."""
+    offsets = csr.offsets.cpu()
+    total = int(offsets[-1])
+    ids = csr.ids[:total].cpu().numpy()
+    lps = csr.logprobs[:total].cpu().numpy() if csr.logprobs is not None else None
+    return offsets.numpy(), ids, lps

@@ -6,6 +6,7 @@
 
 #include "tsc.h"
 #include "tsc_fast.h"
+#include "tsc_csr.h"
 #include "tsc_replay.h"
 
 namespace {
@@ -110,6 +111,22 @@ int32_t tsc_sample_with_mask(const void* logits, int32_t dtype, int64_t B, int64
 }
 
 int64_t tsc_support_bits_ld(int64_t V) { return V < 1 ? 0 : tsc::bitmask_words(V) * 4; }
+
+int32_t tsc_support_csr(const int32_t* lengths, const int32_t* packed_ids, const float* logprobs,
+                        int64_t R, int32_t W, int64_t* offsets, int32_t* csr_ids,
+                        float* csr_logprobs, int64_t cap, void* stream) {
+  if (R < 0 || R > 0x7FFFFFFF || cap < 0 || W < 1) return TSC_ERR_INVALID_ARGUMENT;
+  if (W > TSC_MAX_PACKED_WIDTH) return TSC_ERR_UNSUPPORTED;
+  if (!offsets || (R > 0 && (!lengths || !packed_ids)) || (cap > 0 && !csr_ids))
+    return TSC_ERR_INVALID_ARGUMENT;
+  tsc::CsrArgs a{lengths, packed_ids, logprobs, R, W, offsets, csr_ids,
+                 logprobs ? csr_logprobs : nullptr, cap};
+  (void)hipGetLastError();
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(tsc::csr_scan_kernel, dim3(1), dim3(tsc::kThreads), 0, s, a);
+  if (R > 0) hipLaunchKernelGGL(tsc::csr_copy_kernel, dim3((unsigned)R), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? TSC_OK : TSC_ERR_HIP;
+}
 
 int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld,
                            const float* temperature, const int32_t* packed_ids,

@@ -1,0 +1,68 @@
+// Compressed (CSR) layout of captured supports: the packed [R, W] capture written back to back,
+// so that a copy to the host can be sized by the realized support instead of R * W (sglang PR
+// #40986, "Limitations": the packed buffer crosses whole, sized by its capacity).
+//
+// Two launches on the caller's stream: one workgroup scans the R lengths into offsets[0..R];
+// then one workgroup per slot copies its first lengths[j] ids (and logprobs) to
+// offsets[j] .. offsets[j + 1], with coalesced loads and stores.
+#pragma once
+
+#include "tsc_device.h"
+
+namespace tsc {
+
+struct CsrArgs {
+  const int32_t* lengths;     // [R]
+  const int32_t* packed_ids;  // [R, W]
+  const float* logprobs;      // [R, W] or null
+  int64_t R;
+  int32_t W;
+  int64_t* offsets;   // [R + 1]
+  int32_t* ids;       // [cap]
+  float* lps;         // [cap] or null
+  int64_t cap;
+};
+
+__device__ inline int64_t csr_len(int32_t n, int32_t W) { return n < 0 ? 0 : (n > W ? W : n); }
+
+// offsets[0] = 0, offsets[j + 1] = offsets[j] + clamp(lengths[j], 0, W): chunks of 1024 lengths,
+// a wave scan plus a scan of the wave totals, carried from chunk to chunk.
+__global__ void __launch_bounds__(kThreads) csr_scan_kernel(CsrArgs a) {
+  __shared__ int64_t wave_tot[kWaves];
+  const uint32_t tid = threadIdx.x, lane = tid & (kWaveSize - 1), w = tid / kWaveSize;
+  int64_t carry = 0;
+  if (tid == 0) a.offsets[0] = 0;
+  for (int64_t base = 0; base < a.R; base += kThreads) {
+    const int64_t j = base + tid;
+    const int64_t v = j < a.R ? csr_len(a.lengths[j], a.W) : 0;
+    const int64_t incl = wave_incl_scan(v, SumOp(), (int64_t)0);
+    if (lane == kWaveSize - 1) wave_tot[w] = incl;
+    lds_barrier();
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const int64_t t = wave_tot[i];
+      before += i < (int)w ? t : 0;
+      total += t;
+    }
+    if (j < a.R) a.offsets[j + 1] = carry + before + incl;
+    carry += total;
+    lds_barrier();  // wave_tot is rewritten by the next chunk
+  }
+}
+
+// Workgroup j copies slot j's prefix; entries at or past cap are not written.
+__global__ void __launch_bounds__(256) csr_copy_kernel(CsrArgs a) {
+  const int64_t j = blockIdx.x;
+  const int64_t n = csr_len(a.lengths[j], a.W);
+  const int64_t at = a.offsets[j];
+  const int32_t* src = a.packed_ids + j * a.W;
+  const float* srcl = a.logprobs ? a.logprobs + j * a.W : nullptr;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    if (at + i >= a.cap) break;
+    a.ids[at + i] = src[i];
+    if (srcl && a.lps) a.lps[at + i] = srcl[i];
+  }
+}
+
+}  // namespace tsc
