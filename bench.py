@@ -14,6 +14,10 @@ R*8 (length + selected logprob) + B*5 (token + status), divided by the kernel's 
 duration: HIP events on the launch stream around the K timed calls, over K.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
 
+``--kernel csr`` times ``tsc_support_csr`` on a sampler call's capture, and the copy to pinned
+host memory of the CSR payload (sized by the realized support) against that of the packed
+[R, W] buffers (sized by the capacity).
+
 ``--kernel replay`` times ``tsc_replay_logprob`` instead: the supports and tokens a sampler call
 captured on the workload, replayed on new logits (the workload's logits plus seeded N(0, 0.25^2)
 noise, cast back to the same dtype); one step = one replay call over all captured rows.
@@ -252,6 +256,89 @@ def bench_replay(args, wl) -> int:
     return 0
 
 
+def bench_csr(args, wl) -> int:
+    """The support CSR of a sampler call's capture (see the module docstring)."""
+    import numpy as np
+    import torch
+    import top_support_capture_amd as tsc
+    from tests.gpu_helpers import device_inputs
+    dev = torch.device("cuda:0")
+    d = device_inputs(wl)
+    cap = tsc.sample_with_mask(d["logits"], d["temperature"], d["top_k"], d["top_p"], d["min_p"],
+                               d["optin_rows"], d["seeds"], d["positions"], wl.W)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    R, W = cap.packed_ids.shape
+    csr = tsc.support_csr(cap, stream=stream)
+    lib = tsc.library()
+    args_c = (cap.lengths.data_ptr(), cap.packed_ids.data_ptr(), cap.logprobs.data_ptr(), R, W,
+              csr.offsets.data_ptr(), csr.ids.data_ptr(), csr.logprobs.data_ptr(), R * W,
+              stream.cuda_stream)
+
+    def step():
+        assert lib.tsc_support_csr(*args_c) == 0
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
+    total = int(csr.offsets[-1].item())
+    alg = R * 4 + total * 8 + (R + 1) * 8 + total * 8
+
+    # Host copies: the packed buffers whole, against the offsets then the realized payload.
+    host_ids = torch.empty(R * W, dtype=torch.int32, pin_memory=True)
+    host_lps = torch.empty(R * W, dtype=torch.float32, pin_memory=True)
+    host_off = torch.empty(R + 1, dtype=torch.int64, pin_memory=True)
+
+    def copy_ms(fn, reps=50):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e3
+
+    def packed_copy():
+        host_ids.copy_(cap.packed_ids.view(-1), non_blocking=True)
+        host_lps.copy_(cap.logprobs.view(-1), non_blocking=True)
+
+    def csr_copy():
+        host_off.copy_(csr.offsets, non_blocking=True)
+        torch.cuda.synchronize()
+        n = int(host_off[-1])
+        host_ids[:n].copy_(csr.ids[:n], non_blocking=True)
+        host_lps[:n].copy_(csr.logprobs[:n], non_blocking=True)
+
+    line = {
+        "metric": "support CSR: kernel time and host-copy bytes, realized support vs capacity",
+        "value": alg / (avg_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32+f32",
+        "data": f"synthetic (a sampler call's capture of {wl.name})",
+        "config": {"workload": f"CSR of the capture of {wl.name}", "R": R, "W": W,
+                   "entries": total},
+        "roofline": {"bound": "hbm", "achieved": alg / (avg_ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": alg / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None},
+        "kernel_ms": {"mean": avg_ms},
+        "algorithmic_bytes_per_launch": alg,
+        "host_copy": {"packed_bytes": R * W * 8, "csr_bytes": total * 8 + (R + 1) * 8,
+                      "packed_ms": copy_ms(packed_copy), "csr_ms_incl_offsets_sync": copy_ms(csr_copy)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,8 +348,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel", choices=["sample", "replay"], default="sample",
-                    help="time the sampler (default) or the replay of its captures")
+    ap.add_argument("--kernel", choices=["sample", "replay", "csr"], default="sample",
+                    help="time the sampler (default), the replay of its captures or their CSR")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the known-size copy kernel that scales the HBM counters")
     ap.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LINE"),
@@ -284,6 +371,8 @@ def main() -> int:
     wl = make_workload(args.workload)
     if args.kernel == "replay":
         return bench_replay(args, wl)
+    if args.kernel == "csr":
+        return bench_csr(args, wl)
     in_bytes = wl.B * wl.V * (2 if wl.dtype == "bf16" else 4)
     if args.ingest_pmc:
         with open(args.ingest_pmc[2]) as f:  # the last JSON line (a profiler may print after it)
