@@ -55,7 +55,7 @@ def replay_row(x: np.ndarray, T: float, support: np.ndarray, token: int) -> Repl
         return ReplayRow(ROW_NO_SUPPORT, np.nan, np.full(support.size, np.nan))
     m = xs.max()
     z = (xs - m) / T
-    lse = np.log(np.sum(np.exp(z)))
+    lse = np.log(np.sum(np.exp((x[np.unique(support)] - m) / T)))  # R14: a set of ids
     lps = z - lse
     if np.any(support == token):
         sel = (x[token] - m) / T - lse

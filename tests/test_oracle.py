@@ -49,7 +49,8 @@ def test_replay():
 
 @pytest.mark.parametrize("old,new", [
     ("z = (xs - m) / T", "z = (xs - m)"),
-    ("lse = np.log(np.sum(np.exp(z)))", "lse = np.log(np.sum(np.exp((x[np.isfinite(x)] - m) / T)))"),
+    ("lse = np.log(np.sum(np.exp((x[np.unique(support)] - m) / T)))",
+     "lse = np.log(np.sum(np.exp((x[np.isfinite(x)] - m) / T)))"),
     ("sel = (x[token] - m) / T - lse", "sel = (x[token] - m) / T + lse"),
     ("sel = -np.inf", "sel = (x[token] - m) / T - lse"),
 ])
@@ -61,6 +62,14 @@ def test_replay_pin_catches_planted_mistakes(old, new):
     ns = dict(vars(oreplay))
     exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
     assert pins.pin_replay(ns["replay_row"], oracle.sample_row, cases=60), old
+
+
+def test_replay_support_is_a_set():
+    # R14: an id listed twice counts once in the normalizer.
+    x = np.log(np.array([0.4, 0.2, 0.2, 0.1, 0.1]))
+    r = oracle.replay_row(x, 1.0, np.array([0, 1, 1, 2]), 0)
+    assert abs(r.selected_logprob - math.log(0.5)) < 1e-12
+    assert np.allclose(r.logprobs, np.log([0.5, 0.25, 0.25, 0.25]), atol=1e-12)
 
 
 def test_replay_batch_statuses():
