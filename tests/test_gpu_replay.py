@@ -181,3 +181,21 @@ def test_replay_edge_cases(dtype):
     got2 = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits, return_logprobs=False)
     assert np.array_equal(got2[2], got[2])
     assert np.array_equal(np.nan_to_num(got2[0], nan=7.0), np.nan_to_num(got[0], nan=7.0))
+
+
+def test_replay_large_vocabulary_gathers():
+    # A vocabulary past the sampler's single-read range, with supports of 1 to 700 ids.
+    rng = np.random.default_rng(21)
+    N, V, W = 4, 600000, 700
+    x = rng.standard_normal((N, V)).astype(np.float32)
+    from workloads import f32_to_bf16_bits
+    xx = f32_to_bf16_bits(x)
+    ids = np.stack([rng.choice(V, W, replace=False) for _ in range(N)]).astype(np.int32)
+    lengths = np.array([700, 1, 350, 699], np.int32)
+    tokens = np.array([ids[0, 5], ids[1, 0], 17, ids[3, 698]], np.int32)
+    T = np.array([1.0, 0.7, 1.3, 2.0], np.float32)
+    log(f"case replay V={V}")
+    got = run_replay(xx, "bf16", T, ids, lengths, tokens)
+    ref = oracle.replay(xx, "bf16", T, ids, lengths, tokens)
+    errs, n, _ = compare_replay(got, ref, lengths)
+    assert errs == [] and n == N, errs
