@@ -424,6 +424,32 @@ def main() -> int:
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     durs_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # Library references on the same rotating copies, timed the same way, for context: a plain
+    # one-pass row maximum (torch.amax; it reads the bytes the sampler must read and does nothing
+    # else) and a device copy of the logits (torch copy_, which reads and writes them once: its
+    # rate is the streaming bandwidth this machine reaches).
+    refs = None
+    if not args.copy_calibration:
+        amax_out = torch.empty(wl.B, dtype=copies[0].dtype, device=dev)
+        dst = torch.empty_like(copies[0])
+
+        def ref_ms(fn, reps=500):
+            for i in range(200):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        amax_ms = ref_ms(lambda i: torch.amax(copies[i % ncopies], dim=1, out=amax_out))
+        copy_ms = ref_ms(lambda i: dst.copy_(copies[i % ncopies]))
+        refs = {"torch.amax rows": {"ms": amax_ms, "read GB/s": in_bytes / (amax_ms * 1e-3) / 1e9},
+                "torch copy_": {"ms": copy_ms,
+                                "read+write GB/s": 2 * in_bytes / (copy_ms * 1e-3) / 1e9}}
     if args.copy_calibration:
         copy_calibration(dev, in_bytes)
 
@@ -459,6 +485,7 @@ def main() -> int:
                       "single_call_p50": float(np.median(durs_ms)),
                       "single_call_p90": float(np.percentile(durs_ms, 90))},
         "algorithmic_bytes_per_launch": alg_bytes,
+        "library_references": refs,
         "rows_overflow": int(np.count_nonzero(status == 1)),
         "rows_not_ok": int(np.count_nonzero(status >= 2)),
         "mean_support": float(lengths.mean()),
