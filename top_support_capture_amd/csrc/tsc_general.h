@@ -55,8 +55,7 @@ __device__ inline void visit_row(const typename E::Bits* row, int64_t V, F&& f) 
   if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
     const uint4* v = reinterpret_cast<const uint4*>(row);
     const int64_t nv = V / E::kVec;
-    for (int64_t i = threadIdx.x; i < nv; i += kThreads) {
-      const uint4 d = v[i];
+    auto visit16 = [&](const uint4& d, int64_t i) {
       const uint32_t w[4] = {d.x, d.y, d.z, d.w};
       const int32_t base = (int32_t)(i * E::kVec);
       if constexpr (E::kVec == 8) {
@@ -69,7 +68,19 @@ __device__ inline void visit_row(const typename E::Bits* row, int64_t V, F&& f) 
 #pragma unroll
         for (int j = 0; j < 4; ++j) f(base + j, w[j]);
       }
+    };
+    // Two loads per thread in flight before either is used (their latencies overlap), then the
+    // remainder one at a time.
+    constexpr int kU = 2;
+    int64_t i = threadIdx.x;
+    for (; i + (kU - 1) * kThreads < nv; i += kU * kThreads) {
+      uint4 d[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) d[u] = v[i + u * kThreads];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) visit16(d[u], i + u * kThreads);
     }
+    for (; i < nv; i += kThreads) visit16(v[i], i);
     done = nv * E::kVec;
   }
   for (int64_t i = done + threadIdx.x; i < V; i += kThreads) f((int32_t)i, (uint32_t)row[i]);
