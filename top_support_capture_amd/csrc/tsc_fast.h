@@ -1043,8 +1043,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
     if (decision != kProceed && lane == 0) fs.decision = decision;
     lds_publish(&fs.scan_ready, 1u);
-    // Wave 0 picks the token once every race draw is done (it has the row's scalars at hand).
-    lds_wait_at_least(&fs.ready, jobs * kStep);
+    // Wave 0 picks the token once every race draw is done; it waits for them just before the
+    // pick, after the row scalars below are read, so that none of that sits after the last draw.
     picker = true;
   } else {
     __builtin_amdgcn_s_setprio(2);
@@ -1121,6 +1121,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // ---- 5. The pick, then the ordered capture of the opt-in row -----------------------------
   if (picker) {
     __builtin_amdgcn_s_setprio(3);
+    lds_wait_at_least(&fs.ready, jobs * kStep);
     // The support is bins d = 0..d*; bin d holds key kmax - d at index dspan - d. Float32 scores
     // first; bins within kRaceMargin of the best are rescored in float64, ties -> lowest id.
     float b1 = -__builtin_inff(), b2 = -__builtin_inff();
