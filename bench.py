@@ -105,8 +105,14 @@ def cpu_baseline(wl, index: int, budget_s: float = 8.0, max_workers: int = 16) -
         res = pool.map(_oracle_rows, [(w, ncores, budget_s) for w in range(ncores)])
     rate = sum(n / b for n, b in res)
     total = sum(n for n, _ in res)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": rate, "unit": "rows/s", "cores": ncores, "kind": "oracle",
-            "single_core_value": n1 / t1,
+            "single_core_value": n1 / t1, "cpu_model": model,
             "sample": f"{total} rows of the B={wl.B}, V={wl.V} {wl.dtype} batch (cycled) through "
                       f"oracle.sample_row, {ncores} worker processes x {budget_s:.0f} s each "
                       f"(one thread each), plus {n1} rows in one process for the 1-core rate; "
