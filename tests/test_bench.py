@@ -1,0 +1,59 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the config record, the HBM-counter
+ingestion and the kernel source hash."""
+import csv
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_param_summary():
+    assert bench.param_summary(np.full(4, 1024, np.int32)) == 1024
+    assert bench.param_summary(np.full(3, 0.95, np.float32)) == np.float32(0.95).item()
+    assert bench.param_summary(np.array([0.5, 1.5, 1.0], np.float32)) == "per row, 0.5..1.5"
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_ingest_pmc_scales_by_the_copy_kernel(tmp_path):
+    # The copy of 1 MiB reads half its bytes on FETCH_SIZE (scale 2) and all on WRITE_SIZE.
+    copy_bytes = 2**20
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    samp = "void tsc::sample_fast_kernel<1, false>(tsc::SampleArgs)"
+    neg = "void at::native::neg_kernel_cuda(...)"
+    _counter_csv(fetch, "FETCH_SIZE", [(samp, 600.0), (samp, 600.0), (neg, 512.0)])
+    _counter_csv(write, "WRITE_SIZE", [(samp, 10.0), (neg, 1024.0)])
+    t = bench.ingest_pmc(str(fetch), str(write), alg_bytes=1_200_000, copy_bytes=copy_bytes)
+    f, w = t["counters"]["FETCH_SIZE"], t["counters"]["WRITE_SIZE"]
+    assert f["scale"] == 2.0 and w["scale"] == 1.0
+    assert f["kernel_bytes_scaled"] == 600.0 * 1024 * 2
+    assert w["kernel_bytes_scaled"] == 10.0 * 1024
+    assert t["hbm_bytes_per_launch"] == 600.0 * 1024 * 2 + 10.0 * 1024
+    assert t["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_kernel_source_hash_is_stable():
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and h == bench.kernel_source_hash()
