@@ -283,8 +283,13 @@ def _fast_rows(rng, V):
     # form of the bin scan, served by the single-read path.
     wide = np.round(rng.standard_normal(V) * 4) / 4
     wide[rng.choice(V, 40, replace=False)] = np.round(np.geomspace(8.0, 60.0, 40))
+    # The maximum is zero, held by +0 and -0 tokens (they tie), over a negative bulk.
+    zeros = -np.abs(rng.standard_normal(V)) - 0.5
+    zpos = rng.choice(V, 12, replace=False)
+    zeros[zpos[:6]] = 0.0
+    zeros[zpos[6:]] = -0.0
     return dict(grid=grid, gauss=gauss, neg=neg, nan=nan, pinf=pinf, allneg=allneg,
-                hidden=hidden, front=front, spread=spread, wide=wide)
+                hidden=hidden, front=front, spread=spread, wide=wide, zeros=zeros)
 
 
 FAST_PARAMS = [
@@ -309,6 +314,11 @@ FAST_PARAMS = [
     ("wide_span_minp", "wide", 12.0, 1024, 1.0, 0.01),
     ("tiny_T", "gauss", 1e-3, 50, 0.9, 0.0),
     ("greedy", "grid", 0.0, 50, 0.9, 0.0),
+    ("min_p_one", "grid", 1.0, 500, 0.9, 1.0),           # only the top tie group
+    ("signed_zero_top_k1", "zeros", 1.0, 1, 1.0, 0.0),   # -0 and +0 tie at the maximum
+    ("signed_zero_p0", "zeros", 0.7, 300, 0.0, 0.0),
+    ("huge_T", "gauss", 1.0e30, 1024, 0.95, 0.0),        # every weight is 1: top-k decides
+    ("top_p_zero_ties", "grid", 1.0, 1024, 0.0, 0.0),
     # top_k above 1536: the compaction mode of the single-read path
     ("compact_k4000_p9", "gauss", 1.0, 4000, 0.9, 0.0),
     ("compact_k8192_p1", "gauss", 1.0, 8192, 1.0, 0.0),
