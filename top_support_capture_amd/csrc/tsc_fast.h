@@ -41,6 +41,7 @@ constexpr int kFastLoads = 32;
 constexpr int kLoadsFirst = 2;        // loads issued before the first one is awaited
 constexpr int kLoadsAhead = 4;        // software pipeline depth afterwards (loads in flight per lane)
 constexpr int kStashPerWave = 256;    // stashed loads per wave (stash mode)
+constexpr int kSpillPerWave = 512;    // stash mode: flagged loads past the stash, read again later
 constexpr int kDBins = 1024;          // histogram bins over the key span above the cutoff
 // Key distances of the sampled maxima below their maximum: heavy-tailed rows (a Zipf-like head
 // over a wide vocabulary) need theta over 256 keys (two binades of bf16) below it.
@@ -48,7 +49,7 @@ constexpr int kThetaBins = 512;
 constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;     // 262144
 constexpr int64_t kShortMaxV = (int64_t)kWaves * kWaveSize * kShortLoads * 8;   // 163840
-constexpr int32_t kFastMaxK = 1536;   // stash mode; compaction mode above it
+constexpr int32_t kFastMaxK = 4096;   // stash mode; compaction mode above it
 constexpr int32_t kCompactMaxK = 8192;
 constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
 // Waves whose stream ends among the first kOwnDraws draw the race uniforms of their own
@@ -85,11 +86,13 @@ struct TailLayout {
 // candidates' ranks.
 constexpr int kStashBytes = kWaves * kStashPerWave * 16;
 constexpr int kStashChBytes = kWaves * kStashPerWave * 4;
-struct LayoutStash : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4> {
+struct LayoutStash
+    : TailLayout<kStashBytes + kStashChBytes + kWaves * 512 * 4 + kWaves * kSpillPerWave * 2> {
   static constexpr int kCandCap = 512;                      // candidate words per wave
   static constexpr int kOffStash = 0;                       // uint4 [16][256]
   static constexpr int kOffStashCh = kStashBytes;           // u32 [16][256]
   static constexpr int kOffCand = kOffStashCh + kStashChBytes;  // u32 [16][512]
+  static constexpr int kOffSpill = kOffCand + kWaves * kCandCap * 4;  // u16 [16][512] chunks
   static constexpr int kOffTables = kOffStash;              // u16 [1024] + u64 [256] per wave
   static constexpr int kTableStride = kStashPerWave * 16;
   static constexpr int kOffRank = kOffStashCh;              // u16 [16][512]
@@ -647,19 +650,31 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
     wcnt += total;
   };
+  uint16_t* spill = reinterpret_cast<uint16_t*>(lds + LayoutStash::kOffSpill) + wid * kSpillPerWave;
   auto stash_load = [&](int j, const uint4& q, bool flag) {
     const uint64_t mask = __ballot(flag);
     const uint32_t n = (uint32_t)__popcll(mask);
     // Capacity is checked per load for the whole wave (scalar), so the flagged lanes only
-    // compute their slot; a load that does not fit is dropped and the row falls back.
-    if (n != 0u && wcnt + n <= (uint32_t)kStashPerWave) {
-      if (flag) {
-        const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, wcnt));
-        stash[at] = q;
-        stash_ch[at] = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
+    // compute their slot. A load that no longer fits the stash (and every later one: the count
+    // only grows) keeps just its chunk index, and is read again after the stream; past that
+    // list too, the row falls back.
+    if (n != 0u) {
+      const uint32_t chunk = (uint32_t)j * kWaveSize + lane;  // chunk within the segment
+      if (wcnt + n <= (uint32_t)kStashPerWave) {
+        if (flag) {
+          const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, wcnt));
+          stash[at] = q;
+          stash_ch[at] = chunk;
+        }
+        wfill = wcnt + n;
+      } else if (wcnt - wfill + n <= (uint32_t)kSpillPerWave) {
+        if (flag) {
+          const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, wcnt - wfill));
+          spill[at] = (uint16_t)chunk;
+        }
       }
-      wfill = wcnt + n;
     }
     wcnt += n;
   };
@@ -820,7 +835,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
     if (lane == 0) {
       fs.wave_z[wid] = wz;
-      fs.wave_stash[wid] = COMPACT ? 0u : wcnt;
+      fs.wave_stash[wid] = COMPACT ? 0u : wcnt - wfill;  // loads past the stash
     }
   }
   // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
@@ -834,28 +849,11 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     ncand = wcnt;
     xcand = m_l >= th ? m_l : -__builtin_inff();  // the lane maximum is a candidate iff >= theta
   } else {
-    // Stash expansion: candidate words of the stashed loads, in id order.
+    // Stash expansion: candidate words of the stashed loads, then of the loads past the stash
+    // (read again now), in id order. Lanes without a load hold -inf, which no candidate is.
     uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + LY::kOffDummy) + lane;
-    const uint32_t nstash = wfill;  // never slots that were not written in this row
-    // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
-    constexpr int kChunks = kStashPerWave / kWaveSize;
-    uint4 qs[kChunks];
-    uint32_t offs[kChunks];
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      const uint32_t i = (uint32_t)ch * kWaveSize + lane;
-      qs[ch] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-      offs[ch] = 0u;
-      if ((uint32_t)ch * kWaveSize < nstash && i < nstash) {
-        qs[ch] = stash[i];
-        offs[ch] = stash_ch[i] * 8u;
-      }
-    }
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      if ((uint32_t)ch * kWaveSize >= nstash) break;
-      const uint32_t w4[4] = {qs[ch].x, qs[ch].y, qs[ch].z, qs[ch].w};
-      const uint32_t off = offs[ch];
+    auto expand_chunk = [&](const uint4& q, uint32_t off) {
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
       uint32_t words[8];
       bool isc[8];
       float xc[8];
@@ -879,6 +877,51 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         at += isc[e];
       }
       ncand += total;
+    };
+    const uint4 kNone = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    const uint32_t nstash = wfill;  // never slots that were not written in this row
+    // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
+    constexpr int kChunks = kStashPerWave / kWaveSize;
+    uint4 qs[kChunks];
+    uint32_t offs[kChunks];
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      const uint32_t i = (uint32_t)ch * kWaveSize + lane;
+      qs[ch] = kNone;
+      offs[ch] = 0u;
+      if ((uint32_t)ch * kWaveSize < nstash && i < nstash) {
+        qs[ch] = stash[i];
+        offs[ch] = stash_ch[i] * 8u;
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      if ((uint32_t)ch * kWaveSize >= nstash) break;
+      expand_chunk(qs[ch], offs[ch]);
+    }
+    // Loads past the stash (when the list overflowed, the row falls back: none are read).
+    const uint32_t nspill = wcnt - wfill <= (uint32_t)kSpillPerWave ? wcnt - wfill : 0u;
+    for (uint32_t base = 0; base < nspill; base += kChunks * kWaveSize) {
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+        const uint32_t i = base + (uint32_t)ch * kWaveSize + lane;
+        qs[ch] = kNone;
+        offs[ch] = 0u;
+        if (base + (uint32_t)ch * kWaveSize < nspill && i < nspill) {
+          // (A lane past the segment's end holds -inf in the stream; its chunk is not read.)
+          const uint32_t chunk = spill[i];
+          if (chunk < nseg) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(chunk * 16u), 0, 0);
+            qs[ch] = make_uint4(v.x, v.y, v.z, v.w);
+            offs[ch] = chunk * 8u;
+          }
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+        if (base + (uint32_t)ch * kWaveSize >= nspill) break;
+        expand_chunk(qs[ch], offs[ch]);
+      }
     }
   }
   // The wave's count table (in stash mode its stash slice, free now).
@@ -998,7 +1041,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const uint32_t w = lane & (kWaves - 1);
     const float m = row16_reduce(fs.wave_m[w], MaximumF32());
     const uint32_t ntot = row16_reduce(fs.wave_cand[w], SumU32());
-    const bool over = __ballot(fs.wave_stash[w] > (uint32_t)kStashPerWave ||
+    const bool over = __ballot(fs.wave_stash[w] > (uint32_t)kSpillPerWave ||
                                fs.wave_cand[w] > (uint32_t)LY::kCandCap) != 0;
     // A NaN logit: in the running maximum when top_p = 1, in the mass when top_p < 1.
     double zr = 0.0;
