@@ -319,7 +319,8 @@ FAST_PARAMS = [
     ("signed_zero_p0", "zeros", 0.7, 300, 0.0, 0.0),
     ("huge_T", "gauss", 1.0e30, 1024, 0.95, 0.0),        # every weight is 1: top-k decides
     ("top_p_zero_ties", "grid", 1.0, 1024, 0.0, 0.0),
-    # top_k above 1536: the compaction mode of the single-read path
+    # top_k above 1536: stash mode with loads past the stash read again (top_k <= 4096), the
+    # compaction mode above that; tiny_T above flags every load, overflows both and falls back
     ("compact_k4000_p9", "gauss", 1.0, 4000, 0.9, 0.0),
     ("compact_k8192_p1", "gauss", 1.0, 8192, 1.0, 0.0),
     ("compact_grid_k2000", "grid", 0.8, 2000, 0.95, 0.0),
