@@ -516,13 +516,14 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   // Rank of theta among the lane maxima of the first loads: a maximum of 8 values exceeds the
   // quantile 1 - q with probability 1 - (1-q)^8. The sample is the lane maxima of the first two
-  // loads (2048 values, 16384 elements). A target of 1.6 k + 64 candidates (stash mode) or
-  // 1.2 k + 320 (compaction mode, larger k: a relatively tighter estimate) keeps the k-th
-  // largest value above theta by about five standard deviations of the estimate.
+  // loads (2048 values, 16384 elements). A target of 1.6 k + 64 candidates, or 1.2 k + 320 for
+  // k above 1536 (the estimate's relative error shrinks as k grows), keeps the k-th largest
+  // value above theta by about five standard deviations of the estimate.
   constexpr int kSamples = 2 * kThreads;
   uint32_t theta_rank;
   {
-    const float target = COMPACT ? 1.2f * (float)k + 320.0f : 1.6f * (float)k + 64.0f;
+    const float target =
+        k > 1536 ? 1.2f * (float)k + 320.0f : 1.6f * (float)k + 64.0f;
     const float q = fminf(1.0f, target / (float)V);
     const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
     const float pr = 1.0f - t4 * t4;
@@ -879,9 +880,32 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       ncand += total;
     };
     const uint4 kNone = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    constexpr int kChunks = kStashPerWave / kWaveSize;
+    // Loads past the stash (when the list overflowed, the row falls back: none are read). The
+    // first batch is read before the stash is expanded, so that its latency overlaps that work.
+    const uint32_t nspill = wcnt - wfill <= (uint32_t)kSpillPerWave ? wcnt - wfill : 0u;
+    uint4 sq[kChunks];
+    uint32_t so[kChunks];
+    auto read_spills = [&](uint32_t base) {
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+        const uint32_t i = base + (uint32_t)ch * kWaveSize + lane;
+        sq[ch] = kNone;
+        so[ch] = 0u;
+        if (base + (uint32_t)ch * kWaveSize < nspill && i < nspill) {
+          // (A lane past the segment's end holds -inf in the stream; its chunk is not read.)
+          const uint32_t chunk = spill[i];
+          if (chunk < nseg) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(chunk * 16u), 0, 0);
+            sq[ch] = make_uint4(v.x, v.y, v.z, v.w);
+            so[ch] = chunk * 8u;
+          }
+        }
+      }
+    };
+    if (nspill > 0u) read_spills(0u);
     const uint32_t nstash = wfill;  // never slots that were not written in this row
     // All stash reads first (at most 4 chunks of 64 loads), so that their latencies overlap.
-    constexpr int kChunks = kStashPerWave / kWaveSize;
     uint4 qs[kChunks];
     uint32_t offs[kChunks];
 #pragma unroll
@@ -899,28 +923,12 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if ((uint32_t)ch * kWaveSize >= nstash) break;
       expand_chunk(qs[ch], offs[ch]);
     }
-    // Loads past the stash (when the list overflowed, the row falls back: none are read).
-    const uint32_t nspill = wcnt - wfill <= (uint32_t)kSpillPerWave ? wcnt - wfill : 0u;
     for (uint32_t base = 0; base < nspill; base += kChunks * kWaveSize) {
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        const uint32_t i = base + (uint32_t)ch * kWaveSize + lane;
-        qs[ch] = kNone;
-        offs[ch] = 0u;
-        if (base + (uint32_t)ch * kWaveSize < nspill && i < nspill) {
-          // (A lane past the segment's end holds -inf in the stream; its chunk is not read.)
-          const uint32_t chunk = spill[i];
-          if (chunk < nseg) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(chunk * 16u), 0, 0);
-            qs[ch] = make_uint4(v.x, v.y, v.z, v.w);
-            offs[ch] = chunk * 8u;
-          }
-        }
-      }
+      if (base > 0u) read_spills(base);
 #pragma unroll
       for (int ch = 0; ch < kChunks; ++ch) {
         if (base + (uint32_t)ch * kWaveSize >= nspill) break;
-        expand_chunk(qs[ch], offs[ch]);
+        expand_chunk(sq[ch], so[ch]);
       }
     }
   }
