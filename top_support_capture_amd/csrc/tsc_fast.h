@@ -5,12 +5,13 @@
 // (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
 //
 //   1. Stream. The lane maxima of the first loads of every segment (a sample spread over the
-//      whole row) give a reference R for the mass and a cutoff theta that about 1.6 top_k tokens
-//      of the row should exceed: an LDS histogram of their key distances to the sample's maximum,
+//      whole row) give a reference R for the mass and a cutoff theta that about 1.2-1.6 top_k
+//      tokens of the row should exceed: an LDS histogram of their key distances to the sample's maximum,
 //      built over the first stream steps so that the loads keep flowing.
 //   2. As each load lands: running maximum (NaN-propagating, so it also detects NaN), for
 //      top_p < 1 the lane sum of exp2(x * log2(e) / T - R * log2(e) / T), and a ballot on "this
-//      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash.
+//      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash
+//      (or, in compaction mode, appends its values >= theta to the wave's candidate list).
 //   3. Each wave, as soon as its segment is done: expands its stash into candidate words
 //      (bf16 bits << 16 | offset in the segment), still in id order, counts them into a
 //      histogram over key - key(theta) and ranks each among its wave's earlier candidates of
@@ -57,9 +58,10 @@ constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of
 constexpr uint32_t kOwnDraws = 4;
 
 // Two modes share everything but the way candidates are gathered during the stream:
-//   stash mode (top_k <= 1536): a load that may hold a value >= theta is stashed whole in LDS
-//     (one ballot per load) and expanded into candidates once the wave's stream has ended;
-//   compaction mode (1536 < top_k <= 8192, where most loads hold candidates): the values >= theta
+//   stash mode (top_k <= 4096): a load that may hold a value >= theta is stashed whole in LDS
+//     (one ballot per load) and expanded into candidates once the wave's stream has ended; past
+//     the stash's capacity a flagged load keeps only its chunk index and is read again then;
+//   compaction mode (4096 < top_k <= 8192, where most loads hold candidates): the values >= theta
 //     of each load are appended to the wave's candidate list as the load lands.
 // Each wave counts its candidates per bin bi = key - theta_key in a table of its own (u16; later
 // the exclusive prefix over the earlier waves) and ranks each among its earlier candidates of the
