@@ -854,7 +854,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   } else {
     // Stash expansion: candidate words of the stashed loads, then of the loads past the stash
     // (read again now), in id order. Lanes without a load hold -inf, which no candidate is.
-    uint32_t* dummy = reinterpret_cast<uint32_t*>(lds + LY::kOffDummy) + lane;
     auto expand_chunk = [&](const uint4& q, uint32_t off) {
       const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
       uint32_t words[8];
@@ -873,10 +872,11 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       xcand = maximum3f(xcand, xc[6], xc[7]);
       uint32_t total;
       uint32_t at = ncand + wave_excl_sum(n, total);
+      // Predicated stores (only candidates are written): fewer instructions than sending the
+      // other elements to a dummy slot.
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t* dst = (isc[e] && at < (uint32_t)LY::kCandCap) ? cand + at : dummy;
-        *dst = words[e];
+        if (isc[e] && at < (uint32_t)LY::kCandCap) cand[at] = words[e];
         at += isc[e];
       }
       ncand += total;
