@@ -77,3 +77,36 @@ def test_sampler_in_a_graph(index, bits):
     assert np.array_equal(got_csr[0], eager_csr[0])
     for a, b in zip(got_csr[1:], eager_csr[1:]):
         assert np.array_equal(a[:n], b[:n])
+
+
+def test_concurrent_streams():
+    # Two batches sampled at the same time on two streams (the library keeps no per-call state)
+    # give what each gives alone.
+    import top_support_capture_amd as tsc
+    log("case two streams at once: workloads 3 and 4")
+    outs = {}
+    calls = {}
+    for index in (3, 4):
+        wl = make_workload(index)
+        d = device_inputs(wl)
+        calls[index] = (wl, d)
+        o = tsc.sample_with_mask(d["logits"], d["temperature"], d["top_k"], d["top_p"],
+                                 d["min_p"], d["optin_rows"], d["seeds"], d["positions"], wl.W)
+        torch.cuda.synchronize()
+        outs[index] = _defined(o)
+    s3, s4 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(5):
+        res = {}
+        for index, s in ((3, s3), (4, s4)):
+            wl, d = calls[index]
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                res[index] = tsc.sample_with_mask(d["logits"], d["temperature"], d["top_k"],
+                                                  d["top_p"], d["min_p"], d["optin_rows"],
+                                                  d["seeds"], d["positions"], wl.W, stream=s)
+        torch.cuda.synchronize()
+        for index in (3, 4):
+            got = _defined(res[index])
+            assert len(got) == len(outs[index])
+            for a, b in zip(got, outs[index]):
+                assert np.array_equal(a, b)
