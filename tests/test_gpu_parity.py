@@ -350,3 +350,21 @@ def test_single_read_path_rows(V):
         assert errs == [], [(e, names[int(e.split()[1].rstrip(':'))]) if e.startswith("row") else e for e in errs]
         check(wl, got, ref, max_flagged_frac=0.2)
         check_bits(wl, got, ref, min_rows=0 if W == 2048 else 10)
+
+
+def test_empty_batch():
+    # B = 0 (and a replay of N = 0 rows): no launch, empty outputs, no error.
+    import torch
+    import top_support_capture_amd as tsc
+    log("case empty batch")
+    dev = "cuda:0"
+    e = lambda dt: torch.empty(0, dtype=dt, device=dev)
+    x = torch.empty((0, 32768), dtype=torch.bfloat16, device=dev)
+    out = tsc.sample_with_mask(x, e(torch.float32), e(torch.int32), e(torch.float32),
+                               e(torch.float32), e(torch.int32), e(torch.int64), e(torch.int64), 16)
+    torch.cuda.synchronize()
+    assert out.tokens.numel() == 0 and out.packed_ids.shape == (0, 16)
+    rep = tsc.replay_logprob(x, e(torch.float32), torch.empty((0, 16), dtype=torch.int32, device=dev),
+                             e(torch.int32), e(torch.int32))
+    torch.cuda.synchronize()
+    assert rep.selected_logprob.numel() == 0 and rep.row_status.numel() == 0
