@@ -187,8 +187,9 @@ def param_summary(v):
     range."""
     import numpy as np
     v = np.asarray(v)
+    one = lambda x: float(f"{x:.6g}") if isinstance(x, float) else x
     if np.all(v == v[0]):
-        return v[0].item()
+        return one(v[0].item())
     return f"per row, {v.min().item():.4g}..{v.max().item():.4g}"
 
 

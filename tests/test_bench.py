@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_param_summary():
     assert bench.param_summary(np.full(4, 1024, np.int32)) == 1024
-    assert bench.param_summary(np.full(3, 0.95, np.float32)) == np.float32(0.95).item()
+    assert bench.param_summary(np.full(3, 0.95, np.float32)) == 0.95
     assert bench.param_summary(np.array([0.5, 1.5, 1.0], np.float32)) == "per row, 0.5..1.5"
 
 
