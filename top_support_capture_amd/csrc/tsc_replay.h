@@ -162,51 +162,64 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
       acc.add(E::to_float((uint32_t)row[id]), c);
     }
   } else {
-    // Chunks of 8 ids, one mask byte each; a chunk with members is loaded whole (16 bytes of
-    // bfloat16, 32 of float32) when the row allows aligned vector loads; each thread takes four
-    // consecutive chunks per step, so that their loads are in flight together.
+    // Chunks of 8 ids, one mask byte each: chunk c0 + s * kThreads at step s, so that
+    // neighbouring lanes take neighbouring chunks and every load instruction is coalesced. The
+    // mask bytes of kS steps are read first, then the chunks with members, kB steps at a time:
+    // one 16-byte vector load per chunk of bfloat16 (two of float32) when the row is 16-byte
+    // aligned, element loads otherwise and for a last, partial chunk.
+    constexpr bool kHalf = sizeof(typename E::Bits) == 2;
+    constexpr int kS = 16, kB = kHalf ? 8 : 4, kV = kHalf ? 1 : 2;
     const int64_t nchunks = (V + 7) / 8;
     const int64_t nfull = V / 8;  // chunks wholly inside the row
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-    constexpr int kQ = 4;
-    for (int64_t q0 = (int64_t)tid * kQ; q0 < nchunks; q0 += (int64_t)kThreads * kQ) {
-      uint32_t bytes[kQ];
-      float x[kQ][8];
+    for (int64_t c0 = tid; c0 < nchunks; c0 += (int64_t)kThreads * kS) {
+      uint32_t bytes[kS];
 #pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-        const int64_t ch = q0 + u;
+      for (int s = 0; s < kS; ++s) {
+        const int64_t ch = c0 + (int64_t)s * kThreads;
         uint32_t byte = ch < nchunks ? brow[ch] : 0u;
         if (ch == nchunks - 1 && (V & 7)) byte &= (1u << (V & 7)) - 1u;  // bits past V
-        bytes[u] = byte;
+        bytes[s] = byte;
       }
 #pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-        const int64_t ch = q0 + u;
-        if (vec && ch < nfull && bytes[u] != 0u) {
-          if constexpr (sizeof(typename E::Bits) == 2) {
-            const uint4 v = *reinterpret_cast<const uint4*>(row + ch * 8);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      for (int s0 = 0; s0 < kS; s0 += kB) {
+        uint4 raw[kB][kV];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[u][e] = E::to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          } else {
-            const uint4 v0 = *reinterpret_cast<const uint4*>(row + ch * 8);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(row + ch * 8 + 4);
-            const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        for (int u = 0; u < kB; ++u) {
+          const int64_t ch = c0 + (int64_t)(s0 + u) * kThreads;
+          if (vec && ch < nfull && bytes[s0 + u] != 0u) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[u][e] = E::to_float(w8[e]);
+            for (int h = 0; h < kV; ++h) raw[u][h] = *reinterpret_cast<const uint4*>(row + ch * 8 + 4 * h);
           }
-        } else {
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int64_t ch = c0 + (int64_t)(s0 + u) * kThreads;
+          const uint32_t byte = bytes[s0 + u];
+          if (byte == 0u) continue;
+          float x[8];
+          if (vec && ch < nfull) {
+            if constexpr (kHalf) {
+              const uint32_t w4[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = E::to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            } else {
+              const uint32_t w8[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
+                                      raw[u][kV - 1].x, raw[u][kV - 1].y, raw[u][kV - 1].z,
+                                      raw[u][kV - 1].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = E::to_float(w8[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              x[e] = (byte >> e) & 1u ? E::to_float((uint32_t)row[ch * 8 + e]) : 0.0f;
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            x[u][e] = (bytes[u] >> e) & 1u ? E::to_float((uint32_t)row[ch * 8 + e]) : 0.0f;
+            if ((byte >> e) & 1u) acc.add(x[e], c);
+          if ((int64_t)tok >> 3 == ch && ((byte >> (tok & 7)) & 1u)) acc.flags |= OnlineLse::kFound;
         }
-      }
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if ((bytes[u] >> e) & 1u) acc.add(x[u][e], c);
-        if ((int64_t)tok >> 3 == q0 + u && ((bytes[u] >> (tok & 7)) & 1u)) acc.flags |= OnlineLse::kFound;
       }
     }
   }
