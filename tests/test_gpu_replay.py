@@ -19,11 +19,12 @@ pytestmark = pytest.mark.gpu
 LP_TOL = 1e-5
 
 
-def run_replay(logits, dtype, T, ids, lengths, tokens, cs=None, bits=None, return_logprobs=True):
+def run_replay(logits, dtype, T, ids, lengths, tokens, cs=None, bits=None, return_logprobs=True,
+               pad=0):
     import top_support_capture_amd as tsc
     dev = "cuda:0"
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
-    out = tsc.replay_logprob(logits_tensor(logits, dtype), t(T, torch.float32),
+    out = tsc.replay_logprob(logits_tensor(logits, dtype, pad=pad), t(T, torch.float32),
                              t(ids, torch.int32), t(lengths, torch.int32), t(tokens, torch.int32),
                              None if cs is None else t(cs, torch.int8),
                              None if bits is None else t(bits, torch.uint8),
@@ -199,3 +200,54 @@ def test_replay_large_vocabulary_gathers():
     ref = oracle.replay(xx, "bf16", T, ids, lengths, tokens)
     errs, n, _ = compare_replay(got, ref, lengths)
     assert errs == [] and n == N, errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,extra,pad", [(1029, 0, 0), (1029, 3, 0), (1029, 11, 0), (4096, 0, 0),
+                                         (4096, 5, 0), (777, 7, 0), (1029, 15, 3), (1029, 3, 3)])
+def test_replay_bitmask_strides(dtype, V, extra, pad):
+    # Overflow rows whose supports come from bitmask rows of stride ceil(V / 8) + extra bytes:
+    # some rows 16-byte aligned and some not, with a ragged last byte (V % 8 != 0), junk bits past
+    # V and junk bytes past ceil(V / 8); densities from one member to every id. With pad, the
+    # logits rows have stride V + pad, so that every row is 16-byte aligned despite a ragged V.
+    rng = np.random.default_rng(V * 31 + extra)
+    N = 12
+    nb = (V + 7) // 8
+    ld = nb + extra
+    x = rng.standard_normal((N, V)).astype(np.float32) * 3.0
+    density = [0.0005, 0.002, 0.01, 0.05, 0.2, 0.5, 0.9, 1.0, 0.03, 0.3, 0.001, 0.7]
+    bits = rng.integers(0, 256, (N, ld), dtype=np.uint8)  # junk everywhere, then the masks
+    tokens = np.zeros(N, np.int32)
+    for j in range(N):
+        keep = rng.random(V) < density[j]
+        keep[rng.integers(V)] = True
+        bits[j, :nb] = np.packbits(keep, bitorder="little")
+        if V % 8:
+            bits[j, nb - 1] |= np.uint8((0xFF << (V % 8)) & 0xFF)  # bits past V
+        members = np.nonzero(keep)[0]
+        tokens[j] = members[rng.integers(members.size)] if j % 3 else V - 1 - (j % 5)
+    ids = np.zeros((N, 4), np.int32)
+    lengths = np.ones(N, np.int32)
+    T = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    cs = np.ones(N, np.int8)
+    member = lambda j: np.nonzero(np.unpackbits(bits[j, :nb], bitorder="little")[:V])[0]
+    x[2, member(2)[-1]] = np.nan                       # a NaN member: NONFINITE
+    x[4, member(4)[0]] = np.inf                        # a +inf member: NONFINITE
+    x[6, member(6)] = -np.inf                          # every member -inf: NO_SUPPORT
+    x[3, np.setdiff1d(np.arange(V), member(3))] = np.nan  # NaN outside the support: ignored
+    x[5, member(5)[::2]] = -np.inf                     # some members -inf
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        xx = f32_to_bf16_bits(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+        xx[np.isnan(x)] = 0x7FC0
+        xx[np.isposinf(x)] = 0x7F80
+        xx[np.isneginf(x)] = 0xFF80
+    else:
+        xx = x
+    log(f"case replay bitmask strides {dtype} V={V} bits ld={ld} pad={pad}")
+    got = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits, return_logprobs=False, pad=pad)
+    ref = oracle.replay(xx, dtype, T, ids, lengths, tokens, cs, bits)
+    errs, n, _ = compare_replay(got, ref, lengths)
+    assert errs == [] and n == int(np.sum(ref[2] == 0)) == N - 3, errs
+    assert got[2][2] == 3 and got[2][4] == 3 and got[2][6] == 2 and got[2][3] == 0
+    assert np.sum(np.isfinite(got[0])) >= 4

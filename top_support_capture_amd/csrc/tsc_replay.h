@@ -30,6 +30,11 @@ struct ReplayArgs {
   int8_t* row_status;            // [N]
 };
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 struct ReplayShared {
   float m[kWaves];
   float s[kWaves];
@@ -52,6 +57,17 @@ struct OnlineLse {
     } else if (x != -__builtin_inff()) {
       s += __builtin_amdgcn_exp2f((x - m) * c);
     }
+  }
+  // One chunk of 8 logits with the non-members already set to -inf, cm their maximum: one
+  // rescale to the new maximum, then one exponential per position, with no branch. A NaN or
+  // +inf member leaves s NaN for good (the caller flags it once, after its pass); -inf adds 0.
+  __device__ inline void add_masked(const float (&xm)[8], float cm, float c) {
+    const float mn = cm > m ? cm : m;
+    s *= mn == m ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);  // m = -inf: s is 0 and stays 0
+    m = mn;
+    const float base = m == -__builtin_inff() ? 0.0f : m;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((xm[e] - base) * c);
   }
   static constexpr uint32_t kBad = 1, kBadId = 2, kFound = 4, kSeen = 8;
 };
@@ -162,66 +178,115 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
       acc.add(E::to_float((uint32_t)row[id]), c);
     }
   } else {
-    // Chunks of 8 ids, one mask byte each: chunk c0 + s * kThreads at step s, so that
-    // neighbouring lanes take neighbouring chunks and every load instruction is coalesced. The
-    // mask bytes of kS steps are read first, then the chunks with members, kB steps at a time:
-    // one 16-byte vector load per chunk of bfloat16 (two of float32) when the row is 16-byte
-    // aligned, element loads otherwise and for a last, partial chunk.
+    // Chunks of 8 ids, one mask byte each; non-members become -inf, so that every chunk takes
+    // the same branch-free update. With a 16-byte aligned row, the mask bytes of kS chunks are
+    // read first, then all the chunks with members at once, one 16-byte vector load per chunk
+    // of bfloat16 (two of float32). When the mask row is 16-byte aligned too (as the sampler
+    // writes them) a thread takes kS consecutive chunks and reads their mask bytes in one load;
+    // otherwise it takes chunk c0 + s * kThreads at step s, so that neighbouring lanes read
+    // neighbouring mask bytes. Rows that are not aligned, and a last, partial chunk, take
+    // element loads.
     constexpr bool kHalf = sizeof(typename E::Bits) == 2;
-    constexpr int kS = 16, kB = kHalf ? 8 : 4, kV = kHalf ? 1 : 2;
-    const int64_t nchunks = (V + 7) / 8;
-    const int64_t nfull = V / 8;  // chunks wholly inside the row
-    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-    for (int64_t c0 = tid; c0 < nchunks; c0 += (int64_t)kThreads * kS) {
-      uint32_t bytes[kS];
+    constexpr int kS = kHalf ? 16 : 8, kV = kHalf ? 1 : 2;  // kS loads of 16 * kV bytes in flight
+    const uint32_t nfull = (uint32_t)(V / 8);  // chunks wholly inside the row
+    uint32_t seen = 0;
+    auto update = [&](uint32_t byte, const uint32_t (&fb)[8]) {  // fb: float32 bit patterns
+      float xm[8];
+      float cm = -__builtin_inff();
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const int64_t ch = c0 + (int64_t)s * kThreads;
-        uint32_t byte = ch < nchunks ? brow[ch] : 0u;
-        if (ch == nchunks - 1 && (V & 7)) byte &= (1u << (V & 7)) - 1u;  // bits past V
-        bytes[s] = byte;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t keep = (uint32_t)((int32_t)(byte << (31 - e)) >> 31);  // ones for a member
+        xm[e] = __uint_as_float((fb[e] & keep) | (0xFF800000u & ~keep));
+        cm = __builtin_fmaxf(cm, xm[e]);
       }
+      acc.add_masked(xm, cm, c);
+    };
+    auto element_chunk = [&](uint32_t ch, uint32_t byte) {
+      uint32_t fb[8];
 #pragma unroll
-      for (int s0 = 0; s0 < kS; s0 += kB) {
-        uint4 raw[kB][kV];
+      for (int e = 0; e < 8; ++e)
+        fb[e] = (byte >> e) & 1u ? __float_as_uint(E::to_float((uint32_t)row[(size_t)ch * 8 + e])) : 0u;
+      update(byte, fb);
+      seen |= byte;
+    };
+    if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
+      // One pass for each layout, compiled apart, so that each keeps its own simple addressing.
+      auto pass = [&](auto layout) {
+      constexpr bool wide = decltype(layout)::value;
+      auto chunk_of = [&](uint32_t g, int s) -> uint32_t {
+        return wide ? g * kS + (uint32_t)s : g + (uint32_t)s * kThreads;
+      };
+      const uint32_t ngroups = wide ? (nfull + kS - 1) / kS : nfull;
+      const uint32_t gstep = wide ? kThreads : kThreads * kS;
+      for (uint32_t g = tid; g < ngroups; g += gstep) {
+        uint32_t bw[kS / 4];  // the kS mask bytes, four to a word
+        if constexpr (wide) {  // bits_ld is a multiple of 16: the whole group lies inside the mask row
+          if constexpr (kS == 16) {
+            const uint4 mb = *reinterpret_cast<const uint4*>(brow + (size_t)g * kS);
+            bw[0] = mb.x, bw[1] = mb.y, bw[2] = mb.z, bw[3] = mb.w;
+          } else {
+            const uint2 mb = *reinterpret_cast<const uint2*>(brow + (size_t)g * kS);
+            bw[0] = mb.x, bw[1] = mb.y;
+          }
+        } else {
 #pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          const int64_t ch = c0 + (int64_t)(s0 + u) * kThreads;
-          if (vec && ch < nfull && bytes[s0 + u] != 0u) {
+          for (int q = 0; q < kS / 4; ++q) bw[q] = 0u;
 #pragma unroll
-            for (int h = 0; h < kV; ++h) raw[u][h] = *reinterpret_cast<const uint4*>(row + ch * 8 + 4 * h);
+          for (int s = 0; s < kS; ++s) {
+            const uint32_t ch = chunk_of(g, s);
+            bw[s >> 2] |= (ch < nfull ? (uint32_t)brow[ch] : 0u) << (8 * (s & 3));
           }
         }
 #pragma unroll
-        for (int u = 0; u < kB; ++u) {
-          const int64_t ch = c0 + (int64_t)(s0 + u) * kThreads;
-          const uint32_t byte = bytes[s0 + u];
-          if (byte == 0u) continue;
-          float x[8];
-          if (vec && ch < nfull) {
+        for (int s = 0; s < kS; ++s)  // chunks past the full ones: none
+          if (chunk_of(g, s) >= nfull) bw[s >> 2] &= ~(0xFFu << (8 * (s & 3)));
+#pragma unroll
+        for (int q = 0; q < kS / 4; ++q) seen |= bw[q];
+        auto byte_of = [&](int s) -> uint32_t { return (bw[s >> 2] >> (8 * (s & 3))) & 0xFFu; };
+        {
+          uint4 raw[kS][kV] = {};  // chunks without members stay 0; their positions are masked
+#pragma unroll
+          for (int u = 0; u < kS; ++u) {
+            if (byte_of(u) != 0u) {
+              const uint32_t ch = chunk_of(g, u);
+#pragma unroll
+              for (int h = 0; h < kV; ++h)
+                raw[u][h] = *reinterpret_cast<const uint4*>(row + (size_t)ch * 8 + 4 * h);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kS; ++u) {
+            uint32_t fb[8];
             if constexpr (kHalf) {
               const uint32_t w4[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
 #pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = E::to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+              for (int e = 0; e < 8; ++e) fb[e] = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
             } else {
               const uint32_t w8[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
                                       raw[u][kV - 1].x, raw[u][kV - 1].y, raw[u][kV - 1].z,
                                       raw[u][kV - 1].w};
 #pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = E::to_float(w8[e]);
+              for (int e = 0; e < 8; ++e) fb[e] = w8[e];
             }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              x[e] = (byte >> e) & 1u ? E::to_float((uint32_t)row[ch * 8 + e]) : 0.0f;
+            update(byte_of(u), fb);  // a chunk without members adds 0
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if ((byte >> e) & 1u) acc.add(x[e], c);
-          if ((int64_t)tok >> 3 == ch && ((byte >> (tok & 7)) & 1u)) acc.flags |= OnlineLse::kFound;
         }
       }
+      };
+      if ((reinterpret_cast<uintptr_t>(brow) & 15u) == 0 && (a.bits_ld & 15) == 0)
+        pass(BoolTag<true>{});
+      else
+        pass(BoolTag<false>{});
+    } else {
+      for (uint32_t ch = tid; ch < nfull; ch += kThreads) {
+        const uint32_t byte = brow[ch];
+        if (byte != 0u) element_chunk(ch, byte);
+      }
     }
+    if ((V & 7) && tid == kThreads - 1) element_chunk(nfull, brow[nfull] & ((1u << (V & 7)) - 1u));
+    if (seen != 0u) acc.flags |= OnlineLse::kSeen;
+    if (!(acc.s == acc.s) || acc.m == __builtin_inff()) acc.flags |= OnlineLse::kBad;
+    if (tid == 0 && ((brow[tok >> 3] >> (tok & 7)) & 1u)) acc.flags |= OnlineLse::kFound;
   }
   lse_block(acc, c, sh);
   const float M = acc.m;
