@@ -46,14 +46,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch_alg: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_b256_v151936_bf16.json")
+def traffic_path(wl) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_b{wl.B}_v{wl.V}_{wl.dtype}.json")
+
+
+def measured_traffic(wl):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload, if it
+    was taken on the current kernel sources; else None."""
+    path = traffic_path(wl)
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != wl.name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -432,8 +436,11 @@ def main() -> int:
         with open(args.ingest_pmc[2]) as f:  # the last JSON line (a profiler may print after it)
             bench_line = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
         alg = int(bench_line["algorithmic_bytes_per_launch"])
-        t = ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], alg, in_bytes)
-        path = os.path.join(ROOT, "profiles", f"traffic_b{wl.B}_v{wl.V}_{wl.dtype}.json")
+        if bench_line["config"].get("workload") != wl.name:
+            raise SystemExit(f"the bench line is of {bench_line['config'].get('workload')}, "
+                             f"not of {wl.name}")
+        t = {"workload": wl.name, **ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], alg, in_bytes)}
+        path = traffic_path(wl)
         with open(path, "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t))
@@ -512,7 +519,7 @@ def main() -> int:
     alg_bytes = in_bytes + int(np.minimum(lengths, wl.W).sum()) * 8 + wl.R * 8 + wl.B * 5
     avg_s = avg_ms * 1e-3
     achieved = alg_bytes / avg_s / 1e9
-    traffic = measured_traffic(alg_bytes)
+    traffic = measured_traffic(wl)
     rows_per_s = wl.B * args.steps / wall
     line = {
         "metric": METRIC,
