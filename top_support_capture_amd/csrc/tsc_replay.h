@@ -138,6 +138,29 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   const uint32_t tid = threadIdx.x;
   const auto* row = reinterpret_cast<const typename E::Bits*>(a.logits) + j * a.ld;
   const int64_t V = a.V;
+  constexpr bool kHalf = sizeof(typename E::Bits) == 2;
+  constexpr int kS = kHalf ? 16 : 8;  // chunks of 8 ids per group of the bitmask pass
+  const uint32_t nfull = (uint32_t)(V / 8);  // chunks wholly inside the row
+
+  // Loads whose addresses do not depend on the row's scalars go out with them, so that their
+  // latencies overlap: the thread's first packed id and, when rows may come from bitmasks read
+  // in groups of kS mask bytes, the thread's first group.
+  const int32_t* ids = a.packed_ids + j * a.W;
+  const int32_t id_pre = (int32_t)tid < a.W ? ids[tid] : 0;
+  const uint8_t* bits_row = a.bits ? a.bits + j * a.bits_ld : nullptr;
+  const bool wide = bits_row != nullptr && a.capture_status != nullptr &&
+                    (reinterpret_cast<uintptr_t>(row) & 15u) == 0 &&
+                    (reinterpret_cast<uintptr_t>(bits_row) & 15u) == 0 && (a.bits_ld & 15) == 0;
+  uint32_t bw_pre[kS / 4] = {};
+  if (wide && tid * kS < nfull) {  // tid < the number of groups: inside the mask row
+    if constexpr (kS == 16) {
+      const uint4 mb = *reinterpret_cast<const uint4*>(bits_row + (size_t)tid * kS);
+      bw_pre[0] = mb.x, bw_pre[1] = mb.y, bw_pre[2] = mb.z, bw_pre[3] = mb.w;
+    } else {
+      const uint2 mb = *reinterpret_cast<const uint2*>(bits_row + (size_t)tid * kS);
+      bw_pre[0] = mb.x, bw_pre[1] = mb.y;
+    }
+  }
 
   const int32_t cs = a.capture_status ? (int32_t)a.capture_status[j] : TSC_ROW_OK;
   if (cs >= TSC_ROW_NO_SUPPORT) {  // nothing was captured for this row
@@ -165,11 +188,10 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   const float xt = tid == 0 ? E::to_float((uint32_t)row[tok]) : 0.0f;
   const float c = 1.4426950408889634f / T;
   OnlineLse acc;
-  const int32_t* ids = a.packed_ids + j * a.W;
-  const uint8_t* brow = from_bits ? a.bits + j * a.bits_ld : nullptr;
+  const uint8_t* brow = from_bits ? bits_row : nullptr;  // null: a packed row
   if (!from_bits) {
     for (int32_t i = (int32_t)tid; i < n; i += kThreads) {
-      const int32_t id = ids[i];
+      const int32_t id = i == (int32_t)tid ? id_pre : ids[i];
       if (id < 0 || id >= V) {
         acc.flags |= OnlineLse::kBadId;
         continue;
@@ -186,9 +208,7 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
     // otherwise it takes chunk c0 + s * kThreads at step s, so that neighbouring lanes read
     // neighbouring mask bytes. Rows that are not aligned, and a last, partial chunk, take
     // element loads.
-    constexpr bool kHalf = sizeof(typename E::Bits) == 2;
-    constexpr int kS = kHalf ? 16 : 8, kV = kHalf ? 1 : 2;  // kS loads of 16 * kV bytes in flight
-    const uint32_t nfull = (uint32_t)(V / 8);  // chunks wholly inside the row
+    constexpr int kV = kHalf ? 1 : 2;  // kS loads of 16 * kV bytes in flight
     uint32_t seen = 0;
     auto update = [&](uint32_t byte, const uint32_t (&fb)[8]) {  // fb: float32 bit patterns
       float xm[8];
@@ -212,16 +232,19 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
     if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
       // One pass for each layout, compiled apart, so that each keeps its own simple addressing.
       auto pass = [&](auto layout) {
-      constexpr bool wide = decltype(layout)::value;
+      constexpr bool kWide = decltype(layout)::value;
       auto chunk_of = [&](uint32_t g, int s) -> uint32_t {
-        return wide ? g * kS + (uint32_t)s : g + (uint32_t)s * kThreads;
+        return kWide ? g * kS + (uint32_t)s : g + (uint32_t)s * kThreads;
       };
-      const uint32_t ngroups = wide ? (nfull + kS - 1) / kS : nfull;
-      const uint32_t gstep = wide ? kThreads : kThreads * kS;
+      const uint32_t ngroups = kWide ? (nfull + kS - 1) / kS : nfull;
+      const uint32_t gstep = kWide ? kThreads : kThreads * kS;
       for (uint32_t g = tid; g < ngroups; g += gstep) {
         uint32_t bw[kS / 4];  // the kS mask bytes, four to a word
-        if constexpr (wide) {  // bits_ld is a multiple of 16: the whole group lies inside the mask row
-          if constexpr (kS == 16) {
+        if constexpr (kWide) {  // bits_ld is a multiple of 16: the whole group lies inside the mask row
+          if (g == tid) {
+#pragma unroll
+            for (int q = 0; q < kS / 4; ++q) bw[q] = bw_pre[q];
+          } else if constexpr (kS == 16) {
             const uint4 mb = *reinterpret_cast<const uint4*>(brow + (size_t)g * kS);
             bw[0] = mb.x, bw[1] = mb.y, bw[2] = mb.z, bw[3] = mb.w;
           } else {
@@ -273,7 +296,7 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
         }
       }
       };
-      if ((reinterpret_cast<uintptr_t>(brow) & 15u) == 0 && (a.bits_ld & 15) == 0)
+      if (wide)
         pass(BoolTag<true>{});
       else
         pass(BoolTag<false>{});
