@@ -190,14 +190,30 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   OnlineLse acc;
   const uint8_t* brow = from_bits ? bits_row : nullptr;  // null: a packed row
   if (!from_bits) {
-    for (int32_t i = (int32_t)tid; i < n; i += kThreads) {
-      const int32_t id = i == (int32_t)tid ? id_pre : ids[i];
-      if (id < 0 || id >= V) {
-        acc.flags |= OnlineLse::kBadId;
-        continue;
+    // kU entries per thread at a time: their ids, then their logits, load together.
+    constexpr int kU = 4;
+    for (int32_t i0 = (int32_t)tid; i0 < n; i0 += kThreads * kU) {
+      int32_t idv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t i = i0 + u * kThreads;
+        idv[u] = i >= n ? -1 : i == (int32_t)tid ? id_pre : ids[i];
       }
-      if (id == tok) acc.flags |= OnlineLse::kFound;
-      acc.add(E::to_float((uint32_t)row[id]), c);
+      float xv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        xv[u] = idv[u] >= 0 && idv[u] < V ? E::to_float((uint32_t)row[idv[u]]) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (i0 + u * kThreads >= n) continue;
+        const int32_t id = idv[u];
+        if (id < 0 || id >= V) {
+          acc.flags |= OnlineLse::kBadId;
+          continue;
+        }
+        if (id == tok) acc.flags |= OnlineLse::kFound;
+        acc.add(xv[u], c);
+      }
     }
   } else {
     // Chunks of 8 ids, one mask byte each; non-members become -inf, so that every chunk takes
@@ -327,15 +343,37 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
                                         : -__builtin_inff();
     a.selected_logprob[j] = sel;
   }
-  // The logprob of every packed entry (for an overflowing row, of its packed prefix).
+  // The logprob of every packed entry (for an overflowing row, of its packed prefix). A thread
+  // takes kU entries at a time: their ids load together, then their logits (and mask bytes)
+  // together, so that a row of W entries costs a few round trips, not two per entry.
   if (a.logprobs != nullptr && status == TSC_ROW_OK && n_ok) {
+    constexpr int kU = 8;
     float* out = a.logprobs + j * a.W;
-    for (int32_t i = (int32_t)tid; i < n; i += kThreads) {
-      const int32_t id = ids[i];
-      // Masked log-softmax: an id outside the support (possible only in a bitmask row) is -inf.
-      const bool in = id >= 0 && id < V && (brow == nullptr || ((brow[id >> 3] >> (id & 7)) & 1u));
-      const float x = in ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
-      out[i] = (float)(((double)x - (double)M) / (double)T - lnS);
+    for (int32_t i0 = (int32_t)tid; i0 < n; i0 += kThreads * kU) {
+      int32_t idv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t i = i0 + u * kThreads;
+        idv[u] = i >= n ? -1 : i == (int32_t)tid ? id_pre : ids[i];
+      }
+      float xv[kU];
+      uint32_t bv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t id = idv[u];
+        const bool ok = id >= 0 && id < V;
+        xv[u] = ok ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
+        bv[u] = ok ? (brow == nullptr ? 0xFFu : (uint32_t)brow[id >> 3]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t i = i0 + u * kThreads;
+        if (i >= n) continue;
+        // Masked log-softmax: an id outside the support (possible only in a bitmask row) is -inf.
+        const bool in = (bv[u] >> (idv[u] & 7)) & 1u;
+        const float x = in ? xv[u] : -__builtin_inff();
+        out[i] = (float)(((double)x - (double)M) / (double)T - lnS);
+      }
     }
   }
 }
