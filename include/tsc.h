@@ -192,8 +192,8 @@ int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t
  * csr_logprobs [cap] float32 out or NULL, aligned with csr_ids.
  * cap          capacity of the payload buffers in entries: entries at positions >= cap are not
  *              written (offsets[R] is always the full total; R * W never overflows).
- * Two kernels on `stream`, asynchronous, no allocation: the caller reads offsets[R] and copies
- * that many entries. Returns TSC_OK or TSC_ERR_INVALID_ARGUMENT / UNSUPPORTED / HIP.
+ * One kernel (R <= 2048) or two on `stream`, asynchronous, no allocation: the caller reads
+ * offsets[R] and copies that many entries. Returns TSC_OK or TSC_ERR_INVALID_ARGUMENT / UNSUPPORTED / HIP.
  */
 int32_t tsc_support_csr(const int32_t* lengths, const int32_t* packed_ids, const float* logprobs,
                         int64_t R, int32_t W, int64_t* offsets, int32_t* csr_ids,

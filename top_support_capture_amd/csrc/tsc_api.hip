@@ -123,8 +123,13 @@ int32_t tsc_support_csr(const int32_t* lengths, const int32_t* packed_ids, const
                  logprobs ? csr_logprobs : nullptr, cap};
   (void)hipGetLastError();
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(tsc::csr_scan_kernel, dim3(1), dim3(tsc::kThreads), 0, s, a);
-  if (R > 0) hipLaunchKernelGGL(tsc::csr_copy_kernel, dim3((unsigned)R), dim3(256), 0, s, a);
+  if (R >= 1 && R <= tsc::kCsrFusedMaxR) {
+    hipLaunchKernelGGL(tsc::csr_fused_kernel, dim3((unsigned)R), dim3(tsc::kCsrThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(tsc::csr_scan_kernel, dim3(1), dim3(tsc::kThreads), 0, s, a);
+    if (R > 0)
+      hipLaunchKernelGGL(tsc::csr_copy_kernel, dim3((unsigned)R), dim3(tsc::kCsrThreads), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
 

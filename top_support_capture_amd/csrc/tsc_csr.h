@@ -2,9 +2,11 @@
 // so that a copy to the host can be sized by the realized support instead of R * W (sglang PR
 // #40986, "Limitations": the packed buffer crosses whole, sized by its capacity).
 //
-// Two launches on the caller's stream: one workgroup scans the R lengths into offsets[0..R];
-// then one workgroup per slot copies its first lengths[j] ids (and logprobs) to
-// offsets[j] .. offsets[j + 1], with coalesced loads and stores.
+// Up to kCsrFusedMaxR slots, one launch: workgroup j sums the clamped lengths of the slots before
+// it itself (at most kCsrFusedMaxR reads, served by L2 after the first workgroups), writes
+// offsets[j + 1], and copies its first lengths[j] ids (and logprobs) to offsets[j] ..
+// offsets[j + 1] with coalesced loads and stores. More slots take two launches: one workgroup
+// scans the R lengths into offsets[0..R], then the same copy per slot.
 #pragma once
 
 #include "tsc_device.h"
@@ -51,18 +53,46 @@ __global__ void __launch_bounds__(kThreads) csr_scan_kernel(CsrArgs a) {
   }
 }
 
-// Workgroup j copies slot j's prefix; entries at or past cap are not written.
-__global__ void __launch_bounds__(256) csr_copy_kernel(CsrArgs a) {
-  const int64_t j = blockIdx.x;
-  const int64_t n = csr_len(a.lengths[j], a.W);
-  const int64_t at = a.offsets[j];
+constexpr int kCsrThreads = 256;
+constexpr int64_t kCsrFusedMaxR = 2048;
+
+// Slot j's prefix to offset `at`; entries at or past cap are not written.
+__device__ inline void csr_copy_slot(const CsrArgs& a, int64_t j, int64_t n, int64_t at) {
   const int32_t* src = a.packed_ids + j * a.W;
   const float* srcl = a.logprobs ? a.logprobs + j * a.W : nullptr;
-  for (int64_t i = threadIdx.x; i < n; i += 256) {
+  for (int64_t i = threadIdx.x; i < n; i += kCsrThreads) {
     if (at + i >= a.cap) break;
     a.ids[at + i] = src[i];
     if (srcl && a.lps) a.lps[at + i] = srcl[i];
   }
+}
+
+// Workgroup j copies slot j's prefix to the offset the scan wrote.
+__global__ void __launch_bounds__(kCsrThreads) csr_copy_kernel(CsrArgs a) {
+  const int64_t j = blockIdx.x;
+  csr_copy_slot(a, j, csr_len(a.lengths[j], a.W), a.offsets[j]);
+}
+
+// Workgroup j (R <= kCsrFusedMaxR): its offset from the lengths before it, then its copy.
+__global__ void __launch_bounds__(kCsrThreads) csr_fused_kernel(CsrArgs a) {
+  constexpr int kW = kCsrThreads / kWaveSize;
+  __shared__ int64_t part[kW];
+  const int64_t j = blockIdx.x;
+  const uint32_t tid = threadIdx.x;
+  int64_t s = 0;
+  for (int64_t i = tid; i < j; i += kCsrThreads) s += csr_len(a.lengths[i], a.W);
+  s = wave_reduce(s, SumOp());
+  if ((tid & (kWaveSize - 1)) == 0) part[tid / kWaveSize] = s;
+  lds_barrier();
+  int64_t at = 0;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) at += part[i];
+  const int64_t n = csr_len(a.lengths[j], a.W);
+  if (tid == 0) {
+    if (j == 0) a.offsets[0] = 0;
+    a.offsets[j + 1] = at + n;
+  }
+  csr_copy_slot(a, j, n, at);
 }
 
 }  // namespace tsc
