@@ -482,22 +482,58 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 }
 
 
-// Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
-// go through the general path instead; `slot` is then already set.
-// Sets the bitmask bit of every survivor (value >= x_cut) of one wave's candidate list.
+// Sets the bitmask bit of every survivor (value >= x_cut) of one wave's candidate list, whose
+// ids ascend, in a mask row zeroed beforehand. Sparse lists (stash mode): one atomic OR per
+// survivor. Dense lists (compaction mode, k > 4096): 64 candidates at a time, the lanes whose
+// ids share a 32-bit word form a run; doubling steps over the later lanes of the same word
+// gather the run's bits into its first lane, which writes the word once. Words strictly inside
+// the group's id range belong to this group alone and take a plain store; its first and last
+// words, which the neighbouring groups or the neighbouring waves' lists may share, take an
+// atomic OR. On the k = 8192 workload this took the capture with bitmasks from 87 to 61 us;
+// on sparse lists the atomics per survivor were 0.4 us faster.
+template <bool DENSE>
 __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, float x_cut,
                                             uint32_t id0, uint32_t* brow) {
-  for (uint32_t i = lane_id(); i < n; i += kWaveSize) {
-    const uint32_t wd = cand[i];
-    if (!(__uint_as_float(wd & 0xFFFF0000u) >= x_cut)) continue;
+  const uint32_t lane = lane_id();
+  if constexpr (!DENSE) {
+    for (uint32_t i = lane; i < n; i += kWaveSize) {
+      const uint32_t wd = cand[i];
+      if (!(__uint_as_float(wd & 0xFFFF0000u) >= x_cut)) continue;
+      const uint32_t id = id0 + (wd & 0x3FFFu);
+      atomicOr(brow + (id >> 5), 1u << (id & 31u));
+    }
+    return;
+  }
+  for (uint32_t base = 0; base < n; base += kWaveSize) {  // uniform: every lane takes part
+    const uint32_t i = base + lane;
+    const bool valid = i < n;
+    const uint32_t wd = valid ? cand[i] : 0u;
     const uint32_t id = id0 + (wd & 0x3FFFu);
-    atomicOr(brow + (id >> 5), 1u << (id & 31u));
+    const uint32_t widx = valid ? id >> 5 : 0xFFFFFFFFu;
+    uint32_t bits = valid && __uint_as_float(wd & 0xFFFF0000u) >= x_cut ? 1u << (id & 31u) : 0u;
+#pragma unroll
+    for (int d = 1; d < kWaveSize; d <<= 1) {
+      const uint32_t ow = __shfl_down(widx, d, kWaveSize);
+      const uint32_t ob = __shfl_down(bits, d, kWaveSize);
+      if (lane + (uint32_t)d < (uint32_t)kWaveSize && ow == widx) bits |= ob;
+    }
+    const uint32_t prev = __shfl_up(widx, 1, kWaveSize);
+    const uint32_t last = (n - base < (uint32_t)kWaveSize ? n - base : (uint32_t)kWaveSize) - 1u;
+    const uint32_t first_w = read_lane(widx, 0), last_w = read_lane(widx, (int)last);
+    if (valid && (lane == 0 || prev != widx) && bits != 0u) {
+      if (widx == first_w || widx == last_w)
+        atomicOr(brow + widx, bits);
+      else
+        brow[widx] = bits;
+    }
   }
 }
 
 template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
 template <> struct LayoutOf<true> { using type = LayoutCompact; };
 
+// Fast path of one bfloat16 row. Returns false (having written no row output) when the row must
+// go through the general path instead; `slot` is then already set.
 template <bool NEED_P, bool COMPACT, int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
                                               float T, int32_t k, float p, float mp,
@@ -1085,12 +1121,15 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         if (BITS && capture && fs.L > (uint32_t)a.W) {
           // A support wider than W is also written as a bitmask: cleared here, and its bits set
-          // by the capture with atomic ORs. The device-scope release waits until the clearing
-          // stores have reached L2, before any wave can see scan_ready and start its ORs.
+          // by the capture. Waiting for every memory counter to drain means the clearing stores
+          // have reached this CU's L2, where the capture's ORs and stores land, before any wave
+          // can see scan_ready. (A device-scope release here wrote back the whole L2: 3 us more
+          // on the B=256, V=151936 rows captured at W=512.)
           uint4* z = reinterpret_cast<uint4*>(a.bits + slot * a.bits_ld);
           const uint32_t n16 = (uint32_t)(bitmask_words(a.V) / 4);
           for (uint32_t i = lane; i < n16; i += kWaveSize) z[i] = make_uint4(0u, 0u, 0u, 0u);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __builtin_amdgcn_s_waitcnt(0);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         }
       }
     }
@@ -1280,7 +1319,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           }
         }
       }
-      if (BITS && brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
+      if (BITS && brow != nullptr) support_bits_of_list<true>(cand_c, ncj, x_cut, id0c, brow);
       lds_publish_step(&fs.staged);
     }
     // Copy-out of the stage, in slices of 1024 positions.
@@ -1336,7 +1375,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
         }
       }
-      if (BITS && brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
+      if (BITS && brow != nullptr) support_bits_of_list<false>(cand_c, ncj, x_cut, id0c, brow);
     }
   }
   }
