@@ -136,6 +136,7 @@ struct FastShared {
   uint32_t cap_next;            // next wave's candidate list to capture
   uint32_t staged;              // candidate lists captured into the stage
   uint32_t copy_next;           // next slice of the stage to copy out
+  uint32_t bits_next;           // next wave's candidate list to set bitmask bits from
   uint32_t bin_hi[kWaves];      // one past the largest bin of the wave's candidates
   uint32_t noise_done[kWaves];  // candidates whose race draws the wave made itself (from the first)
   int32_t slot_wmax[kWaves];
@@ -484,13 +485,13 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 
 // Sets the bitmask bit of every survivor (value >= x_cut) of one wave's candidate list, whose
 // ids ascend, in a mask row zeroed beforehand. Sparse lists (stash mode): one atomic OR per
-// survivor. Dense lists (compaction mode, k > 4096): 64 candidates at a time, the lanes whose
-// ids share a 32-bit word form a run; doubling steps over the later lanes of the same word
-// gather the run's bits into its first lane, which writes the word once. Words strictly inside
-// the group's id range belong to this group alone and take a plain store; its first and last
-// words, which the neighbouring groups or the neighbouring waves' lists may share, take an
-// atomic OR. On the k = 8192 workload this took the capture with bitmasks from 87 to 61 us;
-// on sparse lists the atomics per survivor were 0.4 us faster.
+// survivor. Dense lists (compaction mode, k > 4096), 64 candidates at a time: the lanes whose ids
+// share a 32-bit word form a run, a segmented OR over the runs (DPP steps) gathers each run's
+// bits into its last lane, and every word is written once. The group's last run is carried into
+// the next group, so that a word the two share is still written once. A plain store suffices
+// for every word but the list's first and last, which the neighbouring waves' lists may share
+// and which take an atomic OR. (An atomic OR per survivor took the k = 8192 workload with
+// bitmasks to 87 us; atomics at the ends of every 64-candidate group, to 57 us.)
 template <bool DENSE>
 __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, float x_cut,
                                             uint32_t id0, uint32_t* brow) {
@@ -504,29 +505,51 @@ __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, fl
     }
     return;
   }
+  if (n == 0u) return;
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  const uint32_t list_first = (id0 + (cand[0] & 0x3FFFu)) >> 5;
+  const uint32_t list_last = (id0 + (cand[n - 1u] & 0x3FFFu)) >> 5;
+  auto put = [&](uint32_t w, uint32_t b) {
+    if (b == 0u) return;
+    if (w == list_first || w == list_last)
+      atomicOr(brow + w, b);
+    else
+      brow[w] = b;
+  };
+  uint32_t carry_w = kNone, carry_b = 0u;  // the previous group's last run, not yet written
   for (uint32_t base = 0; base < n; base += kWaveSize) {  // uniform: every lane takes part
     const uint32_t i = base + lane;
     const bool valid = i < n;
     const uint32_t wd = valid ? cand[i] : 0u;
     const uint32_t id = id0 + (wd & 0x3FFFu);
-    const uint32_t widx = valid ? id >> 5 : 0xFFFFFFFFu;
+    const uint32_t widx = valid ? id >> 5 : kNone;
     uint32_t bits = valid && __uint_as_float(wd & 0xFFFF0000u) >= x_cut ? 1u << (id & 31u) : 0u;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-      const uint32_t ow = __shfl_down(widx, d, kWaveSize);
-      const uint32_t ob = __shfl_down(bits, d, kWaveSize);
-      if (lane + (uint32_t)d < (uint32_t)kWaveSize && ow == widx) bits |= ob;
-    }
-    const uint32_t prev = __shfl_up(widx, 1, kWaveSize);
+    // Segmented inclusive OR (the steps of the wave scan; a source lane of the same word lies in
+    // the same run): each run's last lane ends up with the run's bits.
+    auto step = [&](auto mv) {
+      const uint32_t ow = mv(kNone, widx), ob = mv(0u, bits);
+      if (ow == widx) bits |= ob;
+    };
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowShr1>(o, v); });
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowShr2>(o, v); });
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowShr4>(o, v); });
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowShr8>(o, v); });
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowBcast15, 0xA>(o, v); });
+    step([](uint32_t o, uint32_t v) { return dpp_mov<dpp::kRowBcast31, 0xC>(o, v); });
+    const uint32_t next = __shfl_down(widx, 1, kWaveSize);
     const uint32_t last = (n - base < (uint32_t)kWaveSize ? n - base : (uint32_t)kWaveSize) - 1u;
-    const uint32_t first_w = read_lane(widx, 0), last_w = read_lane(widx, (int)last);
-    if (valid && (lane == 0 || prev != widx) && bits != 0u) {
-      if (widx == first_w || widx == last_w)
-        atomicOr(brow + widx, bits);
-      else
-        brow[widx] = bits;
+    const bool tail = valid && (lane == last || next != widx);
+    const uint32_t g_first = read_lane(widx, 0), g_last = read_lane(widx, (int)last);
+    if (carry_w == g_first) {
+      if (tail && widx == g_first) bits |= carry_b;  // the carried run continues here
+    } else if (carry_w != kNone && lane == 0) {
+      put(carry_w, carry_b);
     }
+    carry_w = g_last;
+    carry_b = read_lane(bits, (int)last);
+    if (tail && widx != g_last) put(widx, bits);
   }
+  if (lane == 0) put(carry_w, carry_b);
 }
 
 template <bool COMPACT> struct LayoutOf { using type = LayoutStash; };
@@ -610,6 +633,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     fs.cap_next = 0u;
     fs.staged = 0u;
     fs.copy_next = 0u;
+    fs.bits_next = 0u;
   }
   reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest)[tid] = 0ull;
 
@@ -1319,7 +1343,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           }
         }
       }
-      if (BITS && brow != nullptr) support_bits_of_list<true>(cand_c, ncj, x_cut, id0c, brow);
       lds_publish_step(&fs.staged);
     }
     // Copy-out of the stage, in slices of 1024 positions.
@@ -1336,6 +1359,18 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           out_ids[j] = (int32_t)(e & 0x3FFFFu);
           if (out_lp) out_lp[j] = (float)(bins[e >> 18] - lnzs);
         }
+      }
+    }
+    // Bitmask bits, one candidate list per claim, by the waves with no stage slice left: off
+    // the path from the ranking to the copy-out.
+    if (BITS && brow != nullptr) {
+      for (;;) {
+        const uint32_t cj = lds_claim(&fs.bits_next);
+        if (cj >= (uint32_t)kWaves) break;
+        const uint32_t ncj0 = fs.wave_cand[cj];
+        const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
+        support_bits_of_list<true>(reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap,
+                                   ncj, x_cut, cj * cw * 8u, brow);
       }
     }
   }
