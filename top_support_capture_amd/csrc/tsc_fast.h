@@ -484,27 +484,17 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 
 
 // Sets the bitmask bit of every survivor (value >= x_cut) of one wave's candidate list, whose
-// ids ascend, in a mask row zeroed beforehand. Sparse lists (stash mode): one atomic OR per
-// survivor. Dense lists (compaction mode, k > 4096), 64 candidates at a time: the lanes whose ids
-// share a 32-bit word form a run, a segmented OR over the runs (DPP steps) gathers each run's
-// bits into its last lane, and every word is written once. The group's last run is carried into
-// the next group, so that a word the two share is still written once. A plain store suffices
-// for every word but the list's first and last, which the neighbouring waves' lists may share
-// and which take an atomic OR. (An atomic OR per survivor took the k = 8192 workload with
-// bitmasks to 87 us; atomics at the ends of every 64-candidate group, to 57 us.)
-template <bool DENSE>
+// ids ascend, in a mask row zeroed beforehand. 64 candidates at a time: the lanes whose ids share
+// a 32-bit word form a run, a segmented OR over the runs (DPP steps) gathers each run's bits into
+// its last lane, and every word is written once. The group's last run is carried into the next
+// group, so that a word the two share is still written once. A plain store suffices for every
+// word but the list's first and last, which the neighbouring waves' lists may share and which
+// take an atomic OR. Atomic ORs on words that plain stores also wrote were slow: one atomic per
+// survivor took the k = 8192 workload with bitmasks to 87 us (47 now), and c3's rows captured at
+// W = 512 to 27.7 us (25.6 now).
 __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, float x_cut,
                                             uint32_t id0, uint32_t* brow) {
   const uint32_t lane = lane_id();
-  if constexpr (!DENSE) {
-    for (uint32_t i = lane; i < n; i += kWaveSize) {
-      const uint32_t wd = cand[i];
-      if (!(__uint_as_float(wd & 0xFFFF0000u) >= x_cut)) continue;
-      const uint32_t id = id0 + (wd & 0x3FFFu);
-      atomicOr(brow + (id >> 5), 1u << (id & 31u));
-    }
-    return;
-  }
   if (n == 0u) return;
   constexpr uint32_t kNone = 0xFFFFFFFFu;
   const uint32_t list_first = (id0 + (cand[0] & 0x3FFFu)) >> 5;
@@ -1369,7 +1359,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         if (cj >= (uint32_t)kWaves) break;
         const uint32_t ncj0 = fs.wave_cand[cj];
         const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
-        support_bits_of_list<true>(reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap,
+        support_bits_of_list(reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap,
                                    ncj, x_cut, cj * cw * 8u, brow);
       }
     }
@@ -1410,7 +1400,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
         }
       }
-      if (BITS && brow != nullptr) support_bits_of_list<false>(cand_c, ncj, x_cut, id0c, brow);
+      if (BITS && brow != nullptr) support_bits_of_list(cand_c, ncj, x_cut, id0c, brow);
     }
   }
   }
