@@ -57,3 +57,25 @@ def test_ingest_pmc_scales_by_the_copy_kernel(tmp_path):
 def test_kernel_source_hash_is_stable():
     h = bench.kernel_source_hash()
     assert len(h) == 16 and h == bench.kernel_source_hash()
+
+
+def test_traffic_summary_is_keyed_by_workload_and_sources(tmp_path, monkeypatch):
+    # A counter summary counts only for the workload it was taken on, and only while the kernel
+    # sources hash to what it records.
+    import json
+    import types
+    h = bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    wl = types.SimpleNamespace(B=256, V=151936, dtype="bf16", name="b256_v151936_bf16_grid")
+    other = types.SimpleNamespace(B=256, V=151936, dtype="bf16", name="another")
+    assert bench.measured_traffic(wl) is None  # no summary
+    with open(bench.traffic_path(wl), "w") as f:
+        json.dump({"workload": wl.name, "kernel_source_hash": h, "hbm_bytes_per_launch": 123.0}, f)
+    assert bench.measured_traffic(wl) == 123.0
+    assert bench.measured_traffic(other) is None
+    with open(bench.traffic_path(wl), "w") as f:
+        json.dump({"workload": wl.name, "kernel_source_hash": "0" * 16,
+                   "hbm_bytes_per_launch": 123.0}, f)
+    assert bench.measured_traffic(wl) is None
