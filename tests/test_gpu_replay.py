@@ -226,11 +226,17 @@ def test_replay_bitmask_strides(dtype, V, extra, pad):
             bits[j, nb - 1] |= np.uint8((0xFF << (V % 8)) & 0xFF)  # bits past V
         members = np.nonzero(keep)[0]
         tokens[j] = members[rng.integers(members.size)] if j % 3 else V - 1 - (j % 5)
-    ids = np.zeros((N, 4), np.int32)
-    lengths = np.ones(N, np.int32)
     T = rng.uniform(0.5, 1.5, N).astype(np.float32)
     cs = np.ones(N, np.int8)
     member = lambda j: np.nonzero(np.unpackbits(bits[j, :nb], bitorder="little")[:V])[0]
+    # Packed ids whose logprobs are asked for: the first and last members, an id outside the
+    # support (when there is one), and the last id of the row (in a ragged last chunk if V % 8).
+    ids = np.zeros((N, 4), np.int32)
+    for j in range(N):
+        mj = member(j)
+        outside = np.setdiff1d(np.arange(V), mj)
+        ids[j] = [mj[0], mj[-1], outside[0] if outside.size else mj[0], V - 1]
+    lengths = np.full(N, 4, np.int32)
     x[2, member(2)[-1]] = np.nan                       # a NaN member: NONFINITE
     x[4, member(4)[0]] = np.inf                        # a +inf member: NONFINITE
     x[6, member(6)] = -np.inf                          # every member -inf: NO_SUPPORT
@@ -245,7 +251,7 @@ def test_replay_bitmask_strides(dtype, V, extra, pad):
     else:
         xx = x
     log(f"case replay bitmask strides {dtype} V={V} bits ld={ld} pad={pad}")
-    got = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits, return_logprobs=False, pad=pad)
+    got = run_replay(xx, dtype, T, ids, lengths, tokens, cs, bits, pad=pad)
     ref = oracle.replay(xx, dtype, T, ids, lengths, tokens, cs, bits)
     errs, n, _ = compare_replay(got, ref, lengths)
     assert errs == [] and n == int(np.sum(ref[2] == 0)) == N - 3, errs

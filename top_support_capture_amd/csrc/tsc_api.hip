@@ -155,10 +155,14 @@ int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t
                     support_bits, bits_ld, tokens, selected_logprob, logprobs, row_status};
   (void)hipGetLastError();
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Support logprobs of bitmask rows read their logits from an LDS stage (bfloat16).
+  const bool stage = logprobs != nullptr && support_bits != nullptr && capture_status != nullptr;
   if (dtype == TSC_DTYPE_F32)
-    hipLaunchKernelGGL(tsc::replay_kernel<TSC_DTYPE_F32>, dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
+    hipLaunchKernelGGL((tsc::replay_kernel<TSC_DTYPE_F32, false>), dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
+  else if (stage)
+    hipLaunchKernelGGL((tsc::replay_kernel<TSC_DTYPE_BF16, true>), dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(tsc::replay_kernel<TSC_DTYPE_BF16>, dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
+    hipLaunchKernelGGL((tsc::replay_kernel<TSC_DTYPE_BF16, false>), dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
 

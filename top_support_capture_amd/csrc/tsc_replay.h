@@ -39,6 +39,17 @@ struct ReplayShared {
   float m[kWaves];
   float s[kWaves];
   uint32_t f[kWaves];
+  uint32_t scan[kWaves];  // member chunks per wave (staging)
+};
+
+// Staging of a bitmask row's member chunks in LDS for the support-logprob pass (bfloat16 rows of
+// at most kStageChunks chunks, with at most kStageSlots member chunks): the pass then reads
+// each packed id's logit from LDS instead of gathering it from memory again.
+constexpr int kStageChunks = 16384;  // V <= 131072
+constexpr int kStageSlots = 7168;    // 112 KB of 16-byte chunks
+struct ReplayStage {
+  uint16_t slot_of[kStageChunks];  // chunk -> its slot, for member chunks only
+  uint4 chunk[kStageSlots];
 };
 
 // Online log-sum-exp state of one thread: m the largest finite logit seen, s = sum of
@@ -130,10 +141,16 @@ __device__ inline void lse_block(OnlineLse& st, float c, ReplayShared& sh) {
   st.m = m, st.s = s, st.flags = f;
 }
 
-template <int DT>
+template <int DT, bool STAGE>
 __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   using E = Elem<DT>;
+  static_assert(!STAGE || DT == TSC_DTYPE_BF16, "staging holds bfloat16 chunks");
   __shared__ ReplayShared sh;
+  [[maybe_unused]] ReplayStage* stg = nullptr;
+  if constexpr (STAGE) {
+    __shared__ ReplayStage stage_lds;
+    stg = &stage_lds;
+  }
   const int64_t j = blockIdx.x;
   const uint32_t tid = threadIdx.x;
   const auto* row = reinterpret_cast<const typename E::Bits*>(a.logits) + j * a.ld;
@@ -189,6 +206,33 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   const float c = 1.4426950408889634f / T;
   OnlineLse acc;
   const uint8_t* brow = from_bits ? bits_row : nullptr;  // null: a packed row
+  // Staging: the member chunks of the thread's first group take consecutive slots, from a
+  // block-wide exclusive scan of their counts (rows of one group per thread only).
+  [[maybe_unused]] bool staged_row = false;
+  [[maybe_unused]] uint32_t slot_next = 0;
+  if constexpr (STAGE) {
+    if (from_bits && wide && nfull <= (uint32_t)kStageChunks) {  // uniform over the block
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int q = 0; q < kS; ++q) {
+        const uint32_t byte = (bw_pre[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+        cnt += (tid * kS + (uint32_t)q < nfull && byte != 0u) ? 1u : 0u;
+      }
+      const uint32_t incl = wave_incl_scan(cnt, SumOp(), 0u);
+      const uint32_t w = tid / kWaveSize;
+      if ((tid & (kWaveSize - 1)) == kWaveSize - 1) sh.scan[w] = incl;
+      lds_barrier();
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const uint32_t t = sh.scan[i];
+        before += i < (int)w ? t : 0u;
+        total += t;
+      }
+      slot_next = before + incl - cnt;
+      staged_row = total <= (uint32_t)kStageSlots;
+    }
+  }
   if (!from_bits) {
     // kU entries per thread at a time: their ids, then their logits, load together.
     constexpr int kU = 4;
@@ -293,6 +337,19 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
                 raw[u][h] = *reinterpret_cast<const uint4*>(row + (size_t)ch * 8 + 4 * h);
             }
           }
+          if constexpr (STAGE && kWide) {
+            if (staged_row) {  // one group per thread: this is the thread's first
+#pragma unroll
+              for (int u = 0; u < kS; ++u) {
+                if (byte_of(u) != 0u) {
+                  const uint32_t ch = chunk_of(g, u);
+                  stg->chunk[slot_next] = raw[u][0];
+                  stg->slot_of[ch] = (uint16_t)slot_next;
+                  ++slot_next;
+                }
+              }
+            }
+          }
 #pragma unroll
           for (int u = 0; u < kS; ++u) {
             uint32_t fb[8];
@@ -358,12 +415,35 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
       }
       float xv[kU];
       uint32_t bv[kU];
+      if (STAGE && staged_row) {  // members of full chunks: their logits from the LDS stage
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int32_t id = idv[u];
-        const bool ok = id >= 0 && id < V;
-        xv[u] = ok ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
-        bv[u] = ok ? (brow == nullptr ? 0xFFu : (uint32_t)brow[id >> 3]) : 0u;
+        for (int u = 0; u < kU; ++u) {
+          const int32_t id = idv[u];
+          bv[u] = id >= 0 && id < V ? (uint32_t)brow[id >> 3] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int32_t id = idv[u];
+          const uint32_t ch = (uint32_t)id >> 3;
+          float x = -__builtin_inff();
+          if ((bv[u] >> (id & 7)) & 1u) {
+            if (ch < nfull) {
+              const uint16_t* st16 = reinterpret_cast<const uint16_t*>(stg->chunk);
+              x = E::to_float((uint32_t)st16[(uint32_t)stg->slot_of[ch] * 8u + (uint32_t)(id & 7)]);
+            } else {
+              x = E::to_float((uint32_t)row[id]);  // the ragged last chunk is not staged
+            }
+          }
+          xv[u] = x;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int32_t id = idv[u];
+          const bool ok = id >= 0 && id < V;
+          xv[u] = ok ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
+          bv[u] = ok ? (brow == nullptr ? 0xFFu : (uint32_t)brow[id >> 3]) : 0u;
+        }
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
