@@ -56,14 +56,32 @@ __global__ void __launch_bounds__(kThreads) csr_scan_kernel(CsrArgs a) {
 constexpr int kCsrThreads = 256;
 constexpr int64_t kCsrFusedMaxR = 2048;
 
-// Slot j's prefix to offset `at`; entries at or past cap are not written.
+// Slot j's prefix to offset `at`; entries at or past cap are not written. A thread moves kU
+// entries per step, all their loads before any store, so that a long prefix costs a few round
+// trips rather than one per entry.
 __device__ inline void csr_copy_slot(const CsrArgs& a, int64_t j, int64_t n, int64_t at) {
+  constexpr int kU = 8;
   const int32_t* src = a.packed_ids + j * a.W;
-  const float* srcl = a.logprobs ? a.logprobs + j * a.W : nullptr;
-  for (int64_t i = threadIdx.x; i < n; i += kCsrThreads) {
-    if (at + i >= a.cap) break;
-    a.ids[at + i] = src[i];
-    if (srcl && a.lps) a.lps[at + i] = srcl[i];
+  const float* srcl = a.logprobs && a.lps ? a.logprobs + j * a.W : nullptr;
+  const int64_t room = a.cap - at;
+  const int64_t lim = n < room ? n : (room > 0 ? room : 0);
+  for (int64_t i0 = threadIdx.x; i0 < lim; i0 += (int64_t)kCsrThreads * kU) {
+    int32_t v[kU];
+    float l[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + (int64_t)u * kCsrThreads;
+      v[u] = i < lim ? src[i] : 0;
+      l[u] = srcl && i < lim ? srcl[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + (int64_t)u * kCsrThreads;
+      if (i < lim) {
+        a.ids[at + i] = v[u];
+        if (srcl) a.lps[at + i] = l[u];
+      }
+    }
   }
 }
 
