@@ -1344,10 +1344,26 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         const uint32_t sl = lds_claim(&fs.copy_next);
         if (sl * 1024u >= nout) break;
         const uint32_t end = (sl + 1u) * 1024u < nout ? (sl + 1u) * 1024u : nout;
-        for (uint32_t j = sl * 1024u + lane; j < end; j += kWaveSize) {
-          const uint32_t e = stage[j];
-          out_ids[j] = (int32_t)(e & 0x3FFFFu);
-          if (out_lp) out_lp[j] = (float)(bins[e >> 18] - lnzs);
+        // Four entries per lane at a time: their stage words, then their bins' logprobs, are
+        // read together.
+        for (uint32_t j0 = sl * 1024u + lane; j0 < end; j0 += 4u * kWaveSize) {
+          uint32_t e[4];
+          double bl[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t j = j0 + (uint32_t)t * kWaveSize;
+            e[t] = j < end ? stage[j] : 0u;
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) bl[t] = out_lp ? bins[e[t] >> 18] : 0.0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t j = j0 + (uint32_t)t * kWaveSize;
+            if (j < end) {
+              out_ids[j] = (int32_t)(e[t] & 0x3FFFFu);
+              if (out_lp) out_lp[j] = (float)(bl[t] - lnzs);
+            }
+          }
         }
       }
     }
