@@ -35,7 +35,8 @@ def run_csr(lengths, packed, lps, cap=None):
     return off.cpu().numpy(), ids.cpu().numpy(), out_lp.cpu().numpy()
 
 
-@pytest.mark.parametrize("R,W", [(0, 4), (1, 1), (7, 5), (256, 2048), (3000, 16), (5000, 3)])
+@pytest.mark.parametrize("R,W", [(0, 4), (1, 1), (7, 5), (256, 2048), (2048, 7), (2049, 7), (3000, 16),
+                                 (5000, 3)])
 def test_csr_synthetic(R, W):
     log(f"case csr synthetic R={R} W={W}")
     rng = np.random.default_rng(R * 31 + W)
