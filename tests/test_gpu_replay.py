@@ -257,3 +257,35 @@ def test_replay_bitmask_strides(dtype, V, extra, pad):
     assert errs == [] and n == int(np.sum(ref[2] == 0)) == N - 3, errs
     assert got[2][2] == 3 and got[2][4] == 3 and got[2][6] == 2 and got[2][3] == 0
     assert np.sum(np.isfinite(got[0])) >= 4
+
+
+@pytest.mark.parametrize("V", [131072, 131080])
+def test_replay_support_logprobs_staging_limits(V):
+    # bfloat16 bitmask rows with support logprobs: at V = 131072 (16384 chunks, the most that are
+    # staged in LDS) a sparse row is staged and a dense one (more member chunks than slots) is
+    # not; at V = 131080 no row is. Both ways must agree with the oracle.
+    rng = np.random.default_rng(V)
+    N, W = 4, 64
+    nb = (V + 7) // 8
+    ld = (nb + 15) // 16 * 16
+    from workloads import f32_to_bf16_bits
+    xx = f32_to_bf16_bits(rng.standard_normal((N, V)).astype(np.float32) * 2.0)
+    bits = np.zeros((N, ld), np.uint8)
+    ids = np.zeros((N, W), np.int32)
+    tokens = np.zeros(N, np.int32)
+    for j, density in enumerate([0.002, 0.6, 0.05, 1.0]):
+        keep = rng.random(V) < density
+        keep[rng.integers(V)] = True
+        bits[j, :nb] = np.packbits(keep, bitorder="little")
+        mj = np.nonzero(keep)[0]
+        ids[j] = rng.choice(mj, W) if mj.size < W else rng.choice(mj, W, replace=False)
+        ids[j, -1] = np.setdiff1d(np.arange(V), mj)[0] if mj.size < V else mj[0]  # outside
+        tokens[j] = mj[rng.integers(mj.size)]
+    lengths = np.full(N, W, np.int32)
+    T = np.array([1.0, 0.7, 1.3, 1.0], np.float32)
+    cs = np.ones(N, np.int8)
+    log(f"case replay staging limits V={V}")
+    got = run_replay(xx, "bf16", T, ids, lengths, tokens, cs, bits)
+    ref = oracle.replay(xx, "bf16", T, ids, lengths, tokens, cs, bits)
+    errs, n, worst = compare_replay(got, ref, lengths)
+    assert errs == [] and n == N, errs
