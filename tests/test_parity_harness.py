@@ -112,3 +112,34 @@ def test_bitmask_harness():
     bad = copy.deepcopy(got)
     bad["support_bits"][3, 5] = 0  # a row without OVERFLOW written
     assert compare_bits(bad, ref, opt)[0]
+
+
+def test_race_report_exempts_only_the_token():
+    got, ref, opt = _tie_batch()
+    ref.rows[2].race_gap = 0.0  # the oracle reports a race near-tie on row 2
+    got["tokens"][2] = (got["tokens"][2] + 1) % 3
+    got["selected_logprob"][2] = got["logprobs"][2, (got["tokens"][2]) % 3]
+    errs, stats = compare(got, ref, opt)
+    assert errs == [] and stats["race_flagged"] == 1
+    got["packed_ids"][2, [1, 2]] = got["packed_ids"][2, [2, 1]]  # its support is still checked
+    assert compare(got, ref, opt)[0]
+    got, ref, opt = _tie_batch()
+    ref.rows[2].race_gap = 0.0
+    got["logprobs"][2, 0] += 1e-3
+    assert compare(got, ref, opt)[0]
+
+
+def test_top_p_report_exempts_the_support_but_not_an_equal_supports_token():
+    got, ref, opt = _tie_batch()
+    ref.rows[4].top_p_flag = True
+    got["lengths"][4] = 2  # a boundary group decided the other way: exempt
+    errs, stats = compare(got, ref, opt)
+    assert errs == [] and stats["top_p_flagged"] == 1 and stats["support_exempt"] == 1
+    got, ref, opt = _tie_batch()
+    ref.rows[4].top_p_flag = True
+    got["tokens"][4] = [t for t in (0, 1, 2) if t != got["tokens"][4]][0]  # same support
+    assert compare(got, ref, opt)[0]
+    got, ref, opt = _tie_batch()
+    ref.rows[4].min_p_flag = True
+    got["logprobs"][4, 1] += 1e-3  # same support, wrong logprob
+    assert compare(got, ref, opt)[0]
