@@ -228,14 +228,17 @@ def slot_validity(optin_rows: np.ndarray, B: int) -> np.ndarray:
 def sample_with_mask(logits: np.ndarray, dtype: str, temperature, top_k, top_p, min_p,
                      optin_rows, seeds, positions, W: int,
                      rows: Optional[np.ndarray] = None,
-                     bits_ld: Optional[int] = None) -> BatchResult:
+                     bits_ld: Optional[int] = None,
+                     row_results: Optional[dict] = None) -> BatchResult:
     """Oracle of the whole batched call.
 
     ``logits``: float32 [B, V] or uint16 [B, V] of bfloat16 bits. Returns every output of the
     library call plus the per-row diagnostics. With ``rows`` given, only those rows are sampled
     (the others keep token -1 / status -1 and empty captures): used for sampled checks at full
     size. With ``bits_ld`` the support of every OVERFLOW slot is also returned as a bitmask row
-    of that many bytes (R11)."""
+    of that many bytes (R11). ``row_results`` maps row index -> RowResult already computed by
+    ``sample_row`` for that row (e.g. by worker processes); those rows are assembled, not
+    sampled again."""
     B = logits.shape[0]
     R = len(optin_rows)
     tokens = np.full(B, -1, np.int32)
@@ -251,8 +254,11 @@ def sample_with_mask(logits: np.ndarray, dtype: str, temperature, top_k, top_p, 
     todo = range(B) if rows is None else [int(r) for r in rows]
     results: List[Optional[RowResult]] = [None] * B
     for r in todo:
-        res = sample_row(decode_logits(logits[r], dtype), temperature[r], top_k[r], top_p[r],
-                         min_p[r], int(seeds[r]), int(positions[r]))
+        if row_results is not None and r in row_results:
+            res = row_results[r]
+        else:
+            res = sample_row(decode_logits(logits[r], dtype), temperature[r], top_k[r], top_p[r],
+                             min_p[r], int(seeds[r]), int(positions[r]))
         results[r] = res
         tokens[r] = res.token
         st = res.status

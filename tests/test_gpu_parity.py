@@ -330,6 +330,14 @@ FAST_PARAMS = [
     ("compact_pinf", "pinf", 1.0, 2000, 1.0, 0.0),
     ("compact_neg_inf", "neg", 1.0, 3000, 0.9, 0.0),
     ("compact_hidden_top", "hidden", 1.0, 4096, 0.95, 0.0),
+    # A NaN or +inf logit with top_p < 1: the mass overflows or turns NaN; in stash mode
+    # (top_k <= 4096) and in compaction mode (top_k above 4096), with and without min-p.
+    ("pinf_p", "pinf", 1.0, 100, 0.9, 0.0),
+    ("pinf_minp_p", "pinf", 0.8, 300, 0.8, 0.05),
+    ("nan_minp_p", "nan", 1.2, 300, 0.8, 0.05),
+    ("compact8k_nan_p", "nan", 1.0, 6000, 0.9, 0.0),
+    ("compact8k_pinf_p", "pinf", 1.0, 6000, 0.9, 0.0),
+    ("compact8k_pinf_minp", "pinf", 1.0, 8192, 0.95, 0.02),
 ]
 
 

@@ -1,0 +1,107 @@
+"""More parity of the HIP library with the CPU oracle (needs an MI355X): every row of the mixed
+1024-row workload, selected mode (no support logprobs) against the oracle on every path, and
+single-read rows whose top-p boundary lies just outside the report window.
+
+Every case prints its name before touching the GPU, so a fault names the case that caused it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import device_inputs, log, run_gpu
+from tests.invariants import check_invariants
+from tests.oracle_pool import oracle_batch
+from tests.parity import compare
+from tests.test_gpu_parity import make
+from workloads import f32_to_bf16_bits, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, got, ref, W=None, max_flagged_frac=0.05):
+    errs, stats = compare(got, ref, wl.optin_rows)
+    xr = lambda r: oracle.decode_logits(wl.logits[r], wl.dtype)
+    errs += check_invariants(got["tokens"], got["row_status"], got["packed_ids"], got["logprobs"],
+                             got["lengths"], got["selected_logprob"], wl.optin_rows,
+                             wl.W if W is None else W, xr, wl.temperature)
+    log(f"  {wl.name}: {stats}")
+    assert errs == [], errs[:10]
+    assert stats["flagged"] <= max(2, max_flagged_frac * stats["rows"]), stats
+    return stats
+
+
+def test_workload5_every_row():
+    # The mixed 1024-row batch (top_k 1..4096, top_p, min_p, temperature per row, 10% greedy
+    # rows): every row against the oracle, which samples its rows in worker processes.
+    wl = make_workload(5)
+    log(f"case workload 5 {wl.name} B={wl.B} V={wl.V}: every row")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref)
+    assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("index,W", [(2, None), (3, None), (4, 8192), (4, 9216), (5, None)])
+def test_selected_mode_against_oracle(index, W):
+    # logprobs == NULL: packed ids, lengths, tokens and the selected logprob, against the oracle,
+    # on the general path (float32), stash mode, compaction mode (clamped and full width) and
+    # the mixed batch; the support mode of the same inputs must agree with it too.
+    wl = make_workload(index, W=W) if W is not None else make_workload(index)
+    log(f"case selected mode workload {index} W={wl.W}")
+    d = device_inputs(wl)
+    sel = run_gpu(wl, inputs=d, return_logprobs=False)
+    assert sel["logprobs"] is None
+    ref = oracle_batch(wl)
+    _check(wl, sel, ref)
+    sup = run_gpu(wl, inputs=d)
+    for key in ("tokens", "row_status", "lengths"):
+        assert np.array_equal(sup[key], sel[key]), key
+    assert np.array_equal(sup["selected_logprob"], sel["selected_logprob"], equal_nan=True)
+    for j, n in enumerate(sup["lengths"]):
+        assert np.array_equal(sup["packed_ids"][j, :n], sel["packed_ids"][j, :n])
+
+
+def _group_masses(x64, T):
+    """(first sorted position, C/Z) of every tie group of a finite row, in logit-descending order
+    (input construction only: the expected outputs come from the oracle)."""
+    s = np.sort(x64)[::-1]
+    w = np.exp((s - s[0]) / T)
+    C = np.concatenate(([0.0], np.cumsum(w)[:-1]))
+    Z = w.sum()
+    starts = np.concatenate(([0], np.nonzero(s[1:] != s[:-1])[0] + 1))
+    return starts, C[starts] / Z
+
+
+@pytest.mark.parametrize("V", [151936, 262144])
+def test_top_p_boundary_just_outside_the_window(V):
+    # Rows whose top-p threshold lies 1.5e-5 to 3e-5 (in C/Z) from a tie group's boundary: no
+    # row is reported, so support, length, order, logprobs and token must all be exact. Stash
+    # mode (top_k 1024) and compaction mode (top_k 6000), on bf16 rows with and without ties.
+    rng = np.random.default_rng(V + 17)
+    deltas = [1.5e-5, -1.5e-5, 2e-5, -2e-5, 3e-5, -3e-5]
+    rows, Ts, ks, ps = [], [], [], []
+    for kind, k in (("gauss", 1024), ("grid", 1024), ("gauss", 6000), ("grid", 6000)):
+        for i, dlt in enumerate(deltas):
+            x = rng.standard_normal(V) * 1.5
+            if kind == "grid":
+                x = np.round(x * 8) / 8
+            x = oracle.decode_logits(f32_to_bf16_bits(np.asarray(x, np.float32)), "bf16")
+            T = float(np.float32(rng.uniform(0.7, 1.3)))
+            starts, cz = _group_masses(x, T)
+            inside = np.nonzero((starts > 0) & (starts < k) & (cz > 0.01) & (cz < 0.99))[0]
+            g = inside[rng.integers(len(inside))]
+            p = np.float32(cz[g] + dlt)
+            rows.append(x)
+            Ts.append(T)
+            ks.append(k)
+            ps.append(float(p))
+    wl = make(f"top_p_boundary_V{V}", rows, "bf16", T=np.array(Ts), k=np.array(ks),
+              p=np.array(ps), W=8192)
+    ref = oracle_batch(wl)
+    flagged = [r for r in range(wl.B) if ref.rows[r].flagged]
+    assert not flagged, flagged  # the construction keeps every row outside the windows
+    log(f"case top-p boundary rows V={V}")
+    got = run_gpu(wl)
+    errs, stats = compare(got, ref, wl.optin_rows)
+    assert errs == [], errs[:10]
+    assert stats["flagged"] == 0 and stats["rows"] == wl.B

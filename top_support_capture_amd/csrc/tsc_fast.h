@@ -629,7 +629,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
   // Lanes past the segment's end read zeros: only loads that reach the end need the test.
   const uint32_t nfull = uniform_u32(nseg / kWaveSize);  // loads wholly inside the segment
-  [[maybe_unused]] const uint32_t nloads = uniform_u32((nseg + kWaveSize - 1) / kWaveSize);
   auto mask_tail = [&](int j) {
     if ((uint32_t)j >= nfull) {  // wave-uniform: a scalar branch, no vector work on full loads
       if ((uint32_t)j * kWaveSize + lane >= nseg)
@@ -843,15 +842,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const float wth = 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc));
 #pragma unroll
   for (int j = 3; j < LOADS; ++j) {
-    // The long stream skips the steps a shorter row does not need (a wave-uniform test). The
-    // short one has no such test: conditional issues make the compiler's wait counts
-    // conservative, which serialises the load pipeline (loads past the segment read zeros).
-    if constexpr (LOADS > kShortLoads) {
-      if ((uint32_t)j >= nloads) continue;
-      if (j + kLoadsAhead < LOADS && (uint32_t)(j + kLoadsAhead) < nloads) issue(j + kLoadsAhead);
-    } else {
-      if (j + kLoadsAhead < LOADS) issue(j + kLoadsAhead);
-    }
+    // Every step issues its load unconditionally (loads past the segment read zeros through the
+    // buffer descriptor, with no memory traffic): a conditional issue makes the compiler's wait
+    // counts conservative (vmcnt(0) at every step), which serialises the load pipeline.
+    if (j + kLoadsAhead < LOADS) issue(j + kLoadsAhead);
     mask_tail(j);
     unpack(r[j], f);
     bool flag;
