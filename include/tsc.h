@@ -58,8 +58,12 @@ enum {
                                 the ordered support are written, logprobs still use the full S */
   TSC_ROW_NO_SUPPORT = 2,    /* every logit is -inf                                            */
   TSC_ROW_NONFINITE = 3,     /* some logit is NaN or +inf                                       */
-  TSC_ROW_INVALID_PARAM = 4  /* temperature negative / non-finite / subnormal, or top_p or min_p
+  TSC_ROW_INVALID_PARAM = 4, /* temperature negative / non-finite / subnormal, or top_p or min_p
                                 NaN or outside [0, 1]                                          */
+  TSC_ROW_ABORTED = 5        /* a wait between the waves of the row's workgroup reached its limit
+                                (tsc_set_wait_limit): token -1, length 0, selected logprob NaN;
+                                the slot's packed entries and bitmask row may be written in part.
+                                Never produced by a correct run with the default limit.        */
 };
 
 /* Largest packed width W this build accepts. */
@@ -204,6 +208,19 @@ size_t tsc_workspace_size(int64_t B, int64_t V, int64_t R, int32_t W, int32_t dt
 
 /* Static, human-readable name of a TSC_* return code. */
 const char* tsc_status_string(int32_t status);
+
+/*
+ * tsc_set_wait_limit -- the limit of the bounded waits inside the single-read sampler kernel.
+ *
+ * The waves of a row's workgroup hand work to each other through flags in shared memory; each
+ * wait for such a flag sleeps at most `sleeps` times (one sleep is 64 clocks) before the row
+ * gives up with TSC_ROW_ABORTED, so that a row whose flag is never published still ends and the
+ * kernel exits normally. 0 restores the default (2^20 sleeps, tens of milliseconds, far beyond
+ * any wait of a correct row: microseconds). A small value makes rows give up on purpose, for
+ * tests of that path. Process-wide; takes effect at the next launch; returns the previous limit.
+ * Not a sampling parameter: results are unchanged for every row that does not report ABORTED.
+ */
+uint32_t tsc_set_wait_limit(uint32_t sleeps);
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t tsc_version(void);

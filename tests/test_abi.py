@@ -24,9 +24,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["tsc_replay_logprob", "tsc_sample_with_mask",
-                                    "tsc_sample_with_mask_bits", "tsc_status_string",
-                                    "tsc_support_bits_ld", "tsc_support_csr", "tsc_version",
-                                    "tsc_workspace_size"]
+                                    "tsc_sample_with_mask_bits", "tsc_set_wait_limit",
+                                    "tsc_status_string", "tsc_support_bits_ld", "tsc_support_csr",
+                                    "tsc_version", "tsc_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -40,6 +40,17 @@ def test_status_strings_and_version(lib):
     assert lib.tsc_status_string(99) == b"TSC_UNKNOWN_STATUS"
     assert lib.tsc_version() >= 100
     assert lib.tsc_workspace_size(256, 151936, 256, 2048, 1) == 0
+
+
+def test_wait_limit_setting(lib):
+    # Host-side state only: 0 restores the default (2^20 sleeps); the previous value is returned.
+    import top_support_capture_amd as tsc
+    prev = tsc.set_wait_limit(7)
+    try:
+        assert tsc.set_wait_limit(0) == 7
+        assert tsc.set_wait_limit(0) == 1 << 20
+    finally:
+        tsc.set_wait_limit(prev)
 
 
 def _call(lib, **kw):

@@ -79,3 +79,28 @@ def test_traffic_summary_is_keyed_by_workload_and_sources(tmp_path, monkeypatch)
         json.dump({"workload": wl.name, "kernel_source_hash": "0" * 16,
                    "hbm_bytes_per_launch": 123.0}, f)
     assert bench.measured_traffic(wl) is None
+
+
+def test_cpu_model_is_named():
+    import bench
+    assert bench.cpu_model().strip() not in ("", "unknown CPU")
+
+
+def test_oracle_check_counts_the_boundary_reports():
+    # The oracle's own outputs for workload 1 pass the bench's check; a wrong token is counted.
+    import numpy as np
+    import oracle
+    import bench
+    from workloads import make_workload
+    wl = make_workload(1)
+    ref = oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k, wl.top_p,
+                                  wl.min_p, wl.optin_rows, wl.seeds, wl.positions, wl.W)
+    got = {"tokens": ref.tokens.copy(), "row_status": ref.row_status.copy(),
+           "packed_ids": ref.packed_ids.copy(), "lengths": ref.lengths.copy(),
+           "logprobs": ref.logprobs.copy(), "selected_logprob": ref.selected_logprob.copy()}
+    chk = bench.oracle_check(wl, got)
+    assert chk["rows"] == wl.B and chk["rows_with_errors"] == 0
+    for key in ("race_flagged", "top_p_flagged", "min_p_flagged", "overflow"):
+        assert chk[key] >= 0
+    got["tokens"][0] = (got["tokens"][0] + 1) % wl.V
+    assert bench.oracle_check(wl, got)["rows_with_errors"] >= 1

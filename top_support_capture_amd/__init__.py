@@ -19,12 +19,13 @@ __all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "wor
            "csr_to_host",
            "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
+           "ROW_ABORTED", "set_wait_limit",
            "MAX_PACKED_WIDTH", "TscError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsc.so")
 
 TSC_DTYPE_F32, TSC_DTYPE_BF16 = 0, 1
-ROW_OK, ROW_OVERFLOW, ROW_NO_SUPPORT, ROW_NONFINITE, ROW_INVALID_PARAM = 0, 1, 2, 3, 4
+ROW_OK, ROW_OVERFLOW, ROW_NO_SUPPORT, ROW_NONFINITE, ROW_INVALID_PARAM, ROW_ABORTED = 0, 1, 2, 3, 4, 5
 MAX_PACKED_WIDTH = 16384
 
 _lib: Optional[ctypes.CDLL] = None
@@ -65,6 +66,8 @@ def library() -> ctypes.CDLL:
     lib.tsc_status_string.restype = ctypes.c_char_p
     lib.tsc_version.argtypes = []
     lib.tsc_version.restype = I32
+    lib.tsc_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.tsc_set_wait_limit.restype = ctypes.c_uint32
     _lib = lib
     return lib
 
@@ -84,6 +87,13 @@ class SampleOutput(NamedTuple):
 def workspace_size(B: int, V: int, R: int, W: int, dtype: torch.dtype) -> int:
     dt = TSC_DTYPE_BF16 if dtype == torch.bfloat16 else TSC_DTYPE_F32
     return int(library().tsc_workspace_size(B, V, R, W, dt))
+
+
+def set_wait_limit(sleeps: int) -> int:
+    """Limit of the bounded waits between the waves of a row's workgroup (``tsc_set_wait_limit``):
+    0 restores the default; a tiny value makes rows give up with ROW_ABORTED (for tests of that
+    path). Returns the previous limit."""
+    return int(library().tsc_set_wait_limit(int(sleeps)))
 
 
 def support_bits_ld(V: int) -> int:

@@ -2,6 +2,7 @@
 // caller's stream. Nothing here allocates device memory or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "tsc.h"
@@ -13,28 +14,47 @@ namespace {
 
 constexpr int32_t kVersion = 100;  // 0.1.0
 
+// The dynamic LDS limit of a kernel is a per-device attribute: it is set once for each device
+// the calling thread has current when it launches (devices 0..kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
 // One workgroup per row. Rows the single-read path serves run there; every other row runs the
 // general multi-pass algorithm inside the same launch.
 template <int DT, bool BITS>
 hipError_t launch_sampler(const tsc::SampleArgs& a, hipStream_t stream) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_fast_kernel<DT, BITS>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)tsc::kFastDynLds);
-  });
-  if (attr_err != hipSuccess) return attr_err;
+  static std::mutex mu;
+  static bool attr_set[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!attr_set[dev]) {
+      err = hipFuncSetAttribute(reinterpret_cast<const void*>(&tsc::sample_fast_kernel<DT, BITS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tsc::kFastDynLds);
+      if (err != hipSuccess) return err;
+      attr_set[dev] = true;
+    }
+  }
   hipLaunchKernelGGL((tsc::sample_fast_kernel<DT, BITS>), dim3((unsigned)a.B), dim3(tsc::kThreads),
                      tsc::kFastDynLds, stream, a);
   return hipGetLastError();
 }
+
+// Limit of the bounded waits between the waves of a workgroup (tsc_set_wait_limit).
+std::atomic<uint32_t> g_wait_limit{tsc::kDefaultWaitLimit};
 
 }  // namespace
 
 extern "C" {
 
 int32_t tsc_version(void) { return kVersion; }
+
+uint32_t tsc_set_wait_limit(uint32_t sleeps) {
+  return g_wait_limit.exchange(sleeps == 0u ? tsc::kDefaultWaitLimit : sleeps,
+                               std::memory_order_relaxed);
+}
 
 const char* tsc_status_string(int32_t status) {
   switch (status) {
@@ -86,7 +106,8 @@ int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, 
   tsc::SampleArgs a{logits, B, V, ld, temperature, top_k, top_p, min_p, optin_rows, R,
                     seeds, positions, R > 0 ? W : 1, tokens, row_status, packed_ids,
                     logprobs, lengths, selected_logprob,
-                    R > 0 ? reinterpret_cast<uint32_t*>(support_bits) : nullptr, bits_ld / 4};
+                    R > 0 ? reinterpret_cast<uint32_t*>(support_bits) : nullptr, bits_ld / 4,
+                    g_wait_limit.load(std::memory_order_relaxed)};
   (void)hipGetLastError();  // start from a clean error state so a launch error is ours
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bits = a.bits != nullptr;
@@ -155,8 +176,11 @@ int32_t tsc_replay_logprob(const void* logits, int32_t dtype, int64_t N, int64_t
                     support_bits, bits_ld, tokens, selected_logprob, logprobs, row_status};
   (void)hipGetLastError();
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // Support logprobs of bitmask rows read their logits from an LDS stage (bfloat16).
-  const bool stage = logprobs != nullptr && support_bits != nullptr && capture_status != nullptr;
+  // Support logprobs of bitmask rows read their logits from an LDS stage (bfloat16). That
+  // instantiation holds 144 KB of LDS (one workgroup per CU), so it is launched only when a row
+  // can be staged at all: V / 8 chunks within the stage's chunk table.
+  const bool stage = logprobs != nullptr && support_bits != nullptr && capture_status != nullptr &&
+                     (V + 7) / 8 <= (int64_t)tsc::kStageChunks;
   if (dtype == TSC_DTYPE_F32)
     hipLaunchKernelGGL((tsc::replay_kernel<TSC_DTYPE_F32, false>), dim3((unsigned)N), dim3(tsc::kThreads), 0, s, a);
   else if (stage)

@@ -149,6 +149,7 @@ struct FastShared {
   int32_t dstar;
   uint32_t L;
   double lnzs;
+  uint32_t aborted;            // set by a wait that reached its limit (see lds_wait_at_least)
 };
 
 __device__ inline uint32_t lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -226,7 +227,9 @@ __device__ inline float race_noise(float u) {
 // Flags and counters between the waves of one workgroup, in LDS. A publish orders every earlier
 // LDS write of the wave before the flag (release at workgroup scope); a wait spins with s_sleep
 // until the flag reaches a value, then orders the wave's later LDS reads after it. Every flag a
-// wave waits on is published unconditionally by waves that never wait on it, so every wait ends.
+// wave waits on is published unconditionally by waves that never wait on it, so every wait ends;
+// each wait is bounded all the same (see lds_wait_at_least), so that a broken publish would end
+// the row with an ABORTED status instead of a workgroup that never finishes.
 // Counters move in steps of 64: every lane of the wave (always fully active here) adds 1, so
 // that no branch on the lane surrounds the atomic (such a branch inside a claim loop has been
 // compiled into a loop exit that only lane 0 takes) and the compiler can fold the 64 adds into
@@ -247,10 +250,27 @@ __device__ inline uint32_t lds_claim(uint32_t* ctr) {
   const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return read_lane(old, 0) / kStep;
 }
-__device__ inline void lds_wait_at_least(const uint32_t* flag, uint32_t v) {
-  while (uniform_u32(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v)
+// Waits until *flag >= v and returns true; gives up and returns false after `limit` sleeps of
+// its own, setting *aborted, or as soon as another wave of the workgroup has set *aborted. A wave
+// whose wait gave up skips the rest of its work up to the row's last barrier, where the row gets
+// the ABORTED status (fast_row_bf16). One s_sleep(1) is 64 clocks, so the default limit (2^20
+// sleeps, tens of milliseconds) is far beyond any wait of a correct row (microseconds).
+constexpr uint32_t kDefaultWaitLimit = 1u << 20;
+__device__ inline bool lds_wait_at_least(const uint32_t* flag, uint32_t v, uint32_t limit,
+                                         uint32_t* aborted) {
+  for (uint32_t spins = 0;; ++spins) {
+    if (uniform_u32(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= v)
+      break;
+    if (uniform_u32(__hip_atomic_load(aborted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0u)
+      return false;
+    if (spins >= limit) {
+      __hip_atomic_store(aborted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return false;
+    }
     __builtin_amdgcn_s_sleep(1);
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return true;
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -616,6 +636,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   if (tid < (uint32_t)kThetaBins / 2) fs.theta_hist[tid] = 0u;
   if (tid == 0) {
     fs.ndone = 0u;
+    fs.aborted = 0u;
     fs.scan_ready = 0u;
     fs.prefix_done = 0u;
     fs.job_next = 0u;
@@ -1198,13 +1219,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       lds_publish_step(&fs.ready);
     }
   }
-  lds_wait_at_least(&fs.scan_ready, 1u);
-  const int32_t decision = fs.decision;
-  if (decision == kNonfinite || decision == kNoSupport) {
-    finish_empty_row(a, b, slot, decision == kNonfinite ? TSC_ROW_NONFINITE : TSC_ROW_NO_SUPPORT);
-    return true;
-  }
-  if (decision != kProceed) return false;
+  const uint32_t wlim = a.wait_limit;
+  // Wave 0 published scan_ready itself; every other wave waits for it (bounded).
+  const bool scanned = lds_wait_at_least(&fs.scan_ready, 1u, wlim, &fs.aborted);
+  if (scanned && fs.decision == kProceed) {
   float m = -__builtin_inff();
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
@@ -1221,7 +1239,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // ---- 5. The pick, then the ordered capture of the opt-in row -----------------------------
   if (picker) {
     __builtin_amdgcn_s_setprio(3);
-    lds_wait_at_least(&fs.ready, jobs * kStep);
+    if (lds_wait_at_least(&fs.ready, jobs * kStep, wlim, &fs.aborted)) {
     // The support is bins d = 0..d*; bin d holds key kmax - d at index dspan - d. Float32 scores
     // first; bins within kRaceMargin of the best are rescored in float64, ties -> lowest id.
     float b1 = -__builtin_inff(), b2 = -__builtin_inff();
@@ -1268,6 +1286,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       token = wave_reduce(bs == wt ? bid : 0x7FFFFFFF, [](int32_t x, int32_t y) { return x < y ? x : y; });
       td = wave_reduce(bs == wt && bid == token ? bd : 0u, MaxU32());
     }
+    // Written at once (thread 0, the same thread that writes an ABORTED status over them after
+    // the row's last barrier, in program order, should any wait of the row give up).
     if (lane == 0) {
       a.tokens[b] = token;
       a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
@@ -1275,6 +1295,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         a.lengths[slot] = (int32_t)(L < W ? L : W);
         a.selected_logprob[slot] = (float)(bins[dspan - td] - lnzs);
       }
+    }
     }
   }
   if constexpr (COMPACT) {
@@ -1284,8 +1305,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // members before it in this chunk (ballots over the bits of the bin). Its packed word goes to
   // the LDS stage; once every list is staged, the stage is copied out with coalesced stores.
   __builtin_amdgcn_s_setprio(1);
-  if (capture) {
-    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
+  if (capture && lds_wait_at_least(&fs.prefix_done, 4u * kStep, wlim, &fs.aborted)) {
     // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
     // value >= x_cut (-0 and +0 compare equal, as their keys do).
     const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
@@ -1332,8 +1352,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     // Copy-out of the stage, in slices of 1024 positions.
     const uint32_t nl = L < W ? L : W;
     const uint32_t nout = nl < (uint32_t)LY::kStageCap ? nl : (uint32_t)LY::kStageCap;
-    if (nout > 0u) {
-      lds_wait_at_least(&fs.staged, (uint32_t)kWaves * kStep);
+    if (nout > 0u && lds_wait_at_least(&fs.staged, (uint32_t)kWaves * kStep, wlim, &fs.aborted)) {
       for (;;) {
         const uint32_t sl = lds_claim(&fs.copy_next);
         if (sl * 1024u >= nout) break;
@@ -1379,8 +1398,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // A survivor's position is its bin's base (tokens with larger keys) + the bin's members in
   // earlier segments (smaller ids: the prefix over the waves) + its rank in its wave.
   __builtin_amdgcn_s_setprio(1);
-  if (capture) {
-    lds_wait_at_least(&fs.prefix_done, 4u * kStep);
+  if (capture && lds_wait_at_least(&fs.prefix_done, 4u * kStep, wlim, &fs.aborted)) {
     // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
     // value >= x_cut (-0 and +0 compare equal, as their keys do).
     const float x_cut = E::to_float(bits_of_key<E>(kmax - (uint32_t)dstar));
@@ -1414,7 +1432,20 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
   }
   }
-  return true;
+  }
+  // Every wave arrives here exactly once, whatever its waits gave: the row's outputs are decided
+  // after this barrier, by what the workgroup as a whole saw.
+  lds_barrier();
+  if (fs.aborted != 0u) {
+    finish_empty_row(a, b, slot, TSC_ROW_ABORTED);
+    return true;
+  }
+  const int32_t decision = fs.decision;
+  if (decision == kNonfinite || decision == kNoSupport) {
+    finish_empty_row(a, b, slot, decision == kNonfinite ? TSC_ROW_NONFINITE : TSC_ROW_NO_SUPPORT);
+    return true;
+  }
+  return decision == kProceed;
 }
 
 

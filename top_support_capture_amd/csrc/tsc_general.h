@@ -37,6 +37,7 @@ struct SampleArgs {
   float* selected_logprob;
   uint32_t* bits;   // [R, bits_ld] support bitmasks of OVERFLOW slots, or null
   int64_t bits_ld;  // row stride of `bits` in 32-bit words (a multiple of 4)
+  uint32_t wait_limit;  // sleeps a wait between the waves of a workgroup may take (>= 1)
 };
 
 // Words of a support bitmask row that a kernel writes: the bits of ids 0..V-1 (bit i in word
