@@ -288,8 +288,12 @@ def _fast_rows(rng, V):
     zpos = rng.choice(V, 12, replace=False)
     zeros[zpos[:6]] = 0.0
     zeros[zpos[6:]] = -0.0
+    # A language-model-like head: a log-Zipf rank bonus on a random permutation over a Gaussian
+    # bulk, so that top-p keeps a handful of tokens (drawn last: the rows above keep their draws).
+    rank = rng.permutation(V).astype(np.float64) + 1.0
+    zipf = rng.standard_normal(V) + 4.0 * (-1.2 * np.log(rank))
     return dict(grid=grid, gauss=gauss, neg=neg, nan=nan, pinf=pinf, allneg=allneg,
-                hidden=hidden, front=front, spread=spread, wide=wide, zeros=zeros)
+                hidden=hidden, front=front, spread=spread, wide=wide, zeros=zeros, zipf=zipf)
 
 
 FAST_PARAMS = [
@@ -338,6 +342,24 @@ FAST_PARAMS = [
     ("compact8k_nan_p", "nan", 1.0, 6000, 0.9, 0.0),
     ("compact8k_pinf_p", "pinf", 1.0, 6000, 0.9, 0.0),
     ("compact8k_pinf_minp", "pinf", 1.0, 8192, 0.95, 0.02),
+    # top_k off (<= 0 or >= V) or above the compaction range: the row is served here when top-p
+    # or min-p ends its support among the candidates, else by the general path.
+    ("koff_zipf_p9", "zipf", 1.0, -1, 0.9, 0.0),
+    ("koff_zipf_p99", "zipf", 1.4, 0, 0.99, 0.0),
+    ("koff_zipf_minp", "zipf", 1.0, -1, 1.0, 0.05),
+    ("koff_zipf_p_minp", "zipf", 0.7, -1, 0.95, 0.001),
+    ("koff_grid_p5", "grid", 0.8, -1, 0.5, 0.0),
+    ("koff_grid_p0", "grid", 1.0, -1, 0.0, 0.0),
+    ("koff_gauss_minp", "gauss", 1.0, -1, 1.0, 0.3),
+    ("koff_gauss_p9", "gauss", 1.0, -1, 0.9, 0.0),         # a wide support: general path
+    ("koff_wide_minp_p", "wide", 12.0, -1, 0.97, 0.01),
+    ("koff_nan_p", "nan", 1.0, -1, 0.9, 0.0),
+    ("koff_pinf_p", "pinf", 1.0, -1, 0.9, 0.0),
+    ("koff_allneg_p", "allneg", 1.0, -1, 0.9, 0.0),
+    ("kgeV_grid_p7", "grid", 1.0, 10**6, 0.7, 0.0),
+    ("kbig_zipf_p8", "zipf", 0.5, 20000, 0.8, 0.0),
+    ("kbig_gauss_p", "gauss", 1.0, 12000, 0.5, 0.0),
+    ("koff_nofilter", "zipf", 1.0, -1, 1.0, 0.0),          # every finite token: general path
 ]
 
 

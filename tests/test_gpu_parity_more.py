@@ -30,11 +30,13 @@ def _check(wl, got, ref, W=None, max_flagged_frac=0.05):
     return stats
 
 
-def test_workload5_every_row():
+@pytest.mark.parametrize("index", [5, 6])
+def test_workload_every_row(index):
     # The mixed 1024-row batch (top_k 1..4096, top_p, min_p, temperature per row, 10% greedy
-    # rows): every row against the oracle, which samples its rows in worker processes.
-    wl = make_workload(5)
-    log(f"case workload 5 {wl.name} B={wl.B} V={wl.V}: every row")
+    # rows) and the same recipe with top-k off: every row against the oracle, which samples its
+    # rows in worker processes.
+    wl = make_workload(index)
+    log(f"case workload {index} {wl.name} B={wl.B} V={wl.V}: every row")
     got = run_gpu(wl)
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref)

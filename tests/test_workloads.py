@@ -11,7 +11,7 @@ DIG = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "g
                                   "workload_digests.json")))
 
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5, 6])
 def test_workload_digest(index):
     wl = make_workload(index)
     d = DIG[str(index)]
@@ -27,6 +27,8 @@ def test_workload_shapes_follow_the_recipe():
     wl5 = make_workload(5)
     assert np.count_nonzero(wl5.temperature == 0) == 102 and wl5.R == 256
     assert np.all(np.diff(wl5.optin_rows) > 0)
+    wl6 = make_workload(6)
+    assert np.all(wl6.top_k == -1) and np.count_nonzero(wl6.min_p == 0) == wl6.B // 2
 
 
 def test_bf16_rounding_is_nearest_even():

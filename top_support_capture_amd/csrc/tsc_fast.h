@@ -147,6 +147,7 @@ struct FastShared {
   uint32_t wave_cand[kWaves];
   int32_t decision;
   int32_t dstar;
+  int32_t dlow;                // the largest d (lowest key) holding a candidate
   uint32_t L;
   double lnzs;
   uint32_t aborted;            // set by a wait that reached its limit (see lds_wait_at_least)
@@ -369,8 +370,10 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
   }
   uint32_t lc = 0;
   double lmass = 0.0;
+  int32_t low = -1;  // the lane's largest d holding a candidate
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
+    if (cnt[t] != 0u) low = (int32_t)(lane * nb + (uint32_t)t);
     if (need_m && !(((double)xs[t] - (double)m) >= tln_mp)) cnt[t] = 0u;
     bm[t] = (NEED_P || capture) ? (double)cnt[t] * (double)__builtin_amdgcn_exp2f((xs[t] - m) * c)
                                 : 0.0;
@@ -414,9 +417,11 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
   const int owner = (int)((uint32_t)dstar / nb);
   const uint32_t L = read_lane(bL, owner);
   const double lnzs = ln_fast(read_lane(bZ, owner));  // logprob = (x - m) / T - ln Z_S
+  const int32_t dlow = wave_reduce(low, MaxI32());
   if (lane == 0) {
     fs.decision = kProceed;
     fs.dstar = dstar;
+    fs.dlow = dlow;
     fs.L = L;
     fs.lnzs = lnzs;
   }
@@ -435,10 +440,12 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
   auto value_of_d = [&](uint32_t d) { return E::to_float(bits_of_key<E>(kmax - d)); };
   // Count and mass of bin d after min-p (a per-value predicate, monotone in d).
+  int32_t low = -1;  // the lane's largest d holding a candidate
   auto bin = [&](uint32_t d, uint32_t& bc, double& bm) {
     bc = 0;
     bm = 0.0;
     if (d <= dspan) {
+      if (hcnt[dspan - d] != 0u) low = (int32_t)d;
       const float x = value_of_d(d);
       if (!need_m || ((double)x - (double)m) >= tln_mp) {
         bc = hcnt[dspan - d];
@@ -494,9 +501,11 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   const int owner = (int)((uint32_t)dstar / nb);
   const uint32_t L = read_lane(bL, owner);
   const double lnzs = ln_fast(read_lane(bZ, owner));  // logprob = (x - m) / T - ln Z_S
+  const int32_t dlow = wave_reduce(low, MaxI32());
   if (lane == 0) {
     fs.decision = kProceed;
     fs.dstar = dstar;
+    fs.dlow = dlow;
     fs.L = L;
     fs.lnzs = lnzs;
   }
@@ -569,7 +578,7 @@ template <> struct LayoutOf<true> { using type = LayoutCompact; };
 // go through the general path instead; `slot` is then already set.
 template <bool NEED_P, bool COMPACT, int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, int64_t& slot,
-                                              float T, int32_t k, float p, float mp,
+                                              float T, int32_t k, int32_t kv, float p, float mp,
                                               uint64_t seed, uint64_t pos, unsigned char* lds,
                                               FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
@@ -594,7 +603,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   uint32_t theta_rank;
   {
     const float target =
-        k > 1536 ? 1.2f * (float)k + 320.0f : 1.6f * (float)k + 64.0f;
+        kv > 1536 ? 1.2f * (float)kv + 320.0f : 1.6f * (float)kv + 64.0f;
     const float q = fminf(1.0f, target / (float)V);
     const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
     const float pr = 1.0f - t4 * t4;
@@ -1139,16 +1148,20 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         Z = zr * exp2_fast(-(double)nrc - (double)m * (double)c);
         if (!(zr <= 1.0e300)) decision = kFallback;  // a float32 lane sum overflowed
       }
-      // theta is a lower bound of the k-th largest value iff at least k candidates exist.
-      if (over || ntot < (uint32_t)k || kmax < theta_key || kmax - theta_key >= (uint32_t)kDBins)
-        decision = kFallback;
+      if (over || kmax < theta_key || kmax - theta_key >= (uint32_t)kDBins) decision = kFallback;
       if (decision == kProceed) {
         const uint32_t dspan = kmax - theta_key;
         if (dspan < 4u * kWaveSize)
           bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         else
           bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
-        if (BITS && capture && fs.L > (uint32_t)a.W) {
+        // Every token at or above theta is a candidate, so the scan is exact for the tie groups
+        // it covers; the support is decided iff it also ends there: theta lies at or below the
+        // k-th largest value (at least k candidates), or some candidate group below the support's
+        // last group is excluded by top-p, min-p or top-k (with monotone predicates, every
+        // token below theta is excluded too). Otherwise the general path decides the row.
+        if (ntot < (uint32_t)k && !(fs.dstar < fs.dlow)) decision = kFallback;
+        if (decision == kProceed && BITS && capture && fs.L > (uint32_t)a.W) {
           // A support wider than W is also written as a bitmask: cleared here, and its bits set
           // by the capture. Waiting for every memory counter to drain means the clearing stores
           // have reached this CU's L2, where the capture's ORs and stores land, before any wave
@@ -1449,16 +1462,18 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 }
 
 
+// k: the row's top_k, INT32_MAX when the filter is off; kv: the top_k the cutoff theta is chosen
+// for (k itself up to the compaction range, else kFastMaxK in stash mode).
 template <int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b, int64_t& slot,
-                                                  float T, int32_t k, float p, float mp,
+                                                  float T, int32_t k, int32_t kv, float p, float mp,
                                                   uint64_t seed, uint64_t pos, unsigned char* lds,
                                                   FastShared& fs) {
-  if (k <= kFastMaxK)
-    return p < 1.0f ? fast_row_bf16<true, false, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                    : fast_row_bf16<false, false, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
-  return p < 1.0f ? fast_row_bf16<true, true, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-                  : fast_row_bf16<false, true, LOADS, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+  if (kv <= kFastMaxK)
+    return p < 1.0f ? fast_row_bf16<true, false, LOADS, BITS>(a, b, slot, T, k, kv, p, mp, seed, pos, lds, fs)
+                    : fast_row_bf16<false, false, LOADS, BITS>(a, b, slot, T, k, kv, p, mp, seed, pos, lds, fs);
+  return p < 1.0f ? fast_row_bf16<true, true, LOADS, BITS>(a, b, slot, T, k, kv, p, mp, seed, pos, lds, fs)
+                  : fast_row_bf16<false, true, LOADS, BITS>(a, b, slot, T, k, kv, p, mp, seed, pos, lds, fs);
 }
 
 // BITS: the call passed a support bitmask buffer (a separate instantiation, so that calls without
@@ -1478,15 +1493,23 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     const float p = a.top_p[b];
     const float mp = a.min_p[b];
     const uint64_t seed = a.seeds[b], pos = a.positions[b];
-    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f && k >= 1 &&
-                          k <= kCompactMaxK && a.V >= kFastMinV && a.V <= kFastMaxV &&
+    // top_k off (<= 0 or >= V) or beyond the compaction range: the cutoff is chosen as for
+    // top_k = kFastMaxK, and the row is served here when top-p or min-p ends its support among
+    // the candidates (checked after the scan; otherwise the general path takes it). A row with
+    // no filter at all (support = every finite token) goes to the general path directly.
+    const bool k_on = k >= 1 && (int64_t)k < a.V;
+    const int32_t keff = k_on ? k : 0x7FFFFFFF;
+    const int32_t kv = (k_on && k <= kCompactMaxK) ? k : kFastMaxK;
+    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f &&
+                          ((k_on && k <= kCompactMaxK) || p < 1.0f || mp > 0.0f) &&
+                          a.V >= kFastMinV && a.V <= kFastMaxV &&
                           (a.V & 7) == 0 && (a.ld & 7) == 0 &&
                           (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
     if (eligible) {
       const bool done =
           a.V <= kShortMaxV
-              ? fast_row_dispatch<kShortLoads, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs)
-              : fast_row_dispatch<kFastLoads, BITS>(a, b, slot, T, k, p, mp, seed, pos, lds, fs);
+              ? fast_row_dispatch<kShortLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs)
+              : fast_row_dispatch<kFastLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }

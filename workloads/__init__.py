@@ -4,7 +4,7 @@ This module only draws numbers: logits matrices and per-row sampling parameters.
 step of the sampling method itself (no softmax, no filtering, no random race), so both the CPU
 oracle and the HIP path can consume its output without sharing any of the method's arithmetic.
 
-The five workloads follow the shapes and value distributions of the sampling-mask pages: a
+The six workloads follow the shapes and value distributions of the sampling-mask pages: a
 decode batch of logits rows over an LLM vocabulary, per-row temperature / top-k / top-p / min-p,
 a subset of rows that opt in to support capture, and per-request seeds.
 Real model logits are not available, so Gaussian logits (optionally plus a log-Zipf rank bonus,
@@ -145,7 +145,7 @@ def _full(B, v, dt):
 
 
 def make_workload(index: int, *, W: Optional[int] = None) -> Workload:
-    """Build workload ``index`` (1..5). ``W`` overrides the packed width."""
+    """Build workload ``index`` (1..6). ``W`` overrides the packed width."""
     rng = np.random.default_rng(index - 1)
     if index == 1:
         B, V = 4, 1024
@@ -184,6 +184,18 @@ def make_workload(index: int, *, W: Optional[int] = None) -> Workload:
         opt = np.sort(rng.choice(B, 256, replace=False)).astype(np.int32)
         wl = Workload("b1024_v262144_bf16_mixed", "bf16", x, T, k, p, mp, opt,
                       _seeds(index, B), np.zeros(B, np.uint64), 4608)
+    elif index == 6:
+        # The mixed batch's logits recipe with top-k off on every row: pure top-p (U[0.8, 1.0]),
+        # min-p U[0, 0.1] on half the rows, temperature U[0.5, 1.5], 25% of rows opt-in.
+        B, V = 1024, 262144
+        x = _logits(rng, B, V, 1.0, "bf16", zipf=(1.2, 4.0))
+        T = rng.uniform(0.5, 1.5, B).astype(np.float32)
+        p = rng.uniform(0.8, 1.0, B).astype(np.float32)
+        mp = rng.uniform(0.0, 0.1, B).astype(np.float32)
+        mp[rng.choice(B, B // 2, replace=False)] = 0.0
+        opt = np.sort(rng.choice(B, 256, replace=False)).astype(np.int32)
+        wl = Workload("b1024_v262144_bf16_topk_off", "bf16", x, T, _full(B, -1, np.int32), p, mp,
+                      opt, _seeds(index, B), np.zeros(B, np.uint64), 4608)
     else:
         raise ValueError(f"unknown workload {index}")
     if W is not None:
@@ -192,4 +204,5 @@ def make_workload(index: int, *, W: Optional[int] = None) -> Workload:
 
 
 WORKLOADS = {1: "b4_v1024_f32", 2: "b64_v32000_f32_zipf", 3: "b256_v151936_bf16_grid",
-             4: "b256_v129280_bf16_k8192", 5: "b1024_v262144_bf16_mixed"}
+             4: "b256_v129280_bf16_k8192", 5: "b1024_v262144_bf16_mixed",
+             6: "b1024_v262144_bf16_topk_off"}
