@@ -398,3 +398,28 @@ def test_empty_batch():
                              e(torch.int32), e(torch.int32))
     torch.cuda.synchronize()
     assert rep.selected_logprob.numel() == 0 and rep.row_status.numel() == 0
+
+
+@pytest.mark.parametrize("V", [16384, 32000, 100000])
+def test_single_read_path_rows_f32(V):
+    # The float32 single-read path (sorted candidates): the same row kinds and parameters as the
+    # bfloat16 rows, as float32 values; rows it cannot decide take the general path.
+    rng = np.random.default_rng(91 + V)
+    rows = _fast_rows(rng, V)
+    rows["gauss_fine"] = rng.standard_normal(V) * 1.7  # distinct float32 values (few ties)
+    params = FAST_PARAMS + [("fine_k100_p9", "gauss_fine", 1.0, 100, 0.9, 0.0),
+                            ("fine_k2048", "gauss_fine", 0.8, 2048, 0.97, 0.0),
+                            ("fine_koff_minp", "gauss_fine", 0.5, -1, 1.0, 0.02)]
+    names = [e[0] for e in params]
+    x = [rows[e[1]] for e in params]
+    cols = list(zip(*[e[2:] for e in params]))
+    for W in (2048, 16):
+        wl = make(f"fast_f32_V{V}_W{W}", x, "f32", T=np.array(cols[0]), k=np.array(cols[1]),
+                  p=np.array(cols[2]), mp=np.array(cols[3]), W=W)
+        log(f"case float32 single-read path V={V} W={W}: {names}")
+        got = run_gpu(wl, bits=True)
+        ref = oracle_of(wl, bits=True)
+        errs, stats = compare(got, ref, wl.optin_rows)
+        assert errs == [], [(e, names[int(e.split()[1].rstrip(':'))]) if e.startswith("row") else e for e in errs]
+        check(wl, got, ref, max_flagged_frac=0.2)
+        check_bits(wl, got, ref, min_rows=0 if W == 2048 else 10)

@@ -105,6 +105,7 @@ constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowShl4 = 0x104;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 }  // namespace dpp
 
@@ -124,6 +125,37 @@ __device__ inline T dpp_mov(T old, T src) {
                                                               ROW_MASK, 0xF, false);
     return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
   }
+}
+
+// The value held by lane (lane ^ J), J = 1, 2, ..., 32, in VALU instructions only: DPP within a
+// row of 16 lanes (xor 4 takes the row shift in each direction and keeps the one in range), and
+// gfx950's permlane swaps across rows (xor 16: odd rows of one copy with even rows of the other;
+// xor 32: the two halves of the wave).
+template <int J>
+__device__ inline uint32_t xor_lanes(uint32_t x) {
+  static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane xor");
+  const uint32_t lane = threadIdx.x & 63u;
+  if constexpr (J == 1) {
+    return dpp_mov<dpp::kQuadSwap1>(x, x);
+  } else if constexpr (J == 2) {
+    return dpp_mov<dpp::kQuadSwap2>(x, x);
+  } else if constexpr (J == 4) {
+    const uint32_t up = dpp_mov<dpp::kRowShl4>(x, x), dn = dpp_mov<dpp::kRowShr4>(x, x);
+    return (lane & 4u) ? dn : up;
+  } else if constexpr (J == 8) {
+    return dpp_mov<dpp::kRowRor8>(x, x);
+  } else if constexpr (J == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16u) ? sw[0] : sw[1];
+  } else {
+    const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32u) ? sw[0] : sw[1];
+  }
+}
+
+template <int J>
+__device__ inline uint64_t xor_lanes(uint64_t x) {
+  return ((uint64_t)xor_lanes<J>((uint32_t)(x >> 32)) << 32) | xor_lanes<J>((uint32_t)x);
 }
 
 template <class T>
@@ -161,6 +193,43 @@ __device__ inline T wave_incl_scan(T v, Op op, T id) {
   return v;
 }
 
+// ---- Per-wave partials in LDS ------------------------------------------------------------------
+// A 64-lane read of one LDS word (a broadcast) occupies the LDS as long as a read of 64 distinct
+// words, so 16 waves each reading 16 partials one by one keep it busy for ~500 clocks per 32-bit
+// array. Instead every wave reads the 16 partials once (lane i holds s[i % 16]: four copies of
+// the row of 16 lanes) and combines them on DPP within a row.
+static_assert(kWaves == 16, "the partials of a workgroup fill one DPP row of 16 lanes");
+
+// Reduction over the first 16 lanes, for data that every row of 16 lanes holds alike (lane l
+// holding entry l % 16): four DPP steps inside each row (a fixed order), then lane 0.
+template <class T, class Op>
+__device__ inline T row16_reduce(T v, Op op) {
+  v = op(v, dpp_mov<dpp::kQuadSwap1>(v, v));
+  v = op(v, dpp_mov<dpp::kQuadSwap2>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor4>(v, v));
+  v = op(v, dpp_mov<dpp::kRowRor8>(v, v));
+  return read_lane(v, 0);
+}
+
+// op over s[0..15]; the same value (wave-uniform, identical in every wave) for every lane.
+template <class T, class Op>
+__device__ inline T waves_reduce(const T* s, Op op) {
+  return row16_reduce(s[threadIdx.x & (kWaves - 1)], op);
+}
+
+// op over s[0..w-1] for the calling wave w (`id` for wave 0); `total` receives op over all 16.
+template <class T, class Op>
+__device__ inline T waves_prefix(const T* s, Op op, T id, T& total) {
+  T v = s[threadIdx.x & (kWaves - 1)];
+  v = op(v, dpp_mov<dpp::kRowShr1>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr2>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr4>(id, v));
+  v = op(v, dpp_mov<dpp::kRowShr8>(id, v));
+  total = read_lane(v, kWaves - 1);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
+  return w == 0 ? id : read_lane(v, w - 1);
+}
+
 // ---- Block reductions (fixed order, hence deterministic) -----------------------------------
 // Reduces `v` over the workgroup; every thread receives the result. `scratch` is shared memory
 // of at least kWaves * 8 bytes; the leading barrier makes back-to-back calls safe.
@@ -171,10 +240,7 @@ __device__ inline T block_reduce(T v, Op op, uint64_t* scratch) {
   lds_barrier();
   if ((threadIdx.x & (kWaveSize - 1)) == 0) s[threadIdx.x / kWaveSize] = v;
   lds_barrier();
-  T r = s[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = op(r, s[i]);
-  return r;
+  return waves_reduce(s, op);
 }
 
 struct MaxOp {

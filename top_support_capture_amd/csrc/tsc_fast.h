@@ -294,8 +294,8 @@ __device__ inline SlotScan slot_step1(int32_t e, FastShared& fs) {
 __device__ inline void slot_step2(const SampleArgs& a, int64_t b, const SlotScan& sc,
                                   FastShared& fs) {
   const uint32_t tid = threadIdx.x, lane = lane_id(), wid = wave_id();
-  int32_t before = INT32_MIN;
-  for (uint32_t w = 0; w < wid; ++w) before = before > fs.slot_wmax[w] ? before : fs.slot_wmax[w];
+  int32_t all;
+  const int32_t before = waves_prefix(fs.slot_wmax, MaxI32(), INT32_MIN, all);
   const int32_t excl = sc.excl_w > before ? sc.excl_w : before;
   const bool in = (int64_t)tid < a.R;
   const bool valid = in && sc.e >= 0 && (int64_t)sc.e < a.B && sc.e > excl;
@@ -308,10 +308,7 @@ __device__ inline void slot_step2(const SampleArgs& a, int64_t b, const SlotScan
 }
 // After a barrier that follows slot_step2.
 __device__ inline int64_t slot_step3(const FastShared& fs) {
-  int32_t slot = -1;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) slot = slot > fs.slot_hit[w] ? slot : fs.slot_hit[w];
-  return slot;
+  return waves_reduce(fs.slot_hit, MaxI32());
 }
 
 // ln(v) for a positive finite double with an absolute error of about 3e-7: the binary exponent
@@ -326,17 +323,6 @@ __device__ inline double ln_fast(double v) {
 __device__ inline double exp2_fast(double a) {
   const double n = __builtin_floor(a);
   return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
-}
-
-// Reduction over the first 16 lanes, for data that every row of 16 lanes holds alike (lane l
-// holding entry l % 16): four DPP steps inside each row, then lane 0.
-template <class T, class Op>
-__device__ inline T row16_reduce(T v, Op op) {
-  v = op(v, dpp_mov<dpp::kQuadSwap1>(v, v));
-  v = op(v, dpp_mov<dpp::kQuadSwap2>(v, v));
-  v = op(v, dpp_mov<dpp::kRowRor4>(v, v));
-  v = op(v, dpp_mov<dpp::kRowRor8>(v, v));
-  return read_lane(v, 0);
 }
 
 // Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d; they
@@ -786,10 +772,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   lds_barrier();
   // Step 1, exchange 2: the mass reference R = the sample's maximum; histogram of the distances
   // to it; slot step 2.
-  uint32_t kmax0 = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) kmax0 = kmax0 > fs.kmax0_w[w] ? kmax0 : fs.kmax0_w[w];
-  kmax0 = uniform_u32(kmax0);
+  const uint32_t kmax0 = waves_reduce(fs.kmax0_w, MaxU32());
   {
     const float R = E::to_float(bits_of_key<E>(kmax0));
     // A non-finite sample maximum (all -inf, or +inf/NaN: the row is then nonfinite anyway)
@@ -1236,9 +1219,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // Wave 0 published scan_ready itself; every other wave waits for it (bounded).
   const bool scanned = lds_wait_at_least(&fs.scan_ready, 1u, wlim, &fs.aborted);
   if (scanned && fs.decision == kProceed) {
-  float m = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) m = fs.wave_m[w] > m ? fs.wave_m[w] : m;
+  const float m = waves_reduce(fs.wave_m, MaxOp());
   const uint32_t kmax = key_of<E>(__float_as_uint(m) >> 16);
   const uint32_t dspan = kmax - theta_key;
   const int32_t dstar = fs.dstar;
@@ -1476,6 +1457,12 @@ __device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b
                   : fast_row_bf16<false, true, LOADS, BITS>(a, b, slot, T, k, kv, p, mp, seed, pos, lds, fs);
 }
 
+}  // namespace tsc
+
+#include "tsc_fast_f32.h"
+
+namespace tsc {
+
 // BITS: the call passed a support bitmask buffer (a separate instantiation, so that calls without
 // one run no bitmask code at all).
 template <int DT, bool BITS>
@@ -1510,6 +1497,33 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
           a.V <= kShortMaxV
               ? fast_row_dispatch<kShortLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs)
               : fast_row_dispatch<kFastLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs);
+      if (done) return;
+      __syncthreads();  // the general path reuses the LDS
+    }
+  } else {
+    const float T = a.temperature[b];
+    const int32_t k = a.top_k[b];
+    const float p = a.top_p[b];
+    const float mp = a.min_p[b];
+    const uint64_t seed = a.seeds[b], pos = a.positions[b];
+    // As for bfloat16 rows: top_k off or above kF32MaxK chooses the cutoff as for kF32MaxK.
+    const bool k_on = k >= 1 && (int64_t)k < a.V;
+    const int32_t keff = k_on ? k : 0x7FFFFFFF;
+    const int32_t kv = (k_on && k <= kF32MaxK) ? k : kF32MaxK;
+    const bool eligible = row_params_valid(T, p, mp) && T > 0.0f &&
+                          ((k_on && k <= kF32MaxK) || p < 1.0f || mp > 0.0f) &&
+                          a.V >= kF32MinV && a.V <= kF32MaxV && (a.V & 3) == 0 &&
+                          (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
+    if (eligible) {
+      bool done;
+      if (a.V <= kF32ShortMaxV)
+        done = p < 1.0f
+                   ? fast_row_f32<true, kF32ShortLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs)
+                   : fast_row_f32<false, kF32ShortLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs);
+      else
+        done = p < 1.0f
+                   ? fast_row_f32<true, kF32LongLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs)
+                   : fast_row_f32<false, kF32LongLoads, BITS>(a, b, slot, T, keff, kv, p, mp, seed, pos, lds, fs);
       if (done) return;
       __syncthreads();  // the general path reuses the LDS
     }
