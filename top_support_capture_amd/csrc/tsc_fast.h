@@ -174,6 +174,22 @@ __device__ inline uint32_t mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// The lanes where `in` holds whose bin equals this lane's (bins below 2^nbits, nbits <= 10,
+// wave-uniform): one ballot per bit of the bin, and per 32-bit half of the lane mask one
+// XNOR-AND with this lane's own bit spread to all 32 bits (0 or ~0).
+__device__ inline uint64_t same_bin_lanes(uint32_t bin, bool in, uint32_t nbits) {
+  const uint64_t live = __ballot(in);
+  uint32_t lo = (uint32_t)live, hi = (uint32_t)(live >> 32);
+  for (int bit = 0; bit < 10; ++bit) {
+    if ((uint32_t)bit >= nbits) break;
+    const uint64_t ones = __ballot((bin >> bit) & 1u);
+    const uint32_t mine = (uint32_t)((int32_t)(bin << (31 - bit)) >> 31);
+    lo &= ~((uint32_t)ones ^ mine);
+    hi &= ~((uint32_t)(ones >> 32) ^ mine);
+  }
+  return ((uint64_t)hi << 32) | lo;
+}
+
 struct SumU32 {
   __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
 };
@@ -259,11 +275,18 @@ __device__ inline uint32_t lds_claim(uint32_t* ctr) {
 constexpr uint32_t kDefaultWaitLimit = 1u << 20;
 __device__ inline bool lds_wait_at_least(const uint32_t* flag, uint32_t v, uint32_t limit,
                                          uint32_t* aborted) {
+  // Lane 0 alone polls: a read by all 64 lanes of one word costs the LDS as much as 64 distinct
+  // words, and up to 15 polling waves would otherwise take much of the LDS from the waves that
+  // work. The loop's exits test wave-uniform values, so the whole wave leaves together.
+  const bool poller = (threadIdx.x & (kWaveSize - 1)) == 0u;
   for (uint32_t spins = 0;; ++spins) {
-    if (uniform_u32(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= v)
-      break;
-    if (uniform_u32(__hip_atomic_load(aborted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0u)
-      return false;
+    uint32_t f = 0u, ab = 0u;
+    if (poller) {
+      f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      ab = __hip_atomic_load(aborted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (uniform_u32(f) >= v) break;
+    if (uniform_u32(ab) != 0u) return false;
     if (spins >= limit) {
       __hip_atomic_store(aborted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return false;
@@ -1040,12 +1063,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         if (in) atomicOr(reinterpret_cast<unsigned long long*>(&binmask[bi]), 1ull << lane);
         same = in ? binmask[bi] : 0ull;
       } else {
-        same = __ballot(in);
-#pragma unroll
-        for (int bit = 0; bit < 10; ++bit) {
-          const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
-          same &= ((bi >> bit) & 1u) ? ones : ~ones;
-        }
+        same = same_bin_lanes(bi, in, 10u);
       }
       if (in) {
         const uint32_t c0 = bincnt[bi];
@@ -1323,11 +1341,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         const uint32_t wd = i < ncj ? cand_c[i] : 0xFF800000u;
         const bool in = i < ncj && __uint_as_float(wd & 0xFFFF0000u) >= x_cut;
         const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-        uint64_t same = __ballot(in);
-        for (uint32_t bit = 0; bit < nbits; ++bit) {
-          const uint64_t ones = __ballot(in && ((bi >> bit) & 1u));
-          same &= ((bi >> bit) & 1u) ? ones : ~ones;
-        }
+        const uint64_t same = same_bin_lanes(bi, in, nbits);
         if (in) {
           const uint32_t c0 = run_c[bi];
           const uint32_t at = binbase[bi] + c0 + mbcnt(same);
