@@ -65,11 +65,10 @@ constexpr uint32_t kOwnDraws = 4;
 //     of each load are appended to the wave's candidate list as the load lands.
 // Each wave counts its candidates per bin bi = key - theta_key in a table of its own (u16; later
 // the exclusive prefix over the earlier waves) and ranks each among its earlier candidates of the
-// same bin. Stash mode (small supports) ranks before the exchange and writes the capture
-// directly. Compaction mode (supports of thousands) only counts before the exchange, ranks while
-// the race draws run, and writes each survivor's packed word (id | bi << 18) at its position in
-// an LDS stage that is copied out with coalesced stores (positions past the stage are written
-// directly).
+// same bin, before the exchange (stash mode keeps the ranks in LDS, compaction mode in
+// registers). Stash mode (small supports) writes the capture directly. Compaction mode (supports
+// of thousands) writes each survivor's packed word (id | bi << 18) at its position in an LDS stage
+// that is copied out with coalesced stores (positions past the stage are written directly).
 constexpr int kTableBytes = kDBins * 2;
 constexpr int kMaskBins = 256;        // stash mode: bins with a 64-bit lane mask in the table
 
@@ -876,6 +875,25 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // (A theta weight below 2^-100 would flag every load: the stash overflows and the row falls
   // back, which happens only for extreme spreads of the logits at low temperature.)
   const float wth = 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc));
+  // Race draws of 128 candidates from `base` of this wave's list (two Philox chains per lane).
+  // Each candidate's uniform is kept per bin as max(u numerator << 32 | ~id) (see the pick).
+  uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest);
+  const uint32_t* cand_own = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + wid * LY::kCandCap;
+  auto draw_job = [&](uint32_t base, uint32_t lim) {
+    const uint32_t i0 = base + lane, i1 = i0 + kWaveSize;
+    const bool v0 = i0 < lim, v1 = i1 < lim;
+    const uint32_t wd0 = v0 ? cand_own[i0] : 0u, wd1 = v1 ? cand_own[i1] : 0u;
+    const uint32_t id0w = id0 + (wd0 & 0x3FFFu), id1w = id0 + (wd1 & 0x3FFFu);
+    const uint32_t r0 = race_word(id0w, seed, pos);
+    const uint32_t r1 = race_word(id1w, seed, pos);
+    const uint32_t bi0 = key_of<E>(wd0 >> 16) - theta_key, bi1 = key_of<E>(wd1 >> 16) - theta_key;
+    if (v0 && bi0 < (uint32_t)kDBins)
+      atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi0]),
+                ((unsigned long long)(2u * (r0 >> 9) + 1u) << 32) | (unsigned long long)(~id0w));
+    if (v1 && bi1 < (uint32_t)kDBins)
+      atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
+                ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
+  };
 #pragma unroll
   for (int j = 3; j < LOADS; ++j) {
     // Every step issues its load unconditionally (loads past the segment read zeros through the
@@ -923,7 +941,6 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   // Candidate word: bf16 bits << 16 | offset of the token in the segment (< 2^14), in id order.
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds + LY::kOffCand) + wid * LY::kCandCap;
-  uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest);
   // theta is finite whenever the row can be served here; clamping it keeps -inf out.
   const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
   uint32_t ncand = 0;            // wave-uniform
@@ -1028,19 +1045,60 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (lane == 0) fs.wave_m[wid] = wm;
   }
   const uint32_t bmax = wxc > -__builtin_inff() ? key_of<E>(__float_as_uint(wxc) >> 16) - theta_key : 0u;
+  // Compaction mode: the rank of candidate 64 c + lane among the wave's earlier candidates of its
+  // bin, two 16-bit ranks per register, kept until the capture (a bin is wholly in the support or
+  // wholly out, so ranks among all candidates are ranks among the survivors).
+  constexpr int kRankRegs = COMPACT ? LY::kCandCap / kWaveSize / 2 : 1;
+  uint32_t crank[kRankRegs];
   if constexpr (COMPACT) {
-    // Counts: the row histogram and this wave's table (two 16-bit counts per word), with LDS
-    // atomics whose results are not needed, so that no chunk waits for another. (The ranks the
-    // capture needs are taken after the exchange, where they overlap the race draws.)
-    uint32_t* bincnt32 = reinterpret_cast<uint32_t*>(bincnt);
-    for (uint32_t base = 0; base < nc_here; base += kWaveSize) {
-      const uint32_t i = base + lane;
-      const uint32_t wd = i < nc_here ? cand[i] : 0xFF800000u;
-      const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-      if (i < nc_here && bi < (uint32_t)kDBins) {  // wider spans fall back (span test)
-        atomicAdd(&hcnt[bi], 1u);
-        atomicAdd(&bincnt32[bi >> 1], 1u << ((bi & 1u) * 16u));
+    // The bin's count in earlier chunks (this wave's own table: plain reads and writes) plus the
+    // lanes of its bin below it in this chunk: a 64-bit lane mask per bin that every lane ORs its
+    // bit into (the wave's 2 KB slice of the stage, unused until the capture), or, when the wave's
+    // bins reach beyond the mask table, ballots over the bits of the bin. The bin's first lane
+    // stores the new count, clears the mask and adds the chunk's count to the row histogram.
+    uint64_t* binmask = reinterpret_cast<uint64_t*>(lds + LY::kOffStage) + wid * kMaskBins;
+    static_assert(kWaves * kMaskBins * 8 <= LY::kStageCap * 4, "lane masks fit the stage");
+    const bool by_mask = bmax < (uint32_t)kMaskBins;
+    if (by_mask)
+      for (uint32_t i = lane; i < (uint32_t)kMaskBins; i += kWaveSize) binmask[i] = 0ull;
+    const uint32_t nbits_w = bmax < (uint32_t)kDBins ? 32u - (uint32_t)__builtin_clz(bmax | 1u) : 10u;
+    // One LDS round trip per chunk: the next chunk's words are read ahead, and the mask and the
+    // count are read together.
+    uint32_t wd_next = lane < nc_here ? cand[lane] : 0xFF800000u;
+#pragma unroll
+    for (int cc = 0; cc < 2 * kRankRegs; ++cc) {
+      uint32_t r = 0u;
+      if ((uint32_t)cc * kWaveSize < nc_here) {
+        const uint32_t i = (uint32_t)cc * kWaveSize + lane;
+        const uint32_t wd = wd_next;
+        if (cc + 1 < 2 * kRankRegs) {
+          const uint32_t in_ = i + kWaveSize;
+          wd_next = in_ < nc_here ? cand[in_] : 0xFF800000u;
+        }
+        const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+        const bool in = i < nc_here && bi < (uint32_t)kDBins;  // wider spans fall back (span test)
+        uint64_t same;
+        uint32_t c0 = 0u;
+        if (by_mask) {
+          if (in) atomicOr(reinterpret_cast<unsigned long long*>(&binmask[bi]), 1ull << lane);
+          same = in ? binmask[bi] : 0ull;
+          c0 = in ? bincnt[bi] : 0u;
+        } else {
+          same = same_bin_lanes(bi, in, nbits_w);
+          c0 = in ? bincnt[bi] : 0u;
+        }
+        if (in) {
+          r = c0 + mbcnt(same);
+          if (lane == (uint32_t)__builtin_ctzll(same)) {
+            const uint32_t cnt = (uint32_t)__popcll(same);
+            bincnt[bi] = (uint16_t)(c0 + cnt);
+            if (by_mask) binmask[bi] = 0ull;
+            atomicAdd(&hcnt[bi], cnt);
+          }
+        }
       }
+      if (cc & 1) crank[cc >> 1] |= r << 16;
+      else crank[cc >> 1] = r;
     }
   } else {
     // Rank of each candidate among the wave's earlier candidates of its bin: the bin's count in
@@ -1077,25 +1135,12 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       }
     }
   }
-  // Race draws of this wave's own candidates, 128 at a time (two Philox chains per lane); the
-  // helper waves draw the rest after the exchange. Each candidate's uniform is kept per bin as
-  // max(u numerator << 32 | ~id) (see the pick).
+  // Race draws of this wave's own candidates (the first waves to end their streams); the helper
+  // waves draw the rest after the exchange.
   uint32_t nz = 0;
   if (order < kOwnDraws) {
     for (uint32_t base = 0; base < nc_here; base += 2u * kWaveSize) {
-      const uint32_t i0 = base + lane, i1 = i0 + kWaveSize;
-      const bool v0 = i0 < nc_here, v1 = i1 < nc_here;
-      const uint32_t wd0 = v0 ? cand[i0] : 0u, wd1 = v1 ? cand[i1] : 0u;
-      const uint32_t id0w = id0 + (wd0 & 0x3FFFu), id1w = id0 + (wd1 & 0x3FFFu);
-      const uint32_t r0 = race_word(id0w, seed, pos);
-      const uint32_t r1 = race_word(id1w, seed, pos);
-      const uint32_t bi0 = key_of<E>(wd0 >> 16) - theta_key, bi1 = key_of<E>(wd1 >> 16) - theta_key;
-      if (v0 && bi0 < (uint32_t)kDBins)
-        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi0]),
-                  ((unsigned long long)(2u * (r0 >> 9) + 1u) << 32) | (unsigned long long)(~id0w));
-      if (v1 && bi1 < (uint32_t)kDBins)
-        atomicMax(reinterpret_cast<unsigned long long*>(&binbest[bi1]),
-                  ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
+      draw_job(base, nc_here);
       nz = base + 2u * kWaveSize < nc_here ? base + 2u * kWaveSize : nc_here;
     }
   }
@@ -1311,11 +1356,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     }
   }
   if constexpr (COMPACT) {
-  // Capture (compaction mode): one job per wave's candidate list, claimed by whichever waves are free. A survivor's
-  // position is its bin's base (tokens with larger keys) + the bin's members in earlier segments
-  // (smaller ids: the wave's table, now the prefix over the waves, kept running) + the bin's
-  // members before it in this chunk (ballots over the bits of the bin). Its packed word goes to
-  // the LDS stage; once every list is staged, the stage is copied out with coalesced stores.
+  // Capture (compaction mode): every wave stages its own list from the ranks it took before the
+  // exchange, then the waves copy the stage out in slices.
   __builtin_amdgcn_s_setprio(1);
   if (capture && lds_wait_at_least(&fs.prefix_done, 4u * kStep, wlim, &fs.aborted)) {
     // A candidate survives iff its key >= kmax - d* (bins failing min-p lie beyond d*), i.e. its
@@ -1326,32 +1368,29 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     uint32_t* stage = reinterpret_cast<uint32_t*>(lds + LY::kOffStage);
     uint32_t* const brow = (BITS && L > W) ? a.bits + slot * a.bits_ld : nullptr;
     if (BITS && brow != nullptr) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // Bits of the bins of the support: bi <= dspan.
-    const uint32_t nbits = 32u - (uint32_t)__builtin_clz(dspan | 1u);
-    for (;;) {
-      const uint32_t cj = lds_claim(&fs.cap_next);
-      if (cj >= (uint32_t)kWaves) break;
-      const uint32_t ncj0 = fs.wave_cand[cj];
-      const uint32_t ncj = ncj0 < (uint32_t)LY::kCandCap ? ncj0 : (uint32_t)LY::kCandCap;
-      const uint32_t* cand_c = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + cj * LY::kCandCap;
-      uint16_t* run_c = reinterpret_cast<uint16_t*>(lds + LY::kOffTables + cj * LY::kTableStride);
-      const uint32_t id0c = cj * cw * 8u;
-      for (uint32_t base = 0; base < ncj; base += kWaveSize) {
-        const uint32_t i = base + lane;
-        const uint32_t wd = i < ncj ? cand_c[i] : 0xFF800000u;
-        const bool in = i < ncj && __uint_as_float(wd & 0xFFFF0000u) >= x_cut;
-        const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
-        const uint64_t same = same_bin_lanes(bi, in, nbits);
-        if (in) {
-          const uint32_t c0 = run_c[bi];
-          const uint32_t at = binbase[bi] + c0 + mbcnt(same);
-          if (lane == (uint32_t)__builtin_ctzll(same)) run_c[bi] = (uint16_t)(c0 + (uint32_t)__popcll(same));
-          const uint32_t id = id0c + (wd & 0x3FFFu);
-          if (at < (uint32_t)LY::kStageCap) {
-            stage[at] = id | (bi << 18);
-          } else if (at < W) {
-            out_ids[at] = (int32_t)id;
-            if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
+    {
+      // Each wave places its own list: a survivor's position is its bin's base (tokens with
+      // larger keys) + the bin's members in earlier segments (the wave's table, now the prefix
+      // over the waves) + its rank in the wave. Its packed word (id | bi << 18) goes to the LDS
+      // stage; once every list is staged, the stage is copied out with coalesced stores.
+      const uint32_t* cand_w = reinterpret_cast<const uint32_t*>(lds + LY::kOffCand) + wid * LY::kCandCap;
+      const uint16_t* pre_w = reinterpret_cast<const uint16_t*>(lds + LY::kOffTables + wid * LY::kTableStride);
+#pragma unroll
+      for (int cc = 0; cc < 2 * kRankRegs; ++cc) {
+        if ((uint32_t)cc * kWaveSize < nc_here) {
+          const uint32_t i = (uint32_t)cc * kWaveSize + lane;
+          const uint32_t wd = i < nc_here ? cand_w[i] : 0xFF800000u;
+          if (i < nc_here && __uint_as_float(wd & 0xFFFF0000u) >= x_cut) {
+            const uint32_t bi = key_of<E>(wd >> 16) - theta_key;
+            const uint32_t r = (crank[cc >> 1] >> ((cc & 1) * 16)) & 0xFFFFu;
+            const uint32_t at = binbase[bi] + pre_w[bi] + r;
+            const uint32_t id = id0 + (wd & 0x3FFFu);
+            if (at < (uint32_t)LY::kStageCap) {
+              stage[at] = id | (bi << 18);
+            } else if (at < W) {
+              out_ids[at] = (int32_t)id;
+              if (out_lp) out_lp[at] = (float)(bins[bi] - lnzs);
+            }
           }
         }
       }
