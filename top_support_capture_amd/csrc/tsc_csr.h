@@ -40,13 +40,8 @@ __global__ void __launch_bounds__(kThreads) csr_scan_kernel(CsrArgs a) {
     const int64_t incl = wave_incl_scan(v, SumOp(), (int64_t)0);
     if (lane == kWaveSize - 1) wave_tot[w] = incl;
     lds_barrier();
-    int64_t before = 0, total = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      const int64_t t = wave_tot[i];
-      before += i < (int)w ? t : 0;
-      total += t;
-    }
+    int64_t total;
+    const int64_t before = waves_prefix(wave_tot, SumOp(), (int64_t)0, total);
     if (j < a.R) a.offsets[j + 1] = carry + before + incl;
     carry += total;
     lds_barrier();  // wave_tot is rewritten by the next chunk

@@ -215,13 +215,13 @@ __device__ inline int64_t find_capture_slot(const SampleArgs& a, int64_t b, uint
     lds_barrier();
     if (lane == kWaveSize - 1) wt[tid / kWaveSize] = inc;
     lds_barrier();
-    int32_t before = carry;
-    for (int w = 0; w < tid / kWaveSize; ++w) before = before > wt[w] ? before : wt[w];
+    int32_t all;
+    const int32_t wbefore = waves_prefix(wt, MaxOp(), INT32_MIN, all);
+    const int32_t before = carry > wbefore ? carry : wbefore;
     int32_t excl = __shfl_up(inc, 1, kWaveSize);
     if (lane == 0) excl = INT32_MIN;
     excl = excl > before ? excl : before;
-    int32_t chunk_max = carry;
-    for (int w = 0; w < kWaves; ++w) chunk_max = chunk_max > wt[w] ? chunk_max : wt[w];
+    const int32_t chunk_max = carry > all ? carry : all;
     if (j < a.R) {
       const bool valid = e >= 0 && (int64_t)e < a.B && e > excl;
       if (valid && (int64_t)e == b) my_slot = (int32_t)j;

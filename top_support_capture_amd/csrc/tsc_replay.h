@@ -94,8 +94,8 @@ __device__ inline void lse_merge(float& m, float& s, float m2, float s2, float c
 }
 
 // One workgroup-wide combination of the threads' states (a single barrier): each wave merges
-// its lanes with DPP moves, lane 0 stores the wave's state, and every thread merges the 16
-// wave states in the same fixed order.
+// its lanes with DPP moves, lane 0 stores the wave's state, and every wave merges the 16 wave
+// states in the same fixed order.
 __device__ inline void lse_block(OnlineLse& st, float c, ReplayShared& sh) {
   float m = st.m, s = st.s;
   uint32_t f = st.flags;
@@ -132,13 +132,16 @@ __device__ inline void lse_block(OnlineLse& st, float c, ReplayShared& sh) {
     sh.f[w] = f;
   }
   lds_barrier();
-  m = sh.m[0], s = sh.s[0], f = sh.f[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) {
-    lse_merge(m, s, sh.m[i], sh.s[i], c);
-    f |= sh.f[i];
-  }
-  st.m = m, st.s = s, st.flags = f;
+  // The 16 wave states: lane l reads wave l % 16's (one LDS read per wave instead of 16
+  // broadcast reads), the same four DPP merges combine each row of 16, and lane 0 holds the
+  // result, the same in every wave.
+  const uint32_t l16 = threadIdx.x & (kWaves - 1);
+  m = sh.m[l16], s = sh.s[l16], f = sh.f[l16];
+  step([](auto v) { return dpp_mov<dpp::kQuadSwap1>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kQuadSwap2>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kRowRor4>(v, v); });
+  step([](auto v) { return dpp_mov<dpp::kRowRor8>(v, v); });
+  st.m = read_lane(m, 0), st.s = read_lane(s, 0), st.flags = read_lane(f, 0);
 }
 
 template <int DT, bool STAGE>
@@ -222,13 +225,8 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
       const uint32_t w = tid / kWaveSize;
       if ((tid & (kWaveSize - 1)) == kWaveSize - 1) sh.scan[w] = incl;
       lds_barrier();
-      uint32_t before = 0, total = 0;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) {
-        const uint32_t t = sh.scan[i];
-        before += i < (int)w ? t : 0u;
-        total += t;
-      }
+      uint32_t total;
+      const uint32_t before = waves_prefix(sh.scan, SumOp(), 0u, total);
       slot_next = before + incl - cnt;
       staged_row = total <= (uint32_t)kStageSlots;
     }
