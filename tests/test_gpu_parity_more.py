@@ -107,3 +107,58 @@ def test_top_p_boundary_just_outside_the_window(V):
     errs, stats = compare(got, ref, wl.optin_rows)
     assert errs == [], errs[:10]
     assert stats["flagged"] == 0 and stats["rows"] == wl.B
+
+
+def _greedy_case(dtype, V):
+    # Greedy rows (temperature 0) with the maximum planted where the one-read greedy pass keeps
+    # its bookkeeping: twice in one thread's chunks (chunk c and c + 1024 are read by the same
+    # thread), twice in one chunk, in neighbouring chunks (two threads), in the ragged tail, as
+    # -0 / +0 ties; and rows that are NaN, +inf, all -inf or finite in one place only.
+    kv = 8 if dtype == "bf16" else 4
+    rng = np.random.default_rng(V + kv)
+    base = np.round(rng.standard_normal(V) * 2 * 8) / 8  # bfloat16-exact values below 64
+    rows, expect = [], []
+
+    def plant(ids, value=64.0, first=None):
+        r = base.copy()
+        r[list(ids)] = value
+        rows.append(r)
+        expect.append(min(ids) if first is None else first)
+
+    c = 777
+    plant([c * kv + 5, (c + 1024) * kv + 1])
+    plant([c * kv + 6, c * kv + 2])
+    plant([(c + 1) * kv, c * kv + kv - 1])
+    plant([V - 1])
+    plant([3, V - 1])
+    z = -np.abs(base) - 1
+    r = z.copy(); r[100] = -0.0; r[50] = 0.0; rows.append(r); expect.append(50)
+    r = z.copy(); r[30] = -0.0; r[60] = 0.0; rows.append(r); expect.append(30)
+    r = base.copy(); r[V // 2] = np.nan; rows.append(r); expect.append(-1)
+    r = base.copy(); r[V - 1] = np.nan; rows.append(r); expect.append(-1)
+    r = base.copy(); r[11] = np.inf; rows.append(r); expect.append(-1)
+    rows.append(np.full(V, -np.inf)); expect.append(-1)
+    r = np.full(V, -np.inf); r[V - 2] = -3.5; rows.append(r); expect.append(V - 2)
+    rows.append(base.copy()); expect.append(int(np.argmax(base)))
+    B = len(rows)
+    p = np.full(B, 0.9, np.float32)
+    p[-1] = 1.5  # invalid parameters on a greedy row: INVALID_PARAM
+    expect[-1] = -1
+    wl = make(f"greedy_{dtype}_V{V}", rows, dtype, T=0.0, k=np.arange(B) - 3, p=p,
+              mp=np.where(np.arange(B) % 3 == 0, 0.05, 0.0), optin=np.arange(0, B, 2), W=4)
+    return wl, np.array(expect)
+
+
+@pytest.mark.parametrize("dtype,V,pad", [("bf16", 262144, 0), ("bf16", 100003, 5),
+                                         ("bf16", 50000, 3), ("f32", 131075, 1),
+                                         ("f32", 32000, 0)])
+def test_greedy_rows(dtype, V, pad):
+    # pad 5 / 1 keeps 16-byte aligned rows with a ragged end (the one-read greedy pass); pad 3
+    # leaves the rows unaligned, which the general path serves.
+    wl, expect = _greedy_case(dtype, V)
+    log(f"case greedy rows {dtype} V={V} row stride V+{pad}")
+    got = run_gpu(wl, pad=pad)
+    assert got["tokens"].tolist() == expect.tolist(), (got["tokens"], expect)
+    _check(wl, got, oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k,
+                                            wl.top_p, wl.min_p, wl.optin_rows, wl.seeds,
+                                            wl.positions, wl.W), max_flagged_frac=0.0)

@@ -1513,6 +1513,7 @@ __device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b
 }  // namespace tsc
 
 #include "tsc_fast_f32.h"
+#include "tsc_greedy.h"
 
 namespace tsc {
 
@@ -1533,6 +1534,11 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     const float p = a.top_p[b];
     const float mp = a.min_p[b];
     const uint64_t seed = a.seeds[b], pos = a.positions[b];
+    if (greedy_eligible<DT>(a, T, p, mp)) {
+      slot = find_capture_slot(a, b, fs.red);
+      greedy_row<DT>(a, b, slot, fs.red);
+      return;
+    }
     // top_k off (<= 0 or >= V) or beyond the compaction range: the cutoff is chosen as for
     // top_k = kFastMaxK, and the row is served here when top-p or min-p ends its support among
     // the candidates (checked after the scan; otherwise the general path takes it). A row with
@@ -1559,6 +1565,11 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
     const float p = a.top_p[b];
     const float mp = a.min_p[b];
     const uint64_t seed = a.seeds[b], pos = a.positions[b];
+    if (greedy_eligible<DT>(a, T, p, mp)) {
+      slot = find_capture_slot(a, b, fs.red);
+      greedy_row<DT>(a, b, slot, fs.red);
+      return;
+    }
     // As for bfloat16 rows: top_k off or above kF32MaxK chooses the cutoff as for kF32MaxK.
     const bool k_on = k >= 1 && (int64_t)k < a.V;
     const int32_t keff = k_on ? k : 0x7FFFFFFF;
