@@ -46,14 +46,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_path(wl) -> str:
-    return os.path.join(ROOT, "profiles", f"traffic_b{wl.B}_v{wl.V}_{wl.dtype}.json")
+# Kernels whose HBM traffic the counter summaries cover: name in the profiler's trace, prefix of
+# the summary file.
+TRAFFIC_KERNELS = {"sample": ("sample_fast_kernel", "traffic"),
+                   "replay": ("replay_kernel", "traffic_replay")}
 
 
-def measured_traffic(wl):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload, if it
-    was taken on the current kernel sources; else None."""
-    path = traffic_path(wl)
+def traffic_path(wl, kernel: str = "sample") -> str:
+    prefix = TRAFFIC_KERNELS[kernel][1]
+    return os.path.join(ROOT, "profiles", f"{prefix}_{wl.name}.json")
+
+
+def measured_traffic(wl, kernel: str = "sample"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload and
+    kernel, if it was taken on the current kernel sources; else None."""
+    path = traffic_path(wl, kernel)
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
@@ -163,20 +170,23 @@ def copy_calibration(dev, nbytes: int, reps: int = 5) -> None:
 
 # How the counter CSVs that --ingest-pmc reads are made (run from /tmp with TMPDIR=/tmp; R is the
 # repository root).
-PMC_COMMANDS = [
-    'timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$R/gpurun_out/prof/fetch" '
-    '-o fetch -- python3 "$R/bench.py" --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration',
-    'timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$R/gpurun_out/prof/write" '
-    '-o write -- python3 "$R/bench.py" --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration',
-    'python3 bench.py --ingest-pmc gpurun_out/prof/fetch/fetch_counter_collection.csv '
-    'gpurun_out/prof/write/write_counter_collection.csv <JSON line of a bench run of the same kernel>',
-]
+def pmc_commands(index: int, kernel: str) -> list:
+    """The commands that produce a counter summary (run from /tmp, R the repository root)."""
+    run = f'python3 "$R/bench.py" --workload {index} --kernel {kernel} --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration'
+    return [
+        f'timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$R/gpurun_out/prof/fetch" -o fetch -- {run}',
+        f'timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$R/gpurun_out/prof/write" -o write -- {run}',
+        f'python3 bench.py --workload {index} --kernel {kernel} --ingest-pmc gpurun_out/prof/fetch/fetch_counter_collection.csv '
+        'gpurun_out/prof/write/write_counter_collection.csv <JSON line of a bench run of the same kernel>',
+    ]
 
 
-def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) -> dict:
-    """Per-launch HBM traffic of the sampler kernel from two rocprofv3 --pmc counter CSVs
-    (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter
+def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int,
+               kernel: str = "sample") -> dict:
+    """Per-launch HBM traffic of the sampler (or replay) kernel from two rocprofv3 --pmc counter
+    CSVs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter
     reads for the copy calibration kernel of known size."""
+    kname = TRAFFIC_KERNELS[kernel][0]
     import csv
     import statistics
 
@@ -196,10 +206,10 @@ def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) 
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         k = per_kernel(path, counter)
-        samp = [v for n, v in k.items() if "sample_fast_kernel" in n]
+        samp = [v for n, v in k.items() if kname in n]
         copy = [v for n, v in k.items() if "neg_kernel" in n]
         if not samp or not copy:
-            raise SystemExit(f"{path}: no sampler or calibration dispatches for {counter}")
+            raise SystemExit(f"{path}: no {kname} or calibration dispatches for {counter}")
         s_kib = statistics.median([x for v in samp for x in v])
         c_kib = statistics.median([x for v in copy for x in v])
         factor = copy_bytes / (c_kib * 1024.0)
@@ -208,7 +218,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, alg_bytes: int, copy_bytes: int) 
                         "kernel_bytes_scaled": s_kib * 1024.0 * factor,
                         "kernel_dispatches": sum(len(v) for v in samp)}
     total = res["FETCH_SIZE"]["kernel_bytes_scaled"] + res["WRITE_SIZE"]["kernel_bytes_scaled"]
-    return {"commands": PMC_COMMANDS, "counters": res, "hbm_bytes_per_launch": total,
+    return {"counters": res, "hbm_bytes_per_launch": total,
             "algorithmic_bytes_per_launch": alg_bytes, "ratio_to_algorithmic": total / alg_bytes,
             "kernel_source_hash": kernel_source_hash()}
 
@@ -296,16 +306,22 @@ def bench_replay(args, wl) -> int:
         torch.cuda.synchronize()
         return time.perf_counter() - t0, ev0.elapsed_time(ev1) / steps
 
+    # A counter run (--copy-calibration) times the selected-logprob mode alone, the mode the
+    # roofline is quoted for, so that the counters cover that mode only.
+    modes = (False,) if args.copy_calibration else (False, True)
     for i in range(args.warmup):
-        step(i, i & 1 == 1)
+        step(i, modes[i % len(modes)])
     # The two modes (selected logprob only; with support logprobs) alternate in blocks, so that
     # clock and thermal drift fall on both alike; each mode's time is the median over its blocks.
     nblk = 10
     per = max(1, args.steps // nblk)
     blocks = {False: [], True: []}
     for _ in range(nblk):
-        for lp in (False, True):
+        for lp in modes:
             blocks[lp].append(timed(lp, per))
+    if args.copy_calibration:
+        copy_calibration(dev, wl.B * wl.V * esize)
+        blocks[True] = blocks[False]
     wall = sum(w for w, _ in blocks[False])
     avg_ms = float(np.median([m for _, m in blocks[False]]))
     avg_ms_lp = float(np.median([m for _, m in blocks[True]]))
@@ -333,7 +349,7 @@ def bench_replay(args, wl) -> int:
                    "rows_from_bitmask": nbits, "mean_support": float(lengths.mean()),
                    "outputs": "selected logprob"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl, "replay")},
         "kernel_ms": {"mean": avg_ms, "with_support_logprobs": avg_ms_lp,
                       "timing": f"median over {nblk} blocks of {per} calls per mode, the two "
                                 f"modes alternating block by block"},
@@ -465,24 +481,29 @@ def main() -> int:
         from tests.gpu_helpers import device_inputs
 
     wl = make_workload(args.workload)
-    if args.kernel == "replay":
-        return bench_replay(args, wl)
-    if args.kernel == "csr":
-        return bench_csr(args, wl)
     in_bytes = wl.B * wl.V * (2 if wl.dtype == "bf16" else 4)
     if args.ingest_pmc:
+        if args.kernel not in TRAFFIC_KERNELS:
+            raise SystemExit(f"no counter summary for --kernel {args.kernel}")
         with open(args.ingest_pmc[2]) as f:  # the last JSON line (a profiler may print after it)
             bench_line = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
         alg = int(bench_line["algorithmic_bytes_per_launch"])
-        if bench_line["config"].get("workload") != wl.name:
+        wname = wl.name if args.kernel == "sample" else f"{args.kernel} of {wl.name}"
+        if bench_line["config"].get("workload") != wname:
             raise SystemExit(f"the bench line is of {bench_line['config'].get('workload')}, "
-                             f"not of {wl.name}")
-        t = {"workload": wl.name, **ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], alg, in_bytes)}
-        path = traffic_path(wl)
+                             f"not of {wname}")
+        t = {"workload": wl.name, "kernel": args.kernel,
+             "commands": pmc_commands(args.workload, args.kernel),
+             **ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], alg, in_bytes, args.kernel)}
+        path = traffic_path(wl, args.kernel)
         with open(path, "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t))
         return 0
+    if args.kernel == "replay":
+        return bench_replay(args, wl)
+    if args.kernel == "csr":
+        return bench_csr(args, wl)
     dev = torch.device("cuda:0")
     d = device_inputs(wl)
     ncopies = max(1, -(-512 * 2**20 // in_bytes) + 1)

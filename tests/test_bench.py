@@ -54,6 +54,23 @@ def test_ingest_pmc_scales_by_the_copy_kernel(tmp_path):
     assert t["kernel_source_hash"] == bench.kernel_source_hash()
 
 
+def test_ingest_pmc_of_the_replay_counts_replay_dispatches_only(tmp_path):
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    samp = "void tsc::sample_fast_kernel<1, false>(tsc::SampleArgs)"
+    rep = "void tsc::replay_kernel<1, false>(tsc::ReplayArgs)"
+    neg = "void at::native::neg_kernel_cuda(...)"
+    _counter_csv(fetch, "FETCH_SIZE", [(samp, 9000.0), (rep, 100.0), (rep, 100.0), (neg, 512.0)])
+    _counter_csv(write, "WRITE_SIZE", [(samp, 90.0), (rep, 1.0), (neg, 1024.0)])
+    t = bench.ingest_pmc(str(fetch), str(write), alg_bytes=200_000, copy_bytes=2**20,
+                         kernel="replay")
+    assert t["counters"]["FETCH_SIZE"]["kernel_dispatches"] == 2
+    assert t["hbm_bytes_per_launch"] == 100.0 * 1024 * 2 + 1.0 * 1024
+    import types
+    wl = types.SimpleNamespace(B=256, V=151936, dtype="bf16", name="w")
+    assert bench.traffic_path(wl, "replay") != bench.traffic_path(wl)
+
+
 def test_kernel_source_hash_is_stable():
     h = bench.kernel_source_hash()
     assert len(h) == 16 and h == bench.kernel_source_hash()
