@@ -51,6 +51,11 @@ constexpr int64_t kFastMinV = 16384;
 constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;     // 262144
 constexpr int64_t kShortMaxV = (int64_t)kWaves * kWaveSize * kShortLoads * 8;   // 163840
 constexpr int32_t kFastMaxK = 4096;   // stash mode; compaction mode above it
+// top_k off (or above the compaction range) with top-p or min-p: theta is chosen as for this
+// top_k (about 2800 candidates). At 4096 (about 5300) the candidates' loads overflow the stash
+// (~330 per wave against 256) and are read again after the stream; supports wider than theta's
+// reach leave the row to the general path.
+constexpr int32_t kOffK = 2048;
 constexpr int32_t kCompactMaxK = 8192;
 constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
 // Waves whose stream ends among the first kOwnDraws draw the race uniforms of their own
@@ -1497,7 +1502,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
 
 
 // k: the row's top_k, INT32_MAX when the filter is off; kv: the top_k the cutoff theta is chosen
-// for (k itself up to the compaction range, else kFastMaxK in stash mode).
+// for (k itself up to the compaction range, else kOffK in stash mode).
 template <int LOADS, bool BITS>
 __device__ __forceinline__ bool fast_row_dispatch(const SampleArgs& a, int64_t b, int64_t& slot,
                                                   float T, int32_t k, int32_t kv, float p, float mp,
@@ -1540,12 +1545,12 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
       return;
     }
     // top_k off (<= 0 or >= V) or beyond the compaction range: the cutoff is chosen as for
-    // top_k = kFastMaxK, and the row is served here when top-p or min-p ends its support among
+    // top_k = kOffK, and the row is served here when top-p or min-p ends its support among
     // the candidates (checked after the scan; otherwise the general path takes it). A row with
     // no filter at all (support = every finite token) goes to the general path directly.
     const bool k_on = k >= 1 && (int64_t)k < a.V;
     const int32_t keff = k_on ? k : 0x7FFFFFFF;
-    const int32_t kv = (k_on && k <= kCompactMaxK) ? k : kFastMaxK;
+    const int32_t kv = (k_on && k <= kCompactMaxK) ? k : kOffK;
     const bool eligible = row_params_valid(T, p, mp) && T > 0.0f &&
                           ((k_on && k <= kCompactMaxK) || p < 1.0f || mp > 0.0f) &&
                           a.V >= kFastMinV && a.V <= kFastMaxV &&
