@@ -222,6 +222,19 @@ const char* tsc_status_string(int32_t status);
  */
 uint32_t tsc_set_wait_limit(uint32_t sleeps);
 
+/*
+ * tsc_set_debug_poison -- a debugging aid for code that reads the capture buffers.
+ *
+ * While on (nonzero), every tsc_sample_with_mask / tsc_sample_with_mask_bits call that captures
+ * rows (R > 0) also fills each slot's packed entries past its length with id -1 and (when
+ * `logprobs` is passed) logprob NaN, in one more kernel on the same stream, so that a reader
+ * that looks past `lengths[r]` sees values no valid capture holds. Off by default (0) unless the
+ * library was built with TSC_DEBUG_POISON defined. Process-wide; takes effect at the next call;
+ * returns the previous setting. The entries up to each length, the tokens and every other
+ * output are unchanged.
+ */
+int32_t tsc_set_debug_poison(int32_t on);
+
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t tsc_version(void);
 

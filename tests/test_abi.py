@@ -24,9 +24,10 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["tsc_replay_logprob", "tsc_sample_with_mask",
-                                    "tsc_sample_with_mask_bits", "tsc_set_wait_limit",
-                                    "tsc_status_string", "tsc_support_bits_ld", "tsc_support_csr",
-                                    "tsc_version", "tsc_workspace_size"]
+                                    "tsc_sample_with_mask_bits", "tsc_set_debug_poison",
+                                    "tsc_set_wait_limit", "tsc_status_string",
+                                    "tsc_support_bits_ld", "tsc_support_csr", "tsc_version",
+                                    "tsc_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,6 +52,18 @@ def test_wait_limit_setting(lib):
         assert tsc.set_wait_limit(0) == 1 << 20
     finally:
         tsc.set_wait_limit(prev)
+
+
+def test_debug_poison_setting(lib):
+    # Host-side state only: off by default, the previous setting is returned.
+    import top_support_capture_amd as tsc
+    prev = tsc.set_debug_poison(True)
+    try:
+        assert prev is False
+        assert tsc.set_debug_poison(False) is True
+        assert tsc.set_debug_poison(False) is False
+    finally:
+        tsc.set_debug_poison(prev)
 
 
 def _call(lib, **kw):

@@ -19,7 +19,7 @@ __all__ = ["sample_with_mask", "prepare", "PreparedSample", "SampleOutput", "wor
            "csr_to_host",
            "library", "LIB_PATH",
            "ROW_OK", "ROW_OVERFLOW", "ROW_NO_SUPPORT", "ROW_NONFINITE", "ROW_INVALID_PARAM",
-           "ROW_ABORTED", "set_wait_limit",
+           "ROW_ABORTED", "set_wait_limit", "set_debug_poison",
            "MAX_PACKED_WIDTH", "TscError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsc.so")
@@ -68,6 +68,8 @@ def library() -> ctypes.CDLL:
     lib.tsc_version.restype = I32
     lib.tsc_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.tsc_set_wait_limit.restype = ctypes.c_uint32
+    lib.tsc_set_debug_poison.argtypes = [ctypes.c_int32]
+    lib.tsc_set_debug_poison.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -94,6 +96,13 @@ def set_wait_limit(sleeps: int) -> int:
     0 restores the default; a tiny value makes rows give up with ROW_ABORTED (for tests of that
     path). Returns the previous limit."""
     return int(library().tsc_set_wait_limit(int(sleeps)))
+
+
+def set_debug_poison(on: bool) -> bool:
+    """While on, every capturing call fills packed slots past each length with id -1 and
+    logprob NaN (``tsc_set_debug_poison``), so that reads past a length stand out. Returns the
+    previous setting."""
+    return bool(library().tsc_set_debug_poison(1 if on else 0))
 
 
 def support_bits_ld(V: int) -> int:

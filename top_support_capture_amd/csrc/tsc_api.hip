@@ -45,11 +45,22 @@ hipError_t launch_sampler(const tsc::SampleArgs& a, hipStream_t stream) {
 // Limit of the bounded waits between the waves of a workgroup (tsc_set_wait_limit).
 std::atomic<uint32_t> g_wait_limit{tsc::kDefaultWaitLimit};
 
+// Packed slots past each length filled with -1 / NaN after a capture (tsc_set_debug_poison).
+#ifdef TSC_DEBUG_POISON
+std::atomic<int32_t> g_poison{1};
+#else
+std::atomic<int32_t> g_poison{0};
+#endif
+
 }  // namespace
 
 extern "C" {
 
 int32_t tsc_version(void) { return kVersion; }
+
+int32_t tsc_set_debug_poison(int32_t on) {
+  return g_poison.exchange(on != 0 ? 1 : 0, std::memory_order_relaxed);
+}
 
 uint32_t tsc_set_wait_limit(uint32_t sleeps) {
   return g_wait_limit.exchange(sleeps == 0u ? tsc::kDefaultWaitLimit : sleeps,
@@ -111,10 +122,15 @@ int32_t tsc_sample_with_mask_bits(const void* logits, int32_t dtype, int64_t B, 
   (void)hipGetLastError();  // start from a clean error state so a launch error is ours
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bits = a.bits != nullptr;
-  const hipError_t err =
+  hipError_t err =
       dtype == TSC_DTYPE_F32
           ? (bits ? launch_sampler<TSC_DTYPE_F32, true>(a, s) : launch_sampler<TSC_DTYPE_F32, false>(a, s))
           : (bits ? launch_sampler<TSC_DTYPE_BF16, true>(a, s) : launch_sampler<TSC_DTYPE_BF16, false>(a, s));
+  if (err == hipSuccess && R > 0 && g_poison.load(std::memory_order_relaxed) != 0) {
+    hipLaunchKernelGGL(tsc::poison_kernel, dim3((unsigned)R), dim3(tsc::kPoisonThreads), 0, s,
+                       lengths, packed_ids, logprobs, (int32_t)a.W);
+    err = hipGetLastError();
+  }
   return err == hipSuccess ? TSC_OK : TSC_ERR_HIP;
 }
 

@@ -108,4 +108,19 @@ __global__ void __launch_bounds__(kCsrThreads) csr_fused_kernel(CsrArgs a) {
   csr_copy_slot(a, j, n, at);
 }
 
+// Slot r's packed entries past its length (clamped to [0, W]) become id -1 and logprob NaN: a
+// debugging aid (tsc_set_debug_poison) that makes reads past a capture's length visible.
+constexpr int kPoisonThreads = 256;
+__global__ void __launch_bounds__(kPoisonThreads) poison_kernel(const int32_t* lengths,
+                                                                int32_t* packed_ids,
+                                                                float* logprobs, int32_t W) {
+  const int64_t r = blockIdx.x;
+  const int32_t l = lengths[r];
+  const int32_t from = l < 0 ? 0 : (l > W ? W : l);
+  for (int32_t j = from + (int32_t)threadIdx.x; j < W; j += kPoisonThreads) {
+    packed_ids[r * W + j] = -1;
+    if (logprobs) logprobs[r * W + j] = __builtin_nanf("");
+  }
+}
+
 }  // namespace tsc
