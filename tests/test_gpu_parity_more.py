@@ -162,3 +162,52 @@ def test_greedy_rows(dtype, V, pad):
     _check(wl, got, oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k,
                                             wl.top_p, wl.min_p, wl.optin_rows, wl.seeds,
                                             wl.positions, wl.W), max_flagged_frac=0.0)
+
+
+def _random_case(seed):
+    # One seeded case: dtype and V drawn across every path's range, rows of mixed shapes, and
+    # per-row parameters drawn from the values each path treats specially.
+    rng = np.random.default_rng(seed)
+    dtype = ["f32", "bf16"][seed % 2]
+    sizes = [1000, 8192, 16384, 32000, 50000, 131072] + ([151936, 262144] if dtype == "bf16" else [131076])
+    V = int(rng.choice(sizes))
+    B = int(rng.integers(4, 13))
+    rows = []
+    for _ in range(B):
+        kind = rng.choice(7, p=[0.28, 0.28, 0.2, 0.14, 0.04, 0.03, 0.03])
+        if kind == 0:
+            x = rng.standard_normal(V) * rng.uniform(0.5, 3.0)
+        elif kind == 1:
+            x = rng.standard_normal(V) + 4.0 * np.log(1.0 / np.arange(1, V + 1) ** 1.2)[rng.permutation(V)]
+        elif kind == 2:
+            x = np.round(rng.standard_normal(V) * 4) / 4  # ties on a grid
+        elif kind == 3:
+            x = rng.standard_normal(V) * 2
+            x[rng.choice(V, V // 4, replace=False)] = -np.inf
+        elif kind == 4:
+            x = rng.standard_normal(V)
+            x[rng.integers(V)] = np.nan
+        elif kind == 5:
+            x = rng.standard_normal(V)
+            x[rng.integers(V)] = np.inf
+        else:
+            x = np.full(V, -np.inf)
+        rows.append(x)
+    T = rng.choice([0.0, 0.5, 0.8, 1.0, 1.3, 2.0], B).astype(np.float32)
+    k = rng.choice([-1, 0, 1, 2, 10, 50, 500, 1024, 3000, 5000, 8192, 10000], B).astype(np.int32)
+    p = rng.choice([1.0, 0.99, 0.95, 0.9, 0.5, 0.0], B).astype(np.float32)
+    mp = rng.choice([0.0, 0.0, 0.01, 0.05, 0.2], B).astype(np.float32)
+    R = int(rng.integers(0, B + 1))
+    opt = np.sort(rng.choice(B, R, replace=False)).astype(np.int32)
+    W = int(rng.choice([1, 8, 64, 1024, 4096]))
+    return make(f"sweep{seed}_{dtype}_V{V}", rows, dtype, T=T, k=k, p=p, mp=mp, optin=opt, W=W)
+
+
+@pytest.mark.parametrize("seed", list(range(64)))
+def test_random_parameter_sweep(seed):
+    wl = _random_case(seed)
+    log(f"case random sweep seed {seed}: {wl.name} B={wl.B} W={wl.W} R={wl.R}")
+    got = run_gpu(wl)
+    ref = oracle.sample_with_mask(wl.logits, wl.dtype, wl.temperature, wl.top_k, wl.top_p,
+                                  wl.min_p, wl.optin_rows, wl.seeds, wl.positions, wl.W)
+    _check(wl, got, ref, max_flagged_frac=0.5)
