@@ -36,7 +36,7 @@ def run_csr(lengths, packed, lps, cap=None):
 
 
 @pytest.mark.parametrize("R,W", [(0, 4), (1, 1), (7, 5), (256, 2048), (2048, 7), (2049, 7), (3000, 16),
-                                 (5000, 3)])
+                                 (5000, 3), (6, 8200), (3, 4097)])
 def test_csr_synthetic(R, W):
     log(f"case csr synthetic R={R} W={W}")
     rng = np.random.default_rng(R * 31 + W)
@@ -63,6 +63,22 @@ def test_csr_capacity_and_selected_mode():
     assert np.array_equal(off, r_off)  # offsets are complete even when the payload is cut
     assert np.array_equal(ids[:cap], r_ids[:cap])
     assert np.all(lp == SENTINEL)       # no logprobs given: none written
+
+
+def test_csr_long_slots_cut_by_capacity():
+    # Slots on either side of the length from which the copy uses nontemporal stores, with the
+    # capacity ending inside a long one.
+    log("case csr long slots, capacity inside a long slot")
+    rng = np.random.default_rng(11)
+    R, W = 5, 6000
+    lengths = np.array([6000, 4095, 4096, 0, 5000], np.int32)
+    packed = rng.integers(0, 2**31 - 1, (R, W)).astype(np.int32)
+    lps = rng.standard_normal((R, W)).astype(np.float32)
+    r_off, r_ids, r_lp = oracle.support_csr(lengths, packed, lps)
+    cap = int(r_off[3]) - 1000  # inside the third slot (4096 entries)
+    off, ids, lp = run_csr(lengths, packed, lps, cap=cap)
+    assert np.array_equal(off, r_off)
+    assert np.array_equal(ids[:cap], r_ids[:cap]) and np.array_equal(lp[:cap], r_lp[:cap])
 
 
 def test_csr_of_an_oracle_capture():

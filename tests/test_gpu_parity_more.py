@@ -63,6 +63,18 @@ def test_selected_mode_against_oracle(index, W):
         assert np.array_equal(sup["packed_ids"][j, :n], sel["packed_ids"][j, :n])
 
 
+@pytest.mark.parametrize("W", [1024, 4095, 4096])
+def test_compaction_capture_widths(W):
+    # Compaction-mode captures (top_k 8192) clamped to W on either side of the length from which
+    # the copy-out uses nontemporal stores: every row against the oracle.
+    wl = make_workload(4, W=W)
+    log(f"case compaction capture width workload 4 W={W}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    _check(wl, got, ref)
+    assert (got["lengths"] == W).sum() >= wl.B // 2, "most rows should fill the capture"
+
+
 def _group_masses(x64, T):
     """(first sorted position, C/Z) of every tie group of a finite row, in logit-descending order
     (input construction only: the expected outputs come from the oracle)."""

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tsc.h"
 
 namespace tsc {
@@ -12,6 +14,9 @@ namespace tsc {
 constexpr int kThreads = 1024;
 constexpr int kWaveSize = 64;
 constexpr int kWaves = kThreads / kWaveSize;
+// Captures (a row's packed ids and logprobs, or a slot of the support CSR) of at least this many
+// entries, written as coalesced rows, use nontemporal stores.
+constexpr uint32_t kNtStoreMin = 4096;
 
 // ---- Logit element types -------------------------------------------------------------------
 // A key is an unsigned integer image of a logit whose order is the order of the values, with -0
