@@ -404,55 +404,70 @@ __global__ void __launch_bounds__(kThreads) replay_kernel(ReplayArgs a) {
   if (a.logprobs != nullptr && status == TSC_ROW_OK && n_ok) {
     constexpr int kU = 8;
     float* out = a.logprobs + j * a.W;
-    for (int32_t i0 = (int32_t)tid; i0 < n; i0 += kThreads * kU) {
-      int32_t idv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int32_t i = i0 + u * kThreads;
-        idv[u] = i >= n ? -1 : i == (int32_t)tid ? id_pre : ids[i];
-      }
-      float xv[kU];
-      uint32_t bv[kU];
-      if (STAGE && staged_row) {  // members of full chunks: their logits from the LDS stage
+    // A row of at least kNtStoreMin logprobs is written with nontemporal stores, so that it
+    // streams to memory instead of staying dirty in L2 for the kernel's end to write back; the
+    // two store kinds are separate instantiations of the loop (a run-time choice between two
+    // otherwise equal stores is merged by the compiler into one ordinary store).
+    auto lp_pass = [&](auto nt_tag) {
+      constexpr bool kNt = decltype(nt_tag)::value;
+      for (int32_t i0 = (int32_t)tid; i0 < n; i0 += kThreads * kU) {
+        int32_t idv[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          const int32_t id = idv[u];
-          bv[u] = id >= 0 && id < V ? (uint32_t)brow[id >> 3] : 0u;
+          const int32_t i = i0 + u * kThreads;
+          idv[u] = i >= n ? -1 : i == (int32_t)tid ? id_pre : ids[i];
         }
+        float xv[kU];
+        uint32_t bv[kU];
+        if (STAGE && staged_row) {  // members of full chunks: their logits from the LDS stage
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int32_t id = idv[u];
-          const uint32_t ch = (uint32_t)id >> 3;
-          float x = -__builtin_inff();
-          if ((bv[u] >> (id & 7)) & 1u) {
-            if (ch < nfull) {
-              const uint16_t* st16 = reinterpret_cast<const uint16_t*>(stg->chunk);
-              x = E::to_float((uint32_t)st16[(uint32_t)stg->slot_of[ch] * 8u + (uint32_t)(id & 7)]);
-            } else {
-              x = E::to_float((uint32_t)row[id]);  // the ragged last chunk is not staged
-            }
+          for (int u = 0; u < kU; ++u) {
+            const int32_t id = idv[u];
+            bv[u] = id >= 0 && id < V ? (uint32_t)brow[id >> 3] : 0u;
           }
-          xv[u] = x;
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int32_t id = idv[u];
+            const uint32_t ch = (uint32_t)id >> 3;
+            float x = -__builtin_inff();
+            if ((bv[u] >> (id & 7)) & 1u) {
+              if (ch < nfull) {
+                const uint16_t* st16 = reinterpret_cast<const uint16_t*>(stg->chunk);
+                x = E::to_float((uint32_t)st16[(uint32_t)stg->slot_of[ch] * 8u + (uint32_t)(id & 7)]);
+              } else {
+                x = E::to_float((uint32_t)row[id]);  // the ragged last chunk is not staged
+              }
+            }
+            xv[u] = x;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int32_t id = idv[u];
+            const bool ok = id >= 0 && id < V;
+            xv[u] = ok ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
+            bv[u] = ok ? (brow == nullptr ? 0xFFu : (uint32_t)brow[id >> 3]) : 0u;
+          }
         }
-      } else {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          const int32_t id = idv[u];
-          const bool ok = id >= 0 && id < V;
-          xv[u] = ok ? E::to_float((uint32_t)row[id]) : -__builtin_inff();
-          bv[u] = ok ? (brow == nullptr ? 0xFFu : (uint32_t)brow[id >> 3]) : 0u;
+          const int32_t i = i0 + u * kThreads;
+          if (i >= n) continue;
+          // Masked log-softmax: an id outside the support (possible only in a bitmask row) is -inf.
+          const bool in = (bv[u] >> (idv[u] & 7)) & 1u;
+          const float x = in ? xv[u] : -__builtin_inff();
+          const float lp = (float)(((double)x - (double)M) / (double)T - lnS);
+          if constexpr (kNt)
+            __builtin_nontemporal_store(lp, &out[i]);
+          else
+            out[i] = lp;
         }
       }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int32_t i = i0 + u * kThreads;
-        if (i >= n) continue;
-        // Masked log-softmax: an id outside the support (possible only in a bitmask row) is -inf.
-        const bool in = (bv[u] >> (idv[u] & 7)) & 1u;
-        const float x = in ? xv[u] : -__builtin_inff();
-        out[i] = (float)(((double)x - (double)M) / (double)T - lnS);
-      }
-    }
+    };
+    if (n >= (int32_t)kNtStoreMin)
+      lp_pass(BoolTag<true>{});
+    else
+      lp_pass(BoolTag<false>{});
   }
 }
 
