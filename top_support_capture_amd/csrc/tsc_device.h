@@ -5,8 +5,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "tsc.h"
 
 namespace tsc {
@@ -17,6 +15,12 @@ constexpr int kWaves = kThreads / kWaveSize;
 // Captures (a row's packed ids and logprobs, or a slot of the support CSR) of at least this many
 // entries, written as coalesced rows, use nontemporal stores.
 constexpr uint32_t kNtStoreMin = 4096;
+
+// A compile-time flag passed to a generic lambda, which then instantiates one body per value.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 // ---- Logit element types -------------------------------------------------------------------
 // A key is an unsigned integer image of a logit whose order is the order of the values, with -0

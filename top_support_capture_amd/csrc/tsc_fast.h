@@ -1446,9 +1446,9 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     };
     if (nout > 0u && lds_wait_at_least(&fs.staged, (uint32_t)kWaves * kStep, wlim, &fs.aborted)) {
       if (nl >= kNtStoreMin)
-        copy_out(std::true_type{});
+        copy_out(BoolTag<true>{});
       else
-        copy_out(std::false_type{});
+        copy_out(BoolTag<false>{});
     }
     // Bitmask bits, one candidate list per claim, by the waves with no stage slice left: off
     // the path from the ranking to the copy-out.

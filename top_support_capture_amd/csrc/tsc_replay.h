@@ -30,11 +30,6 @@ struct ReplayArgs {
   int8_t* row_status;            // [N]
 };
 
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
-
 struct ReplayShared {
   float m[kWaves];
   float s[kWaves];
