@@ -5,9 +5,9 @@
 // (coalesced 1 KB per load instruction), so everything a wave stashes is in id order.
 //
 //   1. Stream. The lane maxima of the first loads of every segment (a sample spread over the
-//      whole row) give a reference R for the mass and a cutoff theta that about 1.2-1.6 top_k
-//      tokens of the row should exceed: an LDS histogram of their key distances to the sample's maximum,
-//      built over the first stream steps so that the loads keep flowing.
+//      whole row) give a reference R for the mass and a cutoff theta set safely below the k-th
+//      largest value: an LDS histogram of their key distances to the sample's maximum, built
+//      over the first stream steps so that the loads keep flowing.
 //   2. As each load lands: running maximum (NaN-propagating, so it also detects NaN), for
 //      top_p < 1 the lane sum of exp2(x * log2(e) / T - R * log2(e) / T), and a ballot on "this
 //      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash
@@ -52,10 +52,11 @@ constexpr int64_t kFastMaxV = (int64_t)kWaves * kWaveSize * kFastLoads * 8;     
 constexpr int64_t kShortMaxV = (int64_t)kWaves * kWaveSize * kShortLoads * 8;   // 163840
 constexpr int32_t kFastMaxK = 4096;   // stash mode; compaction mode above it
 // top_k off (or above the compaction range) with top-p or min-p: theta is chosen as for this
-// top_k (about 2800 candidates). At 4096 (about 5300) the candidates' loads overflow the stash
-// (~330 per wave against 256) and are read again after the stream; supports wider than theta's
-// reach leave the row to the general path.
-constexpr int32_t kOffK = 2048;
+// top_k (about 2800 candidates at V = 262144, 2300 at V = 151936). Such a row needs no margin
+// over a k-th value, only room for its top-p or min-p support; a wider cutoff (about 5300
+// candidates) overflowed the stash (~330 loads per wave against 256), whose excess is read
+// again after the stream. Supports wider than theta's reach leave the row to the general path.
+constexpr int32_t kOffK = 1792;
 constexpr int32_t kCompactMaxK = 8192;
 constexpr float kRaceMargin = 1e-4f;  // float32 race scores are within ~3e-6 of exact
 // Waves whose stream ends among the first kOwnDraws draw the race uniforms of their own
@@ -607,21 +608,27 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   const uint32_t nseg = seg1 - seg0;                      // chunks in this wave's segment
   const uint32_t id0 = seg0 * 8u;                         // first token id of the segment
 
-  // Rank of theta among the lane maxima of the first loads: a maximum of 8 values exceeds the
-  // quantile 1 - q with probability 1 - (1-q)^8. The sample is the lane maxima of the first two
-  // loads (2048 values, 16384 elements). A target of 1.6 k + 64 candidates, or 1.2 k + 320 for
-  // k above 1536 (the estimate's relative error shrinks as k grows), keeps the k-th largest
-  // value above theta by about five standard deviations of the estimate.
-  constexpr int kSamples = 2 * kThreads;
+  // Rank of theta among the lane maxima of the first kSampleLoads loads of every segment (up to
+  // 1024 kSampleLoads chunk maxima). A chunk's maximum exceeds the k-th largest value with
+  // probability at most p_k = 1 - (1 - k/V)^8, so the number of sampled maxima above that value
+  // is at most binomial with mean mu = n p_k and variance n p_k (1 - p_k). theta is the sampled
+  // maximum of rank mu + 5 sd + 6: it lies above the k-th value (the row then leaves for the
+  // general path) with probability of the order of 1e-7 or below for independent logits, from
+  // a Poisson-like count at small mu to a normal tail at large mu. Rows of the short form sample
+  // four loads, which halves the variance and so cuts the candidates of c3-like rows by ~15%;
+  // rows of the long form sample two, because the later exchange that four loads need slowed
+  // their stream by ~0.8 us (B=1024, V=262144), more than the smaller tail saved.
+  constexpr int kSampleLoads = LOADS == kShortLoads ? 4 : 2;
+  constexpr int kSamples = kSampleLoads * kThreads;
   uint32_t theta_rank;
   {
-    const float target =
-        kv > 1536 ? 1.2f * (float)kv + 320.0f : 1.6f * (float)kv + 64.0f;
-    const float q = fminf(1.0f, target / (float)V);
-    const float t2 = (1.0f - q) * (1.0f - q), t4 = t2 * t2;
-    const float pr = 1.0f - t4 * t4;
-    const int rr = (int)ceilf(pr * (float)kSamples);
-    theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kSamples ? kSamples : rr));
+    const float n = (float)(nch < (uint32_t)kSamples ? nch : (uint32_t)kSamples);
+    const float t = 1.0f - fminf(1.0f, (float)kv / (float)V);
+    const float t2 = t * t, t4 = t2 * t2;
+    const float pk = 1.0f - t4 * t4;
+    const float mu = n * pk;
+    const float rr = ceilf(mu + 5.0f * sqrtf(mu * (1.0f - pk)) + 6.0f);
+    theta_rank = (uint32_t)(rr < 1.0f ? 1.0f : (rr > (float)kSamples ? (float)kSamples : rr));
   }
 
   // Wave priorities: streaming waves issue first (priority 3). A wave whose stream has ended
@@ -797,8 +804,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   const SlotScan sscan = slot_step1(opt_e, fs);
   lds_barrier();
-  // Step 1, exchange 2: the mass reference R = the sample's maximum; histogram of the distances
-  // to it; slot step 2.
+  // Step 1: the mass reference R = the first loads' maximum; the first two loads' maxima enter
+  // the histogram of the distances to it.
   const uint32_t kmax0 = waves_reduce(fs.kmax0_w, MaxU32());
   {
     const float R = E::to_float(bits_of_key<E>(kmax0));
@@ -825,21 +832,42 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (dist1 < (uint32_t)kThetaBins && (key1 >> 7) != 0u)
       atomicAdd(&fs.theta_hist[dist1 >> 1], 1u << (16u * (dist1 & 1u)));
   }
+  // Lane maxima of the sampled loads (loads 0 .. kSampleLoads), for their stash decisions.
+  float lmx[kSampleLoads + 1];
+  lmx[0] = lm0;
+  lmx[1] = lm1;
+  auto hist_add = [&](float lmv) {
+    const uint32_t kx = key_of<E>(__float_as_uint(lmv) >> 16);
+    const uint32_t dx = kx >= kmax0 ? 0u : kmax0 - kx;
+    if (dx < (uint32_t)kThetaBins && (kx >> 7) != 0u)
+      atomicAdd(&fs.theta_hist[dx >> 1], 1u << (16u * (dx & 1u)));
+  };
+  auto step = [&](int j) {  // load j: maximum and mass
+    issue(kLoadsAhead + j);
+    mask_tail(j);
+    unpack(r[j], f);
+    lmx[j] = load_max(f);
+    m_l = maximum2f(m_l, lmx[j]);
+    add_mass(f);
+    pin();
+  };
+  // Short form, steps 2 and 3: the next two loads' maxima join the histogram.
+  if constexpr (kSampleLoads == 4) {
+    step(2);
+    hist_add(lmx[2]);
+    step(3);
+    hist_add(lmx[3]);
+  }
+  // Exchange 2 (every sampled maximum is in the histogram) and slot step 2.
   if (a.R <= kThreads) slot_step2(a, b, sscan, fs);
   lds_barrier();
-  // Step 2: every wave finds the smallest distance whose cumulative count reaches the rank (when
-  // fewer maxima are within reach, the deepest reachable key); the same scan in each wave saves
-  // an exchange.
-  issue(kLoadsAhead + 2);
-  mask_tail(2);
-  unpack(r[2], f);
-  const float lm2 = load_max(f);
-  m_l = maximum2f(m_l, lm2);
-  add_mass(f);
-  pin();
+  // Next step: every wave finds the smallest distance whose cumulative count reaches the rank
+  // (when fewer maxima are within reach, the deepest reachable key); the same scan in each wave
+  // saves an exchange.
+  step(kSampleLoads);
   uint32_t theta_key;
   {
-    // At most 2048 samples, so a u16 count never carries into its neighbour.
+    // At most 4096 samples, so a u16 count never carries into its neighbour.
     constexpr int kPer = kThetaBins / kWaveSize;
     uint32_t hc[kPer];
     uint32_t lsum = 0;
@@ -864,14 +892,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   }
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
-  if constexpr (COMPACT) {
-    compact_load(0, r[0]);
-    compact_load(1, r[1]);
-    compact_load(2, r[2]);
-  } else {
-    stash_load(0, r[0], lm0 >= theta);
-    stash_load(1, r[1], lm1 >= theta);
-    stash_load(2, r[2], lm2 >= theta);
+#pragma unroll
+  for (int j = 0; j <= kSampleLoads; ++j) {
+    if constexpr (COMPACT) compact_load(j, r[j]);
+    else stash_load(j, r[j], lmx[j] >= theta);
   }
   // From here on, for top_p < 1, a load is stashed when the sum of its weights reaches the
   // weight of theta (any element >= theta implies it; the small slack covers exp2 rounding), so
@@ -900,7 +924,7 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
                 ((unsigned long long)(2u * (r1 >> 9) + 1u) << 32) | (unsigned long long)(~id1w));
   };
 #pragma unroll
-  for (int j = 3; j < LOADS; ++j) {
+  for (int j = kSampleLoads + 1; j < LOADS; ++j) {
     // Every step issues its load unconditionally (loads past the segment read zeros through the
     // buffer descriptor, with no memory traffic): a conditional issue makes the compiler's wait
     // counts conservative (vmcnt(0) at every step), which serialises the load pipeline.
@@ -1593,10 +1617,10 @@ __global__ void __launch_bounds__(kThreads) sample_fast_kernel(SampleArgs a) {
       greedy_row<DT>(a, b, slot, fs.red);
       return;
     }
-    // As for bfloat16 rows: top_k off or above kF32MaxK chooses the cutoff as for kF32MaxK.
+    // As for bfloat16 rows: top_k off or above kF32MaxK chooses the cutoff as for kF32OffK.
     const bool k_on = k >= 1 && (int64_t)k < a.V;
     const int32_t keff = k_on ? k : 0x7FFFFFFF;
-    const int32_t kv = (k_on && k <= kF32MaxK) ? k : kF32MaxK;
+    const int32_t kv = (k_on && k <= kF32MaxK) ? k : kF32OffK;
     const bool eligible = row_params_valid(T, p, mp) && T > 0.0f &&
                           ((k_on && k <= kF32MaxK) || p < 1.0f || mp > 0.0f) &&
                           a.V >= kF32MinV && a.V <= kF32MaxV && (a.V & 3) == 0 &&

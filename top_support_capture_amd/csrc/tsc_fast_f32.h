@@ -30,7 +30,10 @@ constexpr int kF32LoadsAhead = 4;    // loads in flight per lane
 constexpr int64_t kF32MinV = 8192;
 constexpr int64_t kF32ShortMaxV = (int64_t)kWaves * kWaveSize * kF32ShortLoads * 4;  // 32768
 constexpr int64_t kF32MaxV = (int64_t)kWaves * kWaveSize * kF32LongLoads * 4;       // 131072
-constexpr int32_t kF32MaxK = 2048;   // top_k above it (or off) chooses theta as for 2048
+constexpr int32_t kF32MaxK = 2048;   // the largest top_k served with a margin over its k-th value
+// top_k above kF32MaxK (or off) with top-p or min-p: theta is chosen as for this top_k, which
+// leaves about as many candidates as the row's top-p or min-p support needs room for.
+constexpr int32_t kF32OffK = 1792;
 constexpr uint32_t kF32StashPerWave = 256;
 constexpr uint32_t kF32CandCap = 4096;  // sorted candidates (u64 sort words); 4 per thread
 
@@ -110,15 +113,20 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
   F32Scalars& sc = *reinterpret_cast<F32Scalars*>(lds + LY::kEnd);
   static_assert(LOADS >= kF32LoadsAhead, "the first loads are issued together");
 
-  // Rank of theta among the sampled lane maxima (maxima of 4 values, 2048 of them).
+  // Rank of theta among the sampled lane maxima (maxima of 4 values, up to 2048 of them), as on
+  // the bfloat16 path: with p_k = 1 - (1 - k/V)^4 and n the sampled chunks, theta is the sampled
+  // maximum of rank mu + 5 sd + 6 (mu = n p_k, sd^2 = n p_k (1 - p_k)), which lies above the
+  // k-th largest value with probability of the order of 1e-7 or below for independent logits.
   constexpr int kSamples = 2 * kThreads;
   uint32_t theta_rank;
   {
-    const float target = kv > 1536 ? 1.2f * (float)kv + 320.0f : 1.6f * (float)kv + 64.0f;
-    const float q = fminf(1.0f, target / (float)V);
-    const float t2 = (1.0f - q) * (1.0f - q);
-    const int rr = (int)ceilf((1.0f - t2 * t2) * (float)kSamples);
-    theta_rank = (uint32_t)(rr < 1 ? 1 : (rr > kSamples ? kSamples : rr));
+    const float n = (float)(nch < (uint32_t)kSamples ? nch : (uint32_t)kSamples);
+    const float t = 1.0f - fminf(1.0f, (float)kv / (float)V);
+    const float t2 = t * t;
+    const float pk = 1.0f - t2 * t2;
+    const float mu = n * pk;
+    const float rr = ceilf(mu + 5.0f * sqrtf(mu * (1.0f - pk)) + 6.0f);
+    theta_rank = (uint32_t)(rr < 1.0f ? 1.0f : (rr > (float)kSamples ? (float)kSamples : rr));
   }
 
   __builtin_amdgcn_s_setprio(3);
