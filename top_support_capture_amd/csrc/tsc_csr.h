@@ -91,9 +91,10 @@ __device__ inline void csr_copy_slot(const CsrArgs& a, int64_t j, int64_t n, int
   const int64_t room = a.cap - at;
   const int64_t lim = n < room ? n : (room > 0 ? room : 0);
   // Long slots are written with nontemporal stores: they stream to memory as they are written
-  // instead of staying dirty in L2 for the kernel's end to write back (c4's 2M entries: 6.5 ->
-  // 5.5 us). Short slots keep ordinary stores: their partial lines at both ends made the c3
-  // capture's CSR (about 1100 entries a slot) slower, 3.4 -> 4.1 us.
+  // instead of staying dirty in L2 for the kernel's end to write back (the 2M entries of a B=256
+  // capture at width 8192: 6.5 -> 5.5 us). Short slots keep ordinary stores: their partial lines
+  // at both ends made the CSR of a B=256, V=151936 capture (about 1100 entries a slot) slower,
+  // 3.4 -> 4.1 us.
   if (lim >= (int64_t)kNtStoreMin)
     csr_copy_run<true>(a, src, srcl, at, lim);
   else

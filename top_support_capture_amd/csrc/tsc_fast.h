@@ -533,8 +533,8 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
 // group, so that a word the two share is still written once. A plain store suffices for every
 // word but the list's first and last, which the neighbouring waves' lists may share and which
 // take an atomic OR. Atomic ORs on words that plain stores also wrote were slow: one atomic per
-// survivor took the k = 8192 workload with bitmasks to 87 us (47 now), and c3's rows captured at
-// W = 512 to 27.7 us (25.6 now).
+// survivor took the k = 8192 workload with bitmasks to 87 us (47 now), and the B=256, V=151936,
+// k=1024 rows captured at W = 512 to 27.7 us (25.6 now).
 __device__ inline void support_bits_of_list(const uint32_t* cand, uint32_t n, float x_cut,
                                             uint32_t id0, uint32_t* brow) {
   const uint32_t lane = lane_id();
@@ -615,9 +615,10 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // maximum of rank mu + 5 sd + 6: it lies above the k-th value (the row then leaves for the
   // general path) with probability of the order of 1e-7 or below for independent logits, from
   // a Poisson-like count at small mu to a normal tail at large mu. Rows of the short form sample
-  // four loads, which halves the variance and so cuts the candidates of c3-like rows by ~15%;
-  // rows of the long form sample two, because the later exchange that four loads need slowed
-  // their stream by ~0.8 us (B=1024, V=262144), more than the smaller tail saved.
+  // four loads, which halves the variance and so cuts the candidates of k = 1024 rows
+  // (V = 151936) by ~15%; rows of the long form sample two, because the later exchange that four
+  // loads need slowed their stream by ~0.8 us (B=1024, V=262144), more than the smaller tail
+  // saved.
   constexpr int kSampleLoads = LOADS == kShortLoads ? 4 : 2;
   constexpr int kSamples = kSampleLoads * kThreads;
   uint32_t theta_rank;
@@ -1432,8 +1433,8 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     // words, then their bins' logprobs, are read together. A capture of at least kNtStoreMin
     // entries is written with nontemporal stores: these coalesced rows stream to memory as they
     // are written instead of staying dirty in L2 until the kernel's end, whose release then has
-    // to write them back (c4's 16.8 MB: 35.8 -> 33.8 us). Scattered stores (stash mode) stay
-    // ordinary: nontemporal there cost c3 1 us. The two store kinds are separate instantiations
+    // to write them back (B=256 rows of width 8192, 16.8 MB: 35.8 -> 33.8 us). Scattered stores
+    // (stash mode) stay ordinary: nontemporal there cost the B=256, V=151936 batch 1 us. The two store kinds are separate instantiations
     // of the loop: a run-time choice between two otherwise equal stores is merged by the
     // compiler into one ordinary store.
     auto copy_out = [&](auto nt_tag) {
