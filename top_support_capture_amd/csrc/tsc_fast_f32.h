@@ -3,9 +3,10 @@
 // A float32 key is 32 bits wide, so the per-key histograms of the bfloat16 path do not apply.
 // Here the row is still read exactly once, and the candidates are ordered by a sort instead:
 //   1. Stream. The lane maxima of every segment's first two loads give the mass reference R and
-//      a cutoff theta over the keys' top 16 bits that about 1.6 k + 64 tokens (1.2 k + 320 for
-//      k above 1536) should reach; every 16-byte load (4 values) whose maximum reaches theta is
-//      stashed whole in LDS, and (top_p < 1) each lane sums exp2(x log2(e) / T - R log2(e) / T).
+//      a cutoff theta over the keys' top 16 bits, set safely below the k-th largest value (the
+//      sampled maximum of rank mu + 5 sd + 6, below); every 16-byte load (4 values) whose
+//      maximum reaches theta is stashed whole in LDS, and (top_p < 1) each lane sums
+//      exp2(x log2(e) / T - R log2(e) / T).
 //   2. Each wave expands its stash into sort words (key << 32 | ~id) of the values >= theta,
 //      appended to one candidate array of the row (order does not matter: it is sorted next).
 //   3. A bitonic sort of the candidates in LDS into (value descending, id ascending) order; the
