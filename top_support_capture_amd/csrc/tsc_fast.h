@@ -981,30 +981,40 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   } else {
     // Stash expansion: candidate words of the stashed loads, then of the loads past the stash
     // (read again now), in id order. Lanes without a load hold -inf, which no candidate is.
+    uint32_t* const dummy = reinterpret_cast<uint32_t*>(lds + LY::kOffDummy) + lane;
     auto expand_chunk = [&](const uint4& q, uint32_t off) {
       const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
       uint32_t words[8];
-      bool isc[8];
       float xc[8];
-      uint32_t n = 0;
+      uint32_t cm = 0;  // bit e: element e is a candidate
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t hi = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
-        isc[e] = __uint_as_float(hi) >= th;  // -0 ties +0; NaN fails
-        xc[e] = isc[e] ? __uint_as_float(hi) : -__builtin_inff();
+        const bool isc = __uint_as_float(hi) >= th;  // -0 ties +0; NaN fails
+        xc[e] = isc ? __uint_as_float(hi) : -__builtin_inff();
         words[e] = hi | (off + (uint32_t)e);
-        n += isc[e];
+        cm |= (uint32_t)isc << e;
       }
       xcand = maximum3f(xcand, maximum3f(xc[0], xc[1], xc[2]), maximum3f(xc[3], xc[4], xc[5]));
       xcand = maximum3f(xcand, xc[6], xc[7]);
       uint32_t total;
-      uint32_t at = ncand + wave_excl_sum(n, total);
-      // Predicated stores (only candidates are written): fewer instructions than sending the
-      // other elements to a dummy slot.
+      const uint32_t at = ncand + wave_excl_sum((uint32_t)__popc(cm), total);
+      // Element e goes to at + (candidates before it in the lane), a bit count each (no chain
+      // through the elements); the others go to the lane's dummy slot, so that no store needs
+      // its own execution mask. Past the capacity nothing is written (the row falls back).
+      if (ncand + total <= (uint32_t)LY::kCandCap) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (isc[e] && at < (uint32_t)LY::kCandCap) cand[at] = words[e];
-        at += isc[e];
+        for (int e = 0; e < 8; ++e) {
+          uint32_t* dst = ((cm >> e) & 1u) ? cand + (at + (uint32_t)__popc(cm & ((1u << e) - 1u))) : dummy;
+          *dst = words[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t pos = at + (uint32_t)__popc(cm & ((1u << e) - 1u));
+          uint32_t* dst = ((cm >> e) & 1u) && pos < (uint32_t)LY::kCandCap ? cand + pos : dummy;
+          *dst = words[e];
+        }
       }
       ncand += total;
     };
