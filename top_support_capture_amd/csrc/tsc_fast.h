@@ -745,11 +745,20 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     if (__ballot(n != 0u) == 0ull) return;
     uint32_t total;
     uint32_t at = wcnt + wave_excl_sum(n, total);
+    if (wcnt + total <= (uint32_t)LY::kCandCap) {  // wave-uniform: no capacity test per element
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t* dst = (isc[e] && at < (uint32_t)LY::kCandCap) ? cand + at : dummy;
-      *dst = words[e];
-      at += isc[e];
+      for (int e = 0; e < 8; ++e) {
+        uint32_t* dst = isc[e] ? cand + at : dummy;
+        *dst = words[e];
+        at += isc[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t* dst = (isc[e] && at < (uint32_t)LY::kCandCap) ? cand + at : dummy;
+        *dst = words[e];
+        at += isc[e];
+      }
     }
     wcnt += total;
   };
