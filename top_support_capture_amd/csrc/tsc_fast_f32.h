@@ -55,7 +55,10 @@ struct F32Scalars {
   uint32_t fail_i[kWaves];  // index of the wave's first failing group (ntot: none)
   double race_s[kWaves];  // the wave's best race score
   uint32_t race_i[kWaves];  // the lowest id holding it
+  uint32_t decided;       // rows of at most kF32OneWaveMax candidates: decided by wave 0
 };
+// Rows with at most this many candidates are sorted, scanned and raced by one wave.
+constexpr uint32_t kF32OneWaveMax = 256;
 static_assert((size_t)LayoutF32::kEnd + sizeof(F32Scalars) <= kFastDynLds,
               "the float32 layout fits the buffer");
 
@@ -332,6 +335,166 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
   // Z relative to the maximum: exp2(x c - m c) = exp2(x c - R c) * exp2(R c - m c), with the
   // rounded R c of the stream, so that its rounding cancels.
   const double Z = NEED_P ? zr * exp2_fast(-(double)nrc - (double)m * (double)c) : 0.0;
+
+  // ---- Rows of at most kF32OneWaveMax candidates: one wave decides the row -------------------
+  // With so few candidates the workgroup-wide phases below are mostly barrier latency. Wave 0
+  // holds the candidates in registers, four per lane (entry lane + 64 r), sorts them, scans
+  // their weights, decides the support and races it, and writes every output; the other waves
+  // wait at one barrier for its decision (a row it cannot decide goes to the general path, which
+  // needs every wave). The arithmetic is that of the workgroup-wide phases, entry for entry.
+  if (ntot <= kF32OneWaveMax) {
+    auto one_wave = [&]() -> uint32_t {
+      uint64_t v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = lane + (uint32_t)r * kWaveSize;
+        v[r] = i < ntot ? cand[i] : 0ull;  // 0 sorts below every candidate
+      }
+      // Bitonic sort, descending: blocks (v0, v1) = entries 0..127 and (v2, v3) = 128..255.
+      const bool two = ntot > 128u;
+#pragma unroll
+      for (uint32_t kk = 2u; kk <= 128u; kk <<= 1) {
+        bitonic_block(v[0], v[1], 0u, kk, kk >> 1);
+        if (two) bitonic_block(v[2], v[3], 128u, kk, kk >> 1);
+      }
+      if (two) {  // the merge of size 256: entry i against i + 128, then within the blocks
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const uint64_t hi = v[r] > v[r + 2] ? v[r] : v[r + 2], lo = v[r] > v[r + 2] ? v[r + 2] : v[r];
+          v[r] = hi;
+          v[r + 2] = lo;
+        }
+        bitonic_block(v[0], v[1], 0u, 256u, 64u);
+        bitonic_block(v[2], v[3], 128u, 256u, 64u);
+      }
+      // Weights, their exclusive prefix in sorted order, and the first failing tie group.
+      const double dm = (double)m, dT = (double)T;
+      const double pz = (double)p * Z;
+      const bool need_m = mp > 0.0f;
+      const double ln_mp = need_m ? log((double)mp) : 0.0;
+      const double l2e_T = 1.4426950408889634 / dT;
+      double carry = 0.0, zs = 0.0;
+      uint32_t L = ntot, prev_last = 0u;
+      bool found = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = lane + (uint32_t)r * kWaveSize;
+        const bool in = i < ntot;
+        const uint32_t key = (uint32_t)(v[r] >> 32);
+        const float x = E::to_float(bits_of_key<E>(key));
+        const double w = in ? exp2_fast(((double)x - dm) * l2e_T) : 0.0;  // exp((x - m) / T)
+        const double winc = wave_incl_scan(w, [](double p0, double p1) { return p0 + p1; }, 0.0);
+        const double C = carry + (winc - w);
+        const uint32_t up = __shfl_up(key, 1u, kWaveSize);
+        const uint32_t pkey = lane == 0u ? prev_last : up;
+        const bool start = in && (i == 0u || key != pkey);
+        bool qual = (int64_t)i < (int64_t)k;
+        if (NEED_P) qual = qual && C <= pz;
+        if (need_m) qual = qual && ((double)x - dm) / dT >= ln_mp;
+        const uint64_t fails = __ballot(start && !qual);
+        if (!found && fails != 0ull) {
+          const int src = (int)__builtin_ctzll(fails);
+          L = (uint32_t)r * kWaveSize + (uint32_t)src;
+          zs = read_lane(C, src);
+          found = true;
+        }
+        carry += read_lane(winc, kWaveSize - 1);
+        prev_last = read_lane(key, kWaveSize - 1);
+      }
+      if (!found) zs = carry;
+      // Decided here iff theta lies at or below the k-th largest value, or a candidate group fails.
+      if (!(L < ntot || ntot >= (uint32_t)k)) return 0u;
+      const double lnzs = log(zs);
+      // The race over the support, as in the workgroup-wide phase: float32 scores, the entries
+      // within kRaceMargin of the best rescored in float64, ties to the lowest id.
+      const float invT = 1.0f / T;
+      float best32 = -__builtin_inff();
+      uint32_t uw[4];
+      float xv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = lane + (uint32_t)r * kWaveSize;
+        uw[r] = 0u;
+        xv[r] = -__builtin_inff();
+        if (i < L) {
+          uw[r] = race_word(~(uint32_t)v[r], seed, pos);
+          xv[r] = E::to_float(bits_of_key<E>((uint32_t)(v[r] >> 32)));
+          const float s32 = (xv[r] - m) * invT + race_noise((float)(2u * (uw[r] >> 9) + 1u) * 0x1p-24f);
+          best32 = s32 > best32 ? s32 : best32;
+        }
+      }
+      const float top32 = wave_reduce(best32, MaxOp());
+      double best = -__builtin_inf();
+      uint32_t best_id = 0xFFFFFFFFu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = lane + (uint32_t)r * kWaveSize;
+        if (i < L) {
+          const uint32_t id = ~(uint32_t)v[r];
+          const double u = (double)(2u * (uw[r] >> 9) + 1u) * 0x1p-24;
+          if ((xv[r] - m) * invT + race_noise((float)u) >= top32 - kRaceMargin) {
+            const double sc_ = ((double)xv[r] - dm) / dT - log(-log(u));
+            if (sc_ > best || (sc_ == best && id < best_id)) {
+              best = sc_;
+              best_id = id;
+            }
+          }
+        }
+      }
+      const double wbest = wave_reduce(best, MaxOp());
+      const uint32_t token = wave_reduce(best == wbest ? best_id : 0xFFFFFFFFu, MinOp());
+      // Outputs: the capture, its bitmask when wider than W, then the token's entry.
+      const bool capture = slot >= 0;
+      const uint32_t W = (uint32_t)a.W;
+      if (capture) {
+        int32_t* out_ids = a.packed_ids + slot * a.W;
+        float* out_lp = a.logprobs ? a.logprobs + slot * a.W : nullptr;
+        const uint32_t n = L < W ? L : W;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t i = lane + (uint32_t)r * kWaveSize;
+          if (i < n) {
+            out_ids[i] = (int32_t)(~(uint32_t)v[r]);
+            if (out_lp) out_lp[i] = logprob_of(E::to_float(bits_of_key<E>((uint32_t)(v[r] >> 32))), m, T, lnzs);
+          }
+        }
+        if (BITS && L > W && a.bits != nullptr) {
+          // The row cleared, its stores drained, then one atomic OR per support token.
+          uint32_t* brow = a.bits + slot * a.bits_ld;
+          const uint32_t nw = (uint32_t)bitmask_words(V);
+          for (uint32_t i = lane; i < nw; i += kWaveSize) brow[i] = 0u;
+          __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t i = lane + (uint32_t)r * kWaveSize;
+            if (i < L) {
+              const uint32_t id = ~(uint32_t)v[r];
+              atomicOr(brow + (id >> 5), 1u << (id & 31u));
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = lane + (uint32_t)r * kWaveSize;
+        if (i < L && ~(uint32_t)v[r] == token) {
+          a.tokens[b] = (int32_t)token;
+          a.row_status[b] = (capture && L > W) ? TSC_ROW_OVERFLOW : TSC_ROW_OK;
+          if (capture) {
+            a.lengths[slot] = (int32_t)(L < W ? L : W);
+            a.selected_logprob[slot] = logprob_of(xv[r], m, T, lnzs);
+          }
+        }
+      }
+      return 1u;
+    };
+    if (wid == 0) {
+      const uint32_t dec = one_wave();
+      if (lane == 0) sc.decided = dec;
+    }
+    lds_barrier();
+    return sc.decided != 0u;
+  }
 
   // ---- Sort (descending sort words: value descending, then id ascending) ----------------------
   // Bitonic. Stages whose pairs lie within a 128-entry block run in registers, one block per
