@@ -169,15 +169,16 @@ def copy_calibration(dev, nbytes: int, reps: int = 5) -> None:
 
 
 # How the counter CSVs that --ingest-pmc reads are made (run from /tmp with TMPDIR=/tmp; R is the
-# repository root).
+# repository root, OUT a directory for the counter files).
 def pmc_commands(index: int, kernel: str) -> list:
-    """The commands that produce a counter summary (run from /tmp, R the repository root)."""
+    """The commands that produce a counter summary (run from /tmp; R the repository root, OUT the
+    directory the counter files go to)."""
     run = f'python3 "$R/bench.py" --workload {index} --kernel {kernel} --no-cpu-baseline --steps 20 --warmup 2 --copy-calibration'
     return [
-        f'timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$R/gpurun_out/prof/fetch" -o fetch -- {run}',
-        f'timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$R/gpurun_out/prof/write" -o write -- {run}',
-        f'python3 bench.py --workload {index} --kernel {kernel} --ingest-pmc gpurun_out/prof/fetch/fetch_counter_collection.csv '
-        'gpurun_out/prof/write/write_counter_collection.csv <JSON line of a bench run of the same kernel>',
+        f'timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch" -o fetch -- {run}',
+        f'timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o write -- {run}',
+        f'python3 bench.py --workload {index} --kernel {kernel} --ingest-pmc "$OUT/fetch/fetch_counter_collection.csv" '
+        '"$OUT/write/write_counter_collection.csv" <JSON line of a bench run of the same kernel>',
     ]
 
 

@@ -43,7 +43,7 @@ extern "C" {
 enum {
   TSC_OK = 0,
   TSC_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad dtype, misaligned logits        */
-  TSC_ERR_UNSUPPORTED = 2,      /* a valid request this build does not serve (W too large)     */
+  TSC_ERR_UNSUPPORTED = 2,      /* a valid request the library does not serve (W too large)    */
   TSC_ERR_WORKSPACE = 3,        /* workspace smaller than tsc_workspace_size()                 */
   TSC_ERR_HIP = 4               /* the HIP runtime reported an error at launch                  */
 };
@@ -66,7 +66,7 @@ enum {
                                 Never produced by a correct run with the default limit.        */
 };
 
-/* Largest packed width W this build accepts. */
+/* Largest packed width W the library accepts. */
 #define TSC_MAX_PACKED_WIDTH 16384
 
 /*

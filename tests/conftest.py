@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is present, so `-m "not gpu"` and plain runs
-    # behave on CPU-only machines; on a GPU machine they run against the HIP library.
+    # behave on CPU-only machines; where a GPU is present they run against the HIP library.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

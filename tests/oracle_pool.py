@@ -23,7 +23,7 @@ def _rows_job(args):
 
 
 def workers() -> int:
-    # At most 16: the CPU share of a one-GPU machine, whatever os.cpu_count() reports there.
+    # At most 16 workers, whatever os.cpu_count() reports: the host's CPUs are shared.
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 

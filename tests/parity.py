@@ -1,6 +1,6 @@
 """Comparison of a library call's outputs with the oracle's, element by element.
 
-The bar (north star of the sampler): support ids, lengths and order bit-exact, tokens equal,
+The bar: support ids, lengths and order bit-exact, tokens equal,
 logprobs within 1e-5 absolute, except on rows the oracle reports as near a decision boundary
 (top-p mass within 1e-5 of top_p, min-p within 1e-6, top-two race scores within 1e-6), which are
 counted; each report exempts only the outputs it can change (see ``compare``).
