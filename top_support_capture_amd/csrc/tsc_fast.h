@@ -900,6 +900,27 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
     const uint32_t dsel = dmin != 0xFFFFFFFFu ? dmin : (uint32_t)kThetaBins - 1u;
     theta_key = uniform_u32(kmax0 > dsel ? kmax0 - dsel : 0u);
   }
+  // Min-p floor. min-p keeps x - m >= T ln(min_p), and the row maximum m is at least the largest
+  // sampled value r0, so no token below r0 + T ln(min_p) is in the support: theta rises to that
+  // floor when it is higher (heavy-headed rows keep a handful of candidates instead of thousands
+  // chosen for k). The floor sits 2^-16 of its terms below the float computation, far more than
+  // the rounding of that computation and the error of the scan's ln(min_p), so that every token
+  // below theta fails the scan's own min-p test, which the decision after the scan checks.
+  if (mp > 0.0f) {
+    const float r0 = E::to_float(bits_of_key<E>(kmax0));
+    const float lnmp = __logf(mp);
+    const float g = r0 + T * lnmp;
+    const float floor_v = g - (__builtin_fabsf(r0) + T * __builtin_fabsf(lnmp) + T) * 0x1p-16f;
+    // (NaN or infinite terms leave theta as it is.)
+    if (__builtin_isfinite(floor_v)) {
+      // The largest bfloat16 value <= floor_v: truncation, one key lower where truncating a
+      // negative value rounded it up.
+      const uint32_t fb = __float_as_uint(floor_v) >> 16;
+      uint32_t fk = key_of<E>(fb);
+      if (E::to_float(fb) > floor_v) fk -= 1u;
+      theta_key = uniform_u32(fk > theta_key ? fk : theta_key);
+    }
+  }
   theta = E::to_float(bits_of_key<E>(theta_key));
   slot = a.R <= kThreads ? slot_step3(fs) : find_capture_slot(a, b, fs.red);
 #pragma unroll
@@ -1254,8 +1275,16 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
         // it covers; the support is decided iff it also ends there: theta lies at or below the
         // k-th largest value (at least k candidates), or some candidate group below the support's
         // last group is excluded by top-p, min-p or top-k (with monotone predicates, every
-        // token below theta is excluded too). Otherwise the general path decides the row.
-        if (ntot < (uint32_t)k && !(fs.dstar < fs.dlow)) decision = kFallback;
+        // token below theta is excluded too), or the value just below theta fails the scan's
+        // min-p test (then so does every token below theta). Otherwise the general path decides
+        // the row.
+        bool below_fails_min_p = false;
+        if (mp > 0.0f && theta_key > 0u) {
+          const double tln_mp = (double)T * ln_fast((double)mp);
+          const float xb = E::to_float(bits_of_key<E>(theta_key - 1u));
+          below_fails_min_p = !(((double)xb - (double)m) >= tln_mp);
+        }
+        if (ntot < (uint32_t)k && !(fs.dstar < fs.dlow) && !below_fails_min_p) decision = kFallback;
         if (decision == kProceed && BITS && capture && fs.L > (uint32_t)a.W) {
           // A support wider than W is also written as a bitmask: cleared here, and its bits set
           // by the capture. Waiting for every memory counter to drain means the clearing stores
