@@ -225,15 +225,18 @@ def test_random_parameter_sweep(seed):
     _check(wl, got, ref, max_flagged_frac=0.5)
 
 
-@pytest.mark.parametrize("V", [151936, 262144])
-def test_min_p_floor_rows(V):
-    # Rows with min_p > 0 on the single-read path, whose cutoff rises to the min-p floor of the
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("bf16", 262144), ("f32", 32000),
+                                     ("f32", 131072)])
+def test_min_p_floor_rows(dtype, V):
+    # Rows with min_p > 0 on the single-read paths, whose cutoff rises to the min-p floor of the
     # sampled maximum: heavy-headed rows (a Zipf term: a handful of candidates instead of
     # thousands), Gaussian rows, rows of negative values only (the floor is negative and is
-    # rounded down to a bfloat16 value) and rows on a 1/8 grid (ties), crossed with min_p from
-    # 1e-4 to 1, top_k off, 64, 4096 (stash mode) and 6000 (compaction mode), top_p 1 or 0.95,
-    # and three temperatures. Every row against the oracle.
+    # rounded down to a representable cutoff) and rows on a 1/8 grid (ties), crossed with min_p
+    # from 1e-4 to 1, top_p 1 or 0.95, three temperatures and top_k: off, 64, 4096 (stash mode)
+    # and 6000 (compaction mode) for bfloat16; off, 64, 2048 and 3000 (beyond the margin's range)
+    # for float32. Every row against the oracle.
     rng = np.random.default_rng(V + 101)
+    kset = [-1, 64, 4096, 6000] if dtype == "bf16" else [-1, 64, 2048, 3000]
     ranks = np.arange(1, V + 1, dtype=np.float64)
     rows, Ts, ks, ps, mps = [], [], [], [], []
     for kind in ("zipf", "gauss", "negative", "grid"):
@@ -245,14 +248,15 @@ def test_min_p_floor_rows(V):
                 x = x * 1.5 - 40.0
             elif kind == "grid":
                 x = np.round(x * 1.5 * 8) / 8
-            rows.append(oracle.decode_logits(f32_to_bf16_bits(np.asarray(x, np.float32)), "bf16"))
-            ks.append([-1, 64, 4096, 6000][i % 4])
+            x = np.asarray(x, np.float32)
+            rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+            ks.append(kset[i % 4])
             mps.append([1e-4, 0.02, 0.1, 0.6, 1.0, 0.05][i % 6])
             Ts.append([0.4, 1.0, 2.0][i % 3])
             ps.append([1.0, 0.95][(i // 4) % 2])
-    wl = make(f"min_p_floor_V{V}", rows, "bf16", T=np.array(Ts), k=np.array(ks), p=np.array(ps),
-              mp=np.array(mps), W=8192)
-    log(f"case min-p floor rows V={V}")
+    wl = make(f"min_p_floor_{dtype}_V{V}", rows, dtype, T=np.array(Ts), k=np.array(ks),
+              p=np.array(ps), mp=np.array(mps), W=8192)
+    log(f"case min-p floor rows {dtype} V={V}")
     got = run_gpu(wl)
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.1)

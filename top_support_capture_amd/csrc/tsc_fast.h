@@ -7,7 +7,9 @@
 //   1. Stream. The lane maxima of the first loads of every segment (a sample spread over the
 //      whole row) give a reference R for the mass and a cutoff theta set safely below the k-th
 //      largest value: an LDS histogram of their key distances to the sample's maximum, built
-//      over the first stream steps so that the loads keep flowing.
+//      over the first stream steps so that the loads keep flowing. With min_p > 0 theta rises
+//      to the min-p floor of the sample's maximum when that is higher: no token below it passes
+//      min-p.
 //   2. As each load lands: running maximum (NaN-propagating, so it also detects NaN), for
 //      top_p < 1 the lane sum of exp2(x * log2(e) / T - R * log2(e) / T), and a ballot on "this
 //      load's maximum >= theta" that stashes the whole 16-byte load in the wave's LDS stash
@@ -19,8 +21,9 @@
 //   4. After one barrier, no more: wave 0 checks the row and scans the histogram bins from the
 //      maximum down: the joint threshold is the largest distance d from the maximum with fewer
 //      than k tokens strictly above and (top_p < 1) mass strictly above <= top_p * Z; min-p
-//      drops whole bins. theta was a true lower bound iff at least k candidates were found
-//      (checked here). Meanwhile the other waves draw every candidate's race uniform
+//      drops whole bins. The support is decided iff at least k candidates were found, a
+//      candidate bin below the support's last one fails a predicate, or the value just below
+//      theta fails min-p (checked here). Meanwhile the other waves draw every candidate's race uniform
 //      (Philox4x32-10, in jobs claimed from an LDS counter) and keep per bin the largest one
 //      (all candidates of a bin share their logit, so that one is the bin's best race score).
 //   5. Every wave writes the ordered capture of its own candidates: the bin scan gives each tie

@@ -4,7 +4,8 @@
 // Here the row is still read exactly once, and the candidates are ordered by a sort instead:
 //   1. Stream. The lane maxima of every segment's first two loads give the mass reference R and
 //      a cutoff theta over the keys' top 16 bits, set safely below the k-th largest value (the
-//      sampled maximum of rank mu + 5 sd + 6, below); every 16-byte load (4 values) whose
+//      sampled maximum of rank mu + 5 sd + 6, below) or, when higher, at the min-p floor
+//      R + T ln(min_p) below which no token passes min-p; every 16-byte load (4 values) whose
 //      maximum reaches theta is stashed whole in LDS, and (top_p < 1) each lane sums
 //      exp2(x log2(e) / T - R log2(e) / T).
 //   2. Each wave expands its stash into sort words (key << 32 | ~id) of the values >= theta,
@@ -16,7 +17,8 @@
 //      fewer than k entries before it, prefix mass <= top_p * Z, (x - m) / T >= ln(min_p). The
 //      support is the entries before the first failing group. Every token >= theta is a
 //      candidate, so this is exact for the candidates; the row is decided here iff at least k
-//      candidates exist or a candidate group fails (then every smaller token fails as well).
+//      candidates exist, a candidate group fails (then every smaller token fails as well), or
+//      the value just below theta fails min-p.
 //   5. The race in float64 over the support (score (x - m) / T - ln(-ln u), ties to the lowest
 //      id), the logprobs (x - m) / T - ln Z_S, and the capture: the sorted prefix itself.
 // Rows this path cannot decide exactly (capacities, theta above the support's end, a mass sum
@@ -216,8 +218,27 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
     const uint32_t dsel = dmin != 0xFFFFFFFFu ? dmin : (uint32_t)kThetaBins - 1u;
     theta_k16 = uniform_u32(kR > dsel ? kR - dsel : 0u);
   }
+  // Min-p floor, as on the bfloat16 path: no token below R + T ln(min_p) is in the support (the
+  // row maximum is at least R), so theta rises to that floor (2^-16 of its terms lower, more than
+  // the rounding of the float computation and of the scans' min-p test) when it is higher. The
+  // lowest value of a 16-bit key prefix lies at or below every value with that prefix.
+  if (mp > 0.0f) {
+    const float lnmp = __logf(mp);
+    const float floor_v = R + T * lnmp - (__builtin_fabsf(R) + T * __builtin_fabsf(lnmp) + T) * 0x1p-16f;
+    if (__builtin_isfinite(floor_v)) {
+      const uint32_t fk16 = key_of<E>(__float_as_uint(floor_v)) >> 16;
+      theta_k16 = uniform_u32(fk16 > theta_k16 ? fk16 : theta_k16);
+    }
+  }
   // Candidates: values whose key's top 16 bits reach theta_k16, i.e. values >= theta.
   const float theta = E::to_float(bits_of_key<E>(theta_k16 << 16));
+  // True when the value just below theta fails the scans' min-p test: then every token below
+  // theta does, and the candidates hold the whole support whatever k is.
+  auto below_theta_fails_min_p = [&](double dm, double dT, double ln_mp) {
+    if (!(mp > 0.0f) || theta_k16 == 0u) return false;
+    const float xb = E::to_float(bits_of_key<E>((theta_k16 << 16) - 1u));
+    return !(((double)xb - dm) / dT >= ln_mp);
+  };
   const float th = theta > -3.4028234663852886e38f ? theta : -3.4028234663852886e38f;
 
   // ---- Stream: running maximum, mass, stash of the loads that may hold a candidate -----------
@@ -402,8 +423,9 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
         prev_last = read_lane(key, kWaveSize - 1);
       }
       if (!found) zs = carry;
-      // Decided here iff theta lies at or below the k-th largest value, or a candidate group fails.
-      if (!(L < ntot || ntot >= (uint32_t)k)) return 0u;
+      // Decided here iff theta lies at or below the k-th largest value, a candidate group fails,
+      // or every token below theta fails min-p.
+      if (!(L < ntot || ntot >= (uint32_t)k || below_theta_fails_min_p(dm, dT, ln_mp))) return 0u;
       const double lnzs = log(zs);
       // The race over the support, as in the workgroup-wide phase: float32 scores, the entries
       // within kRaceMargin of the best rescored in float64, ties to the lowest id.
@@ -609,8 +631,9 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
       zs = read_lane(fc, src);
     }
   }
-  // Decided here iff theta lies at or below the k-th largest value, or a candidate group fails.
-  if (!(L < ntot || ntot >= (uint32_t)k)) return false;
+  // Decided here iff theta lies at or below the k-th largest value, a candidate group fails, or
+  // every token below theta fails min-p.
+  if (!(L < ntot || ntot >= (uint32_t)k || below_theta_fails_min_p(dm, dT, ln_mp))) return false;
   const double lnzs = log(zs);
 
   // ---- Race over the support, in float64: score (x - m) / T - ln(-ln u), ties -> lowest id ----
