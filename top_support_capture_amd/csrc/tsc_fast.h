@@ -357,16 +357,17 @@ __device__ inline double exp2_fast(double a) {
 }
 
 // Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d; they
-// were counted by bi = key - theta_key = dspan - d. Lane l owns the nb consecutive bins from
-// l * nb. Publishes the threshold d*, the support size and ln Z_S, and for every support bin its
+// were counted by bi = key - theta_key = dspan - d. Only bins d <= dlim are scanned (the bins past
+// the min-p cut cannot qualify). Lane l owns the nb consecutive bins from l * nb. Publishes the threshold d*, the support size and ln Z_S, and for every support bin its
 // capture base (the tokens with larger keys) and (x - m) / T; a logprob is (x - m) / T - ln Z_S.
 template <bool NEED_P, int NB, class LY>
-__device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, float m, float T, float c,
-                                      int32_t k, float p, float mp, double Z, bool capture,
-                                      const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
+__device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, uint32_t dlim, float m,
+                                      float T, float c, int32_t k, float p, float mp, double Z,
+                                      bool capture, const uint32_t* hcnt, unsigned char* lds,
+                                      FastShared& fs) {
   using E = Elem<TSC_DTYPE_BF16>;
   const uint32_t lane = lane_id();
-  const uint32_t nb = (dspan + kWaveSize) / kWaveSize;  // 1..NB
+  const uint32_t nb = (dlim + kWaveSize) / kWaveSize;  // 1..NB
   const bool need_m = mp > 0.0f;
   // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
   const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
@@ -380,7 +381,7 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
     const uint32_t d = lane * nb + (uint32_t)t;
     cnt[t] = 0u;
     xs[t] = 0.0f;
-    if ((uint32_t)t < nb && d <= dspan) {
+    if ((uint32_t)t < nb && d <= dlim) {
       xs[t] = E::to_float(bits_of_key<E>(kmax - d));
       cnt[t] = hcnt[dspan - d];
     }
@@ -444,14 +445,31 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, fl
   }
 }
 
-// The same for spans of 256 bins and more (bins re-read per pass instead of kept in registers).
-template <bool NEED_P, class LY>
-__device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, float m, float T, float c,
-                                      int32_t k, float p, float mp, double Z, bool capture,
-                                      const uint32_t* hcnt, unsigned char* lds, FastShared& fs) {
+// The last bin d <= dspan (< 1024) whose value passes min-p, by wave 0: the predicate is the scan's
+// own and monotone in d, and bin 0 (the maximum) always passes, so one ballot over every 16th bin
+// and one over the 16 bins after the last passing one find it.
+__device__ inline uint32_t min_p_last_bin(uint32_t kmax, uint32_t dspan, float m, float T, float mp) {
   using E = Elem<TSC_DTYPE_BF16>;
   const uint32_t lane = lane_id();
-  const uint32_t nb = (dspan + kWaveSize) / kWaveSize;  // 1..16
+  const double tln_mp = (double)T * ln_fast((double)mp);
+  auto pass = [&](uint32_t d) {
+    return d <= dspan && ((double)E::to_float(bits_of_key<E>(kmax - d)) - (double)m) >= tln_mp;
+  };
+  const uint64_t coarse = __ballot(pass(lane * 16u));
+  const uint32_t l0 = 63u - (uint32_t)__builtin_clzll(coarse | 1ull);
+  const uint64_t fine = __ballot(lane < 16u && pass(l0 * 16u + lane));
+  return l0 * 16u + (63u - (uint32_t)__builtin_clzll(fine | 1ull));
+}
+
+// The same for spans of 256 bins and more (bins re-read per pass instead of kept in registers).
+template <bool NEED_P, class LY>
+__device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspan, uint32_t dlim,
+                                      float m, float T, float c, int32_t k, float p, float mp,
+                                      double Z, bool capture, const uint32_t* hcnt,
+                                      unsigned char* lds, FastShared& fs) {
+  using E = Elem<TSC_DTYPE_BF16>;
+  const uint32_t lane = lane_id();
+  const uint32_t nb = (dlim + kWaveSize) / kWaveSize;  // 1..16
   const bool need_m = mp > 0.0f;
   // min-p keeps (x - m) / T >= ln(min_p), i.e. x - m >= T ln(min_p) (x - m is exact in double).
   const double tln_mp = need_m ? (double)T * ln_fast((double)mp) : 0.0;
@@ -461,7 +479,7 @@ __device__ __forceinline__ void bin_scan_wave0_wide(uint32_t kmax, uint32_t dspa
   auto bin = [&](uint32_t d, uint32_t& bc, double& bm) {
     bc = 0;
     bm = 0.0;
-    if (d <= dspan) {
+    if (d <= dlim) {
       if (hcnt[dspan - d] != 0u) low = (int32_t)d;
       const float x = value_of_d(d);
       if (!need_m || ((double)x - (double)m) >= tln_mp) {
@@ -1270,10 +1288,13 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
       if (over || kmax < theta_key || kmax - theta_key >= (uint32_t)kDBins) decision = kFallback;
       if (decision == kProceed) {
         const uint32_t dspan = kmax - theta_key;
-        if (dspan < 4u * kWaveSize)
-          bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+        // With min-p, the bins past its cut cannot qualify: the scan stops at the last bin that
+        // passes (every token below theta then fails min-p too, which the test below finds).
+        const uint32_t dlim = mp > 0.0f ? min_p_last_bin(kmax, dspan, m, T, mp) : dspan;
+        if (dlim < 4u * kWaveSize)
+          bin_scan_wave0<NEED_P, 4, LY>(kmax, dspan, dlim, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         else
-          bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
+          bin_scan_wave0_wide<NEED_P, LY>(kmax, dspan, dlim, m, T, c, k, p, mp, Z, capture, hcnt, lds, fs);
         // Every token at or above theta is a candidate, so the scan is exact for the tie groups
         // it covers; the support is decided iff it also ends there: theta lies at or below the
         // k-th largest value (at least k candidates), or some candidate group below the support's
