@@ -261,3 +261,46 @@ def test_min_p_floor_rows(dtype, V):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.1)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 32000)])
+def test_min_p_floor_extremes(dtype, V):
+    # The min-p floor where its margin and rounding matter: temperatures of 1e-3 and 50, min_p
+    # of 1e-30 and 0.999999, values near the float range limit, a row of equal values, rows
+    # with -inf entries and rows whose maximum lies outside the sampled loads (the floor then
+    # comes from a smaller sampled maximum). Some of these rows go to the general path; every
+    # row must agree with the oracle either way.
+    rng = np.random.default_rng(V + 202)
+    big = 3.0e38 if dtype == "f32" else 3.3e38
+    rows, Ts, ks, ps, mps = [], [], [], [], []
+
+    def add(x, T, k, p, mp):
+        x = np.asarray(x, np.float32)
+        rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+        Ts.append(T); ks.append(k); ps.append(p); mps.append(mp)
+
+    for T in (1e-3, 50.0):
+        for mp in (1e-30, 0.999999, 0.3):
+            add(rng.standard_normal(V) * 2, T, 64, 1.0, mp)
+            add(rng.standard_normal(V) * 2, T, -1, 0.9, mp)
+    x = rng.standard_normal(V)
+    x[rng.integers(V)] = big
+    add(x, 1.0, 32, 1.0, 0.5)
+    add(-x, 1.0, 32, 1.0, 0.5)
+    add(np.full(V, 1.25), 1.0, 64, 1.0, 0.2)
+    x = rng.standard_normal(V) * 3
+    x[rng.choice(V, V // 3, replace=False)] = -np.inf
+    add(x, 0.7, 128, 0.95, 0.05)
+    add(x, 0.7, -1, 1.0, 0.01)
+    for mp in (0.01, 0.2, 0.9):
+        x = rng.standard_normal(V)
+        x[V - 5] = 12.0  # the maximum in the last load of the last segment, far from the sample
+        add(x, 1.0, 256, 1.0, mp)
+        add(x - 30.0, 1.0, -1, 0.95, mp)
+    wl = make(f"min_p_floor_extremes_{dtype}_V{V}", rows, dtype, T=np.array(Ts), k=np.array(ks),
+              p=np.array(ps), mp=np.array(mps), W=2048)
+    log(f"case min-p floor extremes {dtype} V={V}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref, max_flagged_frac=0.25)
+    assert stats["rows"] == wl.B

@@ -349,9 +349,14 @@ __device__ inline double ln_fast(double v) {
   const double mant = __builtin_frexp(v, &e);  // [0.5, 1)
   return ((double)e + (double)__builtin_amdgcn_logf((float)mant)) * 0.6931471805599453;
 }
-// 2^a for a double argument with a relative error of about 2e-7 (float32 hardware exp2 on the
-// fractional part, the integer part exactly).
+// 2^a for a finite a <= ~0 (every caller passes (x - m) times a positive scale, x <= m), with a
+// relative error of about 2e-7 (float32 hardware exp2 on the fractional part, the integer part
+// exactly). Arguments below -1100 give 0 anyway (the smallest double is 2^-1074); they are raised
+// to -1100 first, so that the integer part always fits an int: converting an out-of-range double
+// is undefined, and a float32 row holding a value near 3e38 got infinite weights through it (its
+// other values lie ~4e38 below the maximum in log2 units).
 __device__ inline double exp2_fast(double a) {
+  a = __builtin_fmax(a, -1100.0);
   const double n = __builtin_floor(a);
   return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
 }
