@@ -304,3 +304,27 @@ def test_min_p_floor_extremes(dtype, V):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.25)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 32000), ("bf16", 4000)])
+def test_tiny_temperatures(dtype, V):
+    # Temperatures of 1e-30 and 1e-12 with top-p, top-k and min-p: log2(e) / T is so large that
+    # the stream's mass, summed against a rounded reference, loses its meaning; such top-p rows
+    # must leave for the general path, whose weights use x - m directly. A float32 row at 1e-30
+    # with top_p = 0.5 once came back with an empty support. The single-read paths and (V = 4000)
+    # the general path, every row against the oracle.
+    rng = np.random.default_rng(V + 303)
+    rows, Ts, ks, ps, mps = [], [], [], [], []
+    for T in (1e-30, 1e-12):
+        for (k, p, mp) in ((8, 0.5, 0.0), (-1, 0.9, 0.0), (64, 1.0, 0.1), (-1, 1.0, 0.05),
+                           (64, 0.95, 0.0), (4, 0.2, 0.3)):
+            x = np.asarray(np.round(rng.standard_normal(V) * 16) / 16, np.float32)
+            rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+            Ts.append(T); ks.append(k); ps.append(p); mps.append(mp)
+    wl = make(f"tiny_T_{dtype}_V{V}", rows, dtype, T=np.array(Ts, np.float32), k=np.array(ks),
+              p=np.array(ps), mp=np.array(mps), W=64)
+    log(f"case tiny temperatures {dtype} V={V}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref, max_flagged_frac=0.25)
+    assert stats["rows"] == wl.B

@@ -349,6 +349,15 @@ __device__ inline double ln_fast(double v) {
   const double mant = __builtin_frexp(v, &e);  // [0.5, 1)
   return ((double)e + (double)__builtin_amdgcn_logf((float)mant)) * 0.6931471805599453;
 }
+// The stream's mass sums exp2(x c - R c) as exp2f(fma(x, c, nrc)) with nrc = -R c rounded to
+// float, and multiplies by exp2(-nrc - m c) in double afterwards, so that the rounding of nrc
+// cancels. That holds while |nrc| <= 2^31: the rounding of R c (up to 2^-25 |R c|, the exponent
+// of the maximum's own term) then stays within float exp2's range, and the double R c within
+// 2^-22. Rows with top-p and a larger |R / T| (tiny temperatures) go to the general path, whose
+// weights use x - m directly (such a row flags every load, or reports an infinite mass, either of
+// which sends it there).
+constexpr float kMassRefMax = 0x1p31f;
+
 // 2^a for a finite a <= ~0 (every caller passes (x - m) times a positive scale, x <= m), with a
 // relative error of about 2e-7 (float32 hardware exp2 on the fractional part, the integer part
 // exactly). Arguments below -1100 give 0 anyway (the smallest double is 2^-1074); they are raised
@@ -960,7 +969,11 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
   // shows up in the mass.
   // (A theta weight below 2^-100 would flag every load: the stash overflows and the row falls
   // back, which happens only for extreme spreads of the logits at low temperature.)
-  const float wth = 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc));
+  // (A reference past kMassRefMax flags every load: the stash overflows, and the row leaves for
+  // the general path through the overflow test.)
+  const float wth = __builtin_fabsf(nrc) <= kMassRefMax
+                        ? 0.99999f * __builtin_amdgcn_exp2f(__builtin_fmaf(theta, c, nrc))
+                        : 0.0f;
   // Race draws of 128 candidates from `base` of this wave's list (two Philox chains per lane).
   // Each candidate's uniform is kept per bin as max(u numerator << 32 | ~id) (see the pick).
   uint64_t* binbest = reinterpret_cast<uint64_t*>(lds + LY::kOffBinBest);

@@ -296,7 +296,8 @@ __device__ __forceinline__ bool fast_row_f32(const SampleArgs& a, int64_t b, int
     if constexpr (NEED_P) wz = wave_reduce((double)(s_a + s_b), SumF64());
     if (lane == 0) {
       sc.wave_f[wid] = wm;
-      sc.wave_d[wid] = wz;
+      // A reference past kMassRefMax: an infinite mass sends the row to the general path.
+      sc.wave_d[wid] = !NEED_P || __builtin_fabsf(nrc) <= kMassRefMax ? wz : __builtin_inf();
       sc.wave_u[wid] = stash_over ? 1u : 0u;
     }
   }
