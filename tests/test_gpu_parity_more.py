@@ -328,3 +328,40 @@ def test_tiny_temperatures(dtype, V):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.25)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("dtype,V,kind", [("bf16", 262152, "plain"), ("bf16", 400000, "plain"),
+                                          ("f32", 200000, "plain"), ("bf16", 151936, "extreme"),
+                                          ("f32", 32000, "extreme")])
+def test_beyond_the_single_read_ranges(dtype, V, kind):
+    # "plain": vocabularies past the single-read limits (bfloat16 above 262144, float32 above
+    # 131072), served by the general path. "extreme": huge temperatures (1e20, 1e30: every
+    # weight ~1) and logits of magnitude ~1e30 at ordinary temperatures (the stream's mass
+    # reference is out of range for top-p rows). Every row against the oracle.
+    rng = np.random.default_rng(V + 404)
+    rows, Ts, ks, ps, mps = [], [], [], [], []
+
+    def add(x, T, k, p, mp):
+        x = np.asarray(x, np.float32)
+        rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+        Ts.append(T); ks.append(k); ps.append(p); mps.append(mp)
+
+    if kind == "plain":
+        for (k, p, mp) in ((64, 0.9, 0.0), (-1, 0.95, 0.0), (8192, 1.0, 0.0), (1000, 0.8, 0.05),
+                           (1, 1.0, 0.0)):
+            add(rng.standard_normal(V) * 2, float(rng.uniform(0.5, 1.5)), k, p, mp)
+        add(np.round(rng.standard_normal(V) * 8) / 8, 1.0, 500, 0.9, 0.0)
+    else:
+        for T in (1e20, 1e30):
+            for (k, p, mp) in ((64, 0.9, 0.0), (-1, 0.5, 0.0), (16, 1.0, 0.5)):
+                add(rng.standard_normal(V), T, k, p, mp)
+        for (k, p, mp) in ((64, 0.9, 0.0), (-1, 0.99, 0.0), (32, 1.0, 0.2)):
+            add(rng.standard_normal(V) * 1e30, 1.0, k, p, mp)
+            add(rng.standard_normal(V) * 1e30 + 1e31, 1.0, k, p, mp)
+    wl = make(f"beyond_{kind}_{dtype}_V{V}", rows, dtype, T=np.array(Ts, np.float32),
+              k=np.array(ks), p=np.array(ps), mp=np.array(mps), W=64)
+    log(f"case beyond the single-read ranges {kind} {dtype} V={V}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref, max_flagged_frac=0.25)
+    assert stats["rows"] == wl.B
