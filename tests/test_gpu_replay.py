@@ -289,3 +289,48 @@ def test_replay_support_logprobs_staging_limits(V):
     ref = oracle.replay(xx, "bf16", T, ids, lengths, tokens, cs, bits)
     errs, n, worst = compare_replay(got, ref, lengths)
     assert errs == [] and n == N, errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_extreme_temperatures_and_magnitudes(dtype):
+    # Temperatures from 1e-30 to 1e30 and logits of magnitude ~1e30, on packed and bitmask
+    # supports: (x - m) / T and the support's log-sum-exp must stay finite where the oracle's
+    # do. Supports and tokens are drawn here; both sides replay them.
+    rng = np.random.default_rng(77)
+    V, W = 3000, 48
+    rows = []
+    for T in (1e-30, 1e-12, 1.0, 1e20, 1e30):
+        for scale in (1.0, 1e30):
+            rows.append((T, scale))
+    N = len(rows)
+    x = np.zeros((N, V), np.float32)
+    ids = np.zeros((N, W), np.int32)
+    lengths = np.zeros(N, np.int32)
+    tokens = np.zeros(N, np.int32)
+    Ts = np.zeros(N, np.float32)
+    cs = np.zeros(N, np.int8)
+    bits = np.zeros((N, (V + 7) // 8), np.uint8)
+    for j, (T, scale) in enumerate(rows):
+        x[j] = (rng.standard_normal(V) * scale).astype(np.float32)
+        Ts[j] = T
+        L = int(rng.integers(1, W + 1))
+        sup = rng.choice(V, L, replace=False).astype(np.int32)
+        ids[j, :L] = sup
+        lengths[j] = L
+        tokens[j] = sup[int(rng.integers(L))]
+        if j % 3 == 2:  # every third row overflowed: its support is a bitmask
+            cs[j] = 1
+            keep = np.zeros(V, bool)
+            keep[rng.choice(V, 200, replace=False)] = True
+            keep[tokens[j]] = True
+            bits[j] = np.packbits(keep, bitorder="little")
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        xx = f32_to_bf16_bits(x)
+    else:
+        xx = x
+    log(f"case replay extreme temperatures and magnitudes {dtype}")
+    got = run_replay(xx, dtype, Ts, ids, lengths, tokens, cs, bits)
+    ref = oracle.replay(xx, dtype, Ts, ids, lengths, tokens, cs, bits)
+    errs, n, _ = compare_replay(got, ref, lengths)
+    assert errs == [], errs
