@@ -365,3 +365,26 @@ def test_beyond_the_single_read_ranges(dtype, V, kind):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.25)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 32000), ("bf16", 4000)])
+def test_extreme_seeds_and_positions(dtype, V):
+    # The race's generator at the ends of its 64-bit inputs: seeds and positions of 0, 2^32 - 1,
+    # 2^32, 2^63 and 2^64 - 1 (every 32-bit half of the Philox key and counter at 0 and all
+    # ones), on flat rows where the token is decided by the draws. Every row against the oracle.
+    rng = np.random.default_rng(V + 505)
+    edge = [0, 2**32 - 1, 2**32, 2**63, 2**64 - 1]
+    seeds, positions, rows = [], [], []
+    for s in edge:
+        for q in edge:
+            seeds.append(s)
+            positions.append(q)
+            x = np.asarray(np.round(rng.standard_normal(V) * 4) / 4, np.float32)
+            rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+    wl = make(f"extreme_seeds_{dtype}_V{V}", rows, dtype, T=1.0, k=256, p=0.95,
+              seeds=np.array(seeds, np.uint64), positions=np.array(positions, np.uint64), W=64)
+    log(f"case extreme seeds and positions {dtype} V={V}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref)
+    assert stats["rows"] == wl.B
