@@ -388,3 +388,27 @@ def test_extreme_seeds_and_positions(dtype, V):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 32000)])
+def test_min_p_floor_overflow_bitmasks(dtype, V):
+    # Min-p floor rows whose support overflows a capture of width 16: the packed prefix and the
+    # exact support bitmask, against the oracle, in stash mode, compaction mode and on the
+    # float32 path.
+    from tests.test_gpu_parity import check_bits
+    rng = np.random.default_rng(V + 606)
+    kset = [256, 4096, 6000] if dtype == "bf16" else [256, 2048, 3000]
+    rows, Ts, ks, ps, mps = [], [], [], [], []
+    for k in kset:
+        for mp in (0.001, 0.01, 0.2):
+            for T in (0.5, 1.0):
+                x = np.asarray(rng.standard_normal(V) * 2, np.float32)
+                rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+                Ts.append(T); ks.append(k); ps.append(0.97); mps.append(mp)
+    wl = make(f"min_p_floor_bits_{dtype}_V{V}", rows, dtype, T=np.array(Ts), k=np.array(ks),
+              p=np.array(ps), mp=np.array(mps), W=16)
+    log(f"case min-p floor overflow bitmasks {dtype} V={V}")
+    got = run_gpu(wl, bits=True)
+    ref = oracle_batch(wl, bits_ld=(wl.V + 127) // 128 * 16)
+    _check(wl, got, ref, max_flagged_frac=0.1)
+    check_bits(wl, got, ref, min_rows=6)
