@@ -23,9 +23,9 @@
 //      than k tokens strictly above and (top_p < 1) mass strictly above <= top_p * Z; min-p
 //      drops whole bins. The support is decided iff at least k candidates were found, a
 //      candidate bin below the support's last one fails a predicate, or the value just below
-//      theta fails min-p (checked here). Meanwhile the other waves draw every candidate's race uniform
-//      (Philox4x32-10, in jobs claimed from an LDS counter) and keep per bin the largest one
-//      (all candidates of a bin share their logit, so that one is the bin's best race score).
+//      theta fails min-p (checked here). Meanwhile the other waves draw every candidate's race
+//      uniform (Philox4x32-10, in jobs claimed from an LDS counter) and keep per bin the largest
+//      one (all candidates of a bin share their logit, so that one is the bin's best race score).
 //   5. Every wave writes the ordered capture of its own candidates: the bin scan gives each tie
 //      group's base position, the ranks and a prefix over the waves the rest. Once every draw
 //      is done, wave 0 picks the token over the support's bins (float32 scores, float64 for the
@@ -371,9 +371,10 @@ __device__ inline double exp2_fast(double a) {
 }
 
 // Bin scan by wave 0 alone. Bin d (0 <= d <= dspan) holds the candidates with key kmax - d; they
-// were counted by bi = key - theta_key = dspan - d. Only bins d <= dlim are scanned (the bins past
-// the min-p cut cannot qualify). Lane l owns the nb consecutive bins from l * nb. Publishes the threshold d*, the support size and ln Z_S, and for every support bin its
-// capture base (the tokens with larger keys) and (x - m) / T; a logprob is (x - m) / T - ln Z_S.
+// were counted by bi = key - theta_key = dspan - d. Only bins d <= dlim are scanned (the bins
+// past the min-p cut cannot qualify). Lane l owns the nb consecutive bins from l * nb. Publishes
+// the threshold d*, the support size and ln Z_S, and for every support bin its capture base (the
+// tokens with larger keys) and (x - m) / T; a logprob is (x - m) / T - ln Z_S.
 template <bool NEED_P, int NB, class LY>
 __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, uint32_t dlim, float m,
                                       float T, float c, int32_t k, float p, float mp, double Z,
