@@ -23,7 +23,17 @@ def check_invariants(tokens, row_status, packed_ids, logprobs, lengths, selected
     if R and (lengths.min() < 0 or lengths.max() > W):
         errs.append("length outside [0, W]")
     check = set(range(B)) if rows is None else set(int(r) for r in rows)
-    slot = {int(optin_rows[j]): j for j in range(R)}
+    # A slot is valid iff its row is in range and exceeds every earlier entry (the boundary's
+    # contract for optin_rows); an invalid slot has length 0 and a NaN selected logprob.
+    slot, running = {}, None
+    for j in range(R):
+        e = int(optin_rows[j])
+        if 0 <= e < B and (running is None or e > running):
+            slot[e] = j
+        elif lengths[j] != 0 or not np.isnan(selected_logprob[j]):
+            errs.append(f"slot {j}: invalid slot with length {lengths[j]} and selected logprob "
+                        f"{selected_logprob[j]}")
+        running = e if running is None else max(running, e)
     for r in sorted(check):
         st = int(row_status[r])
         tok = int(tokens[r])

@@ -412,3 +412,27 @@ def test_min_p_floor_overflow_bitmasks(dtype, V):
     ref = oracle_batch(wl, bits_ld=(wl.V + 127) // 128 * 16)
     _check(wl, got, ref, max_flagged_frac=0.1)
     check_bits(wl, got, ref, min_rows=6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_many_capture_slots_with_invalid_entries(dtype):
+    # More capture slots than one workgroup's threads (R = 1100 > 1024), so that each row finds
+    # its slot by the general lookup instead of the in-kernel scan, with duplicates, a descending
+    # run and out-of-range rows among them (invalid slots: length 0, NaN selected logprob).
+    rng = np.random.default_rng(707)
+    B, V = 1100, 16384
+    x = np.asarray(rng.standard_normal((B, V)) * 2, np.float32)
+    rows = [oracle.decode_logits(f32_to_bf16_bits(r), "bf16") if dtype == "bf16" else r for r in x]
+    opt = np.arange(B, dtype=np.int32)
+    opt[100] = opt[99]            # a duplicate
+    opt[500:510] = opt[500:510][::-1]  # a descending run
+    opt[700] = B + 5              # out of range
+    opt[701] = -3
+    wl = make(f"many_slots_{dtype}", rows, dtype, T=np.asarray(rng.uniform(0.6, 1.2, B), np.float32),
+              k=64, p=0.9, mp=0.0, optin=opt, W=32)
+    log(f"case many capture slots {dtype} B={B} R={len(opt)}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    assert int(np.sum(~ref.slot_valid)) >= 10
+    stats = _check(wl, got, ref)
+    assert stats["rows"] == wl.B
