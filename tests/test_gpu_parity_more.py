@@ -436,3 +436,25 @@ def test_many_capture_slots_with_invalid_entries(dtype):
     assert int(np.sum(~ref.slot_valid)) >= 10
     stats = _check(wl, got, ref)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("V", [32768, 151936, 262144])
+def test_negative_maximum_at_low_temperature(V):
+    # Rows whose maximum is negative, at temperatures where -m / T exceeds float exp2's range
+    # (e.g. m = -1.5, T = 0.01): the bin scan's unused slots once produced 0 * inf = NaN in the
+    # support mass (a NaN logprob on a row of support 1). Stash mode, both stream forms.
+    rng = np.random.default_rng(V + 808)
+    rows, Ts, ks, ps, mps = [], [], [], [], []
+    for shift in (-6.0, -30.0):
+        for (T, k, p, mp) in ((0.01, 64, 1.0, 0.0), (1e-3, 500, 1.0, 0.1), (0.01, 64, 0.9, 0.0),
+                              (0.05, 1024, 0.95, 0.01), (1e-3, -1, 1.0, 0.5)):
+            x = np.round((rng.standard_normal(V) + shift) * 16) / 16
+            rows.append(oracle.decode_logits(f32_to_bf16_bits(np.asarray(x, np.float32)), "bf16"))
+            Ts.append(T); ks.append(k); ps.append(p); mps.append(mp)
+    wl = make(f"neg_max_low_T_V{V}", rows, "bf16", T=np.array(Ts, np.float32), k=np.array(ks),
+              p=np.array(ps), mp=np.array(mps), W=64)
+    log(f"case negative maximum at low temperature V={V}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    stats = _check(wl, got, ref, max_flagged_frac=0.25)
+    assert stats["rows"] == wl.B

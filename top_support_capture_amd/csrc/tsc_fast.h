@@ -395,7 +395,9 @@ __device__ __forceinline__ void bin_scan_wave0(uint32_t kmax, uint32_t dspan, ui
   for (int t = 0; t < NB; ++t) {
     const uint32_t d = lane * nb + (uint32_t)t;
     cnt[t] = 0u;
-    xs[t] = 0.0f;
+    // An unused slot holds the maximum, so that its mass term cnt * exp2((x - m) c) is 0 * 1:
+    // with 0 there, a negative maximum at a low temperature made it 0 * inf = NaN.
+    xs[t] = m;
     if ((uint32_t)t < nb && d <= dlim) {
       xs[t] = E::to_float(bits_of_key<E>(kmax - d));
       cnt[t] = hcnt[dspan - d];
