@@ -442,7 +442,9 @@ def test_many_capture_slots_with_invalid_entries(dtype):
 def test_negative_maximum_at_low_temperature(V):
     # Rows whose maximum is negative, at temperatures where -m / T exceeds float exp2's range
     # (e.g. m = -1.5, T = 0.01): the bin scan's unused slots once produced 0 * inf = NaN in the
-    # support mass (a NaN logprob on a row of support 1). Stash mode, both stream forms.
+    # support mass: a NaN logprob on a row of support 1 (top_p = 1), and with top_p < 1 no bin
+    # qualified, d* = -1, and the pick's loop over d <= d* never ended. Stash mode, both stream
+    # forms.
     rng = np.random.default_rng(V + 808)
     rows, Ts, ks, ps, mps = [], [], [], [], []
     for shift in (-6.0, -30.0):

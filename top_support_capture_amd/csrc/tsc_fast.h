@@ -1330,6 +1330,9 @@ __device__ __forceinline__ bool fast_row_bf16(const SampleArgs& a, int64_t b, in
           below_fails_min_p = !(((double)xb - (double)m) >= tln_mp);
         }
         if (ntot < (uint32_t)k && !(fs.dstar < fs.dlow) && !below_fails_min_p) decision = kFallback;
+        // No qualifying bin (bin 0 always qualifies in exact arithmetic; only a non-finite mass
+        // could do this): the general path takes the row, and no loop below runs to d* = -1.
+        if (fs.dstar < 0) decision = kFallback;
         if (decision == kProceed && BITS && capture && fs.L > (uint32_t)a.W) {
           // A support wider than W is also written as a bitmask: cleared here, and its bits set
           // by the capture. Waiting for every memory counter to drain means the clearing stores
