@@ -460,3 +460,20 @@ def test_negative_maximum_at_low_temperature(V):
     ref = oracle_batch(wl)
     stats = _check(wl, got, ref, max_flagged_frac=0.25)
     assert stats["rows"] == wl.B
+
+
+@pytest.mark.parametrize("seed", list(range(1000, 1096)))
+def test_random_parameter_sweep_wide(seed):
+    # The random sweep's cases with wider parameter sets: temperatures from 1e-3 to 10, min_p
+    # from 1e-4 to 1 and top_p from 0 to 0.999 (this combination found a NaN support mass and a
+    # pick that never ended on rows with a negative maximum at a low temperature).
+    wl = _random_case(seed)
+    rng = np.random.default_rng(seed + 99991)
+    B = wl.B
+    wl.temperature[:] = rng.choice([0.0, 1e-3, 0.05, 0.5, 1.0, 2.0, 10.0], B).astype(np.float32)
+    wl.min_p[:] = rng.choice([0.0, 0.0, 1e-4, 0.01, 0.1, 0.5, 1.0], B).astype(np.float32)
+    wl.top_p[:] = rng.choice([1.0, 0.999, 0.95, 0.7, 0.3, 0.0], B).astype(np.float32)
+    log(f"case wide random sweep seed {seed}: {wl.name} B={wl.B} W={wl.W} R={wl.R}")
+    got = run_gpu(wl)
+    ref = oracle_batch(wl)
+    _check(wl, got, ref, max_flagged_frac=0.5)
