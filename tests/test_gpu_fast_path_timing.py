@@ -17,7 +17,7 @@ from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
-# (workload, bound in microseconds): measured 16, 21, 33, 109 and 122 us.
+# (workload, bound in microseconds): measured 16, 21, 33, 109 and 119 us.
 CASES = [(2, 60.0), (3, 70.0), (4, 100.0), (5, 300.0), (6, 300.0)]
 
 
