@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from tests.gpu_helpers import log, logits_tensor
+from tests.parity import logprob_tol
 from workloads import make_workload, perturbed_logits
 
 pytestmark = pytest.mark.gpu
@@ -54,13 +55,13 @@ def compare_replay(got, ref, lengths, rows=None):
             n += 1
             continue
         worst = max(worst, abs(float(gs[j]) - float(rs[j])))
-        if abs(float(gs[j]) - float(rs[j])) > LP_TOL:
+        if abs(float(gs[j]) - float(rs[j])) > float(logprob_tol(rs[j])):
             errs.append(f"row {j}: logprob {gs[j]} != {rs[j]}")
         m = int(lengths[j])
         if gl is not None and 1 <= m <= gl.shape[1]:
             a, b = gl[j, :m].astype(np.float64), rl[j, :m].astype(np.float64)
             fin = np.isfinite(b)
-            if not np.array_equal(np.isfinite(a), fin) or np.any(np.abs(a[fin] - b[fin]) > LP_TOL):
+            if not np.array_equal(np.isfinite(a), fin) or np.any(np.abs(a[fin] - b[fin]) > logprob_tol(b[fin])):
                 errs.append(f"row {j}: support logprobs differ (max {np.max(np.abs(a[fin] - b[fin]))})")
             if fin.any():
                 worst = max(worst, float(np.max(np.abs(a[fin] - b[fin]))))
@@ -334,3 +335,42 @@ def test_replay_extreme_temperatures_and_magnitudes(dtype):
     ref = oracle.replay(xx, dtype, Ts, ids, lengths, tokens, cs, bits)
     errs, n, _ = compare_replay(got, ref, lengths)
     assert errs == [], errs
+
+
+@pytest.mark.parametrize("seed", list(range(48)))
+def test_replay_random_sweep(seed):
+    # Supports captured by the oracle sampler on random rows (scales, -inf entries, top-k, top-p,
+    # min-p, widths 1..512), replayed on perturbed logits at temperatures from 1e-3 to 1e3.
+    from tests.oracle_pool import oracle_batch
+    from tests.test_gpu_parity import make
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    dtype = ["f32", "bf16"][seed % 2]
+    V = int(rng.choice([1000, 8192, 32000, 131072, 151936] if dtype == "bf16" else [1000, 8192, 32000, 100000]))
+    B = int(rng.integers(2, 9))
+    rows = []
+    for _ in range(B):
+        x = rng.standard_normal(V) * float(rng.choice([0.3, 1.0, 3.0])) + float(rng.choice([0.0, -20.0]))
+        if rng.integers(4) == 0:
+            x[rng.choice(V, V // 5, replace=False)] = -np.inf
+        x = np.asarray(x, np.float32)
+        rows.append(oracle.decode_logits(f32_to_bf16_bits(x), "bf16") if dtype == "bf16" else x)
+    T = rng.choice([0.3, 0.7, 1.0, 2.0], B).astype(np.float32)
+    k = rng.choice([-1, 5, 100, 1000, 5000], B).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.8], B).astype(np.float32)
+    mp = rng.choice([0.0, 0.0, 0.01, 0.1], B).astype(np.float32)
+    W = int(rng.choice([1, 8, 64, 512]))
+    wl = make(f"replay_sweep{seed}_{dtype}_V{V}", rows, dtype, T=T, k=k, p=p, mp=mp, W=W)
+    ref = oracle_batch(wl, bits_ld=(V + 127) // 128 * 16)
+    ids = np.where(ref.packed_ids < 0, 0, ref.packed_ids).astype(np.int32)
+    newx = perturbed_logits(np.asarray(wl.logits), dtype, seed + 7,
+                            sigma=float(rng.choice([0.0, 0.25, 2.0])))
+    T2 = rng.choice([1e-3, 0.5, 1.0, 4.0, 1e3], B).astype(np.float32)
+    cs = ref.row_status[wl.optin_rows].astype(np.int8)
+    toks = ref.tokens[wl.optin_rows].astype(np.int32)
+    xr = np.ascontiguousarray(newx[wl.optin_rows])
+    log(f"case replay random sweep seed {seed}: {wl.name} B={B} W={W}")
+    got = run_replay(xr, dtype, T2, ids, ref.lengths, toks, cs, ref.support_bits)
+    exp = oracle.replay(xr, dtype, T2, ids, ref.lengths, toks, cs, ref.support_bits)
+    errs, n, _ = compare_replay(got, exp, ref.lengths)
+    assert errs == [], errs[:5]
